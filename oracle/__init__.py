@@ -1,0 +1,134 @@
+"""CPU oracle for the weight-only quantized matmul.
+
+TEST INFRASTRUCTURE ONLY: tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The product library never imports,
+links or runs it, and it shares no code with the HIP path.
+
+The arithmetic lives in ``oracle.c`` (plain C, IEEE double accumulation,
+one final rounding to float); this module compiles it with gcc and wraps it
+with numpy arrays. What it computes is
+
+    y[s,o] = scale[o] * sum_i dequant(W[o,i]) * x[s,i]
+
+as given by the qmatmul.comp header quoted in colibri "第 8 章 · 02
+CUDA/Metal/Vulkan 三后端" (section 四) and the weight_at / quant_matmul
+description in colibri-analysis "CUDA 后端" (section 1). The readings the
+pages leave open are listed at the top of ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F32, I8, I4, I2 = 0, 1, 2, 3
+FMT_NAMES = {F32: "f32", I8: "i8", I4: "i4", I2: "i2"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc -O2, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # The mutation test points this at a deliberately broken copy of the
+        # oracle to show that the pin suite rejects it.
+        path = os.environ.get("ORACLE_LIB_UNDER_TEST")
+        if not path:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            path = _LIB
+        lib = ctypes.CDLL(path)
+        lib.oracle_row_bytes.restype = ctypes.c_long
+        lib.oracle_row_bytes.argtypes = [ctypes.c_int, ctypes.c_long]
+        lib.oracle_weight.restype = ctypes.c_double
+        lib.oracle_weight.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_long]
+        lib.oracle_matmul.restype = ctypes.c_int
+        lib.oracle_matmul.argtypes = [
+            ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_void_p, ctypes.c_long,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def row_bytes(fmt: int, I: int) -> int:
+    rb = _load().oracle_row_bytes(int(fmt), int(I))
+    if rb < 0:
+        raise ValueError("invalid fmt/I: %r/%r" % (fmt, I))
+    return int(rb)
+
+
+def dequant_row(fmt: int, row: np.ndarray, I: int) -> np.ndarray:
+    """Dequantized values (float64) of the first I elements of one packed row."""
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    if row.size < row_bytes(fmt, I):
+        raise ValueError("row too short")
+    lib = _load()
+    p = row.ctypes.data
+    return np.array([lib.oracle_weight(int(fmt), p, i) for i in range(I)], dtype=np.float64)
+
+
+def matmul(fmt: int, w: np.ndarray, scales, x: np.ndarray, I: int | None = None,
+           threads: int | None = None, want_bound: bool = True):
+    """Oracle y (float32 [S,O]) and bound magnitude A (float64 [S,O]).
+
+    w: uint8 [O, row_stride] packed rows (row_stride >= row_bytes(fmt, I)).
+    scales: float32 [O] or None (f32 only: scale 1).
+    x: float32 [S, I].
+    """
+    lib = _load()
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be [S, I]")
+    S = x.shape[0]
+    if I is None:
+        I = x.shape[1]
+    if x.shape[1] != I:
+        raise ValueError("x has %d columns, I=%d" % (x.shape[1], I))
+    if w.ndim != 2:
+        raise ValueError("w must be [O, row_stride] bytes")
+    O, stride = w.shape
+    if scales is not None:
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        if scales.shape != (O,):
+            raise ValueError("scales must be [O]")
+    y = np.empty((S, O), dtype=np.float32)
+    a = np.empty((S, O), dtype=np.float64) if want_bound else None
+    rc = lib.oracle_matmul(
+        int(fmt), O, int(I), w.ctypes.data, stride,
+        scales.ctypes.data if scales is not None else None,
+        x.ctypes.data, S, y.ctypes.data, a.ctypes.data if a is not None else None,
+        int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_matmul rejected its arguments (rc=%d)" % rc)
+    return y, a
+
+
+def matmul_rows(fmt: int, w: np.ndarray, scales, x: np.ndarray, rows, I: int | None = None,
+                threads: int | None = None):
+    """Oracle y and A restricted to output rows ``rows`` (columns of y): [S, len(rows)]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    sub_w = np.ascontiguousarray(np.asarray(w)[rows])
+    sub_s = None if scales is None else np.ascontiguousarray(np.asarray(scales)[rows])
+    return matmul(fmt, sub_w, sub_s, x, I=I, threads=threads)
