@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-resident quantized matmul on one MI355X.
+
+Default workload (the headline): int4 W [12288, 6144] (two codes per byte, low
+nibble = even column, value = nibble - 8), per-row fp32 scales, fp32 x with
+S = 1; one step = one y = matmul(W, x) over a weight copy already resident in
+HBM. Weights rotate over >= 1 GiB of distinct copies so the 256 MB Infinity
+Cache cannot serve them. K steps are captured into one HIP graph (one kernel
+node per step) and replayed once inside the timed region; x and y stay on the
+device.
+
+Prints one JSON line: value = weight bytes streamed per second (GB/s) for the
+GEMV workloads, GFLOP/s for the prefill workload; `roofline` compares the
+dominant kernel's algorithmic bytes (or flops) per launch, divided by its
+average launch duration from HIP events on the launch stream, with the MI355X
+peak; `cpu_baseline` is the CPU oracle timed on this host on a bounded sample
+of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+FP32_VALU_FMA_PEAK_TFLOPS = 78.6  # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed FMA)
+METRIC = "effective weight GB/s (and % of HBM peak) for S=1 int4 GEMV; GFLOP/s at S=512"
+ROTATION_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="dense_gemv",
+                    choices=["dense_gemv", "moe_decode", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
+                             "prefill"])
+    ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def problems_for(name):
+    import synth
+    if name == "dense_gemv":
+        return [synth.dense_gemv(S=1)], "dense_gemv: int4 W[12288,6144] (codes U{0..15}), scales U[0.002,0.05], x N(0,1), S=1"
+    if name == "moe_decode":
+        return synth.moe_decode(), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
+                                    "S=1 per expert, one grouped launch")
+    if name.startswith("int2_gemv_s"):
+        S = int(name[len("int2_gemv_s"):])
+        return [synth.int2_gemv(S=S)], "int2_gemv: int2 W[16384,8192] (codes U{0..3}), scales U[0.01,0.1], S=%d" % S
+    if name == "prefill":
+        return [synth.prefill(S=512)], "prefill: int8 W[6144,6144] (rint N(0,40) clipped), scales U[0.001,0.01], S=512"
+    raise ValueError(name)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import weight_only_quantized_matmul_amd as wq
+
+    probs, desc = problems_for(args.workload)
+    wq.wq_init([0])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+    grouped = args.workload == "moe_decode"
+    weight_bytes = sum(p.weight_bytes for p in probs)
+    alg_bytes = sum(p.weight_bytes + 4 * p.O + 4 * p.S * p.I + 4 * p.S * p.O for p in probs)
+    alg_flops = sum(2.0 * p.S * p.O * p.I for p in probs)
+    compute_bound = args.workload == "prefill"
+    n_rot = 1 if compute_bound else max(1, math.ceil(ROTATION_BYTES / weight_bytes))
+
+    # resident weights: n_rot copies of the tensor set
+    copies = []
+    for _ in range(n_rot):
+        copies.append([wq.wq_tensor_upload(None, 0, p.fmt, p.O, p.I, p.w, p.scales) for p in probs])
+    groups = [wq.wq_grouped_create(c) for c in copies] if grouped else None
+    xs = [torch.from_numpy(p.x).to(dev) for p in probs]
+    ys = [torch.empty((p.S, p.O), dtype=torch.float32, device=dev) for p in probs]
+
+    def step(i):
+        r = i % n_rot
+        if grouped:
+            wq.wq_grouped_matmul_dev(groups[r], xs, ys)
+        else:
+            wq.wq_matmul_dev(copies[r][0], xs[0], ys[0])
+
+    stream = torch.cuda.current_stream()
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(K):
+                step(i)
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay: instantiation and first-touch costs
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    ev_s = ev0.elapsed_time(ev1) / 1e3
+    per_launch = ev_s / K  # average launch duration on the launch stream (s)
+
+    if compute_bound:
+        value = alg_flops * K / wall / 1e9
+        unit = "GFLOP/s"
+        roof = {"bound": "mfma", "achieved": alg_flops / per_launch / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        value = weight_bytes * K / wall / 1e9
+        unit = "GB/s"
+        roof = {"bound": "hbm", "achieved": alg_bytes / per_launch / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(probs, compute_bound, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": desc,
+            "weight_bytes_per_step": weight_bytes,
+            "algorithmic_bytes_per_step": alg_bytes,
+            "algorithmic_flops_per_step": alg_flops,
+            "weight_copies_rotated": n_rot,
+            "launch": "eager" if graph is None else "one HIP graph of K kernel launches",
+            "pct_hbm_peak_weight_stream": None if compute_bound else 100.0 * value / HBM_PEAK_GBS,
+            "event_us_per_launch": per_launch * 1e6,
+            "plan": [wq.wq_describe_plan(p.fmt, p.O, p.I, p.S) for p in probs[:3]],
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+    if groups:
+        for g in groups:
+            wq.wq_grouped_free(g)
+    for c in copies:
+        for t in c:
+            wq.wq_tensor_free(t)
+
+
+def cpu_baseline(probs, compute_bound, seconds):
+    """The CPU oracle as it stands, on this host, for about `seconds` of work."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.default_threads()
+    # bounded sample: whole weight matrices, at most 16 activation rows of each
+    sample = []
+    for p in probs:
+        S = min(p.S, 16)
+        sample.append((p, p.x[:S]))
+    unit_work = sum((2.0 * x.shape[0] * p.O * p.I) if compute_bound else p.weight_bytes for p, x in sample)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for p, x in sample:
+            oracle.matmul(p.fmt, p.w, p.scales, x, threads=threads, want_bound=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    rate = unit_work * reps / el / 1e9
+    s_desc = "%d pass(es) over %s with S<=16 activation rows, %.1f s" % (
+        reps, "+".join(sorted(set(p.name.split("_")[0] for p, _ in sample)))[:60], el)
+    return {"value": rate, "unit": "GFLOP/s" if compute_bound else "GB/s", "cores": threads,
+            "kind": "oracle", "sample": s_desc}
+
+
+if __name__ == "__main__":
+    main()

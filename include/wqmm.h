@@ -1,0 +1,176 @@
+/*
+ * wqmm.h — C ABI of libwqmm.so, the weight-resident quantized matmul for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation (colibri "第 8 章 · 02 CUDA/Metal/Vulkan 三后端", section 四, the
+ * qmatmul.comp header; colibri-analysis "CUDA 后端", section 1, quant_matmul):
+ *
+ *     y[s,o] = scale[o] * sum_{i<I} dequant(W[o,i]) * x[s,i]
+ *
+ * W is an [O, I] weight matrix kept resident in device memory in one of four
+ * storage formats, with one fp32 scale per output row applied after the sum;
+ * x is fp32 [S, I] and y is fp32 [S, O], both row-major with s outer
+ * (x[s*I + i], y[s*O + o]).
+ *
+ * Storage formats (format list: colibri-analysis "CUDA 后端", section 1,
+ * row_bytes; codes 0..2 from the Vulkan tensor description in "第 8 章 · 02",
+ * section 三; dequant offsets from weight_at in the same section 1):
+ *   WQ_F32  4 bytes per element, little-endian IEEE single, used as is;
+ *   WQ_I8   1 byte per element, two's complement, used as is;
+ *   WQ_I4   2 elements per byte, even element in the low nibble,
+ *           value = nibble - 8;
+ *   WQ_I2   4 elements per byte, element 4j+k in bits 2k..2k+1 of byte j,
+ *           value = code - 2.
+ * A packed host row is row_bytes = ceil(I*bits/8) bytes; rows follow each
+ * other with no padding; unused high bits of a row's last byte are ignored.
+ *
+ * Accuracy contract: for every output element,
+ *     |y - y_exact| <= 1e-5 * sum_i |scale[o] * q[o,i] * x[s,i]| + 1e-30,
+ * and results are deterministic (same inputs, same launch configuration,
+ * same bits). Rows whose codes all decode to 0, rows with scale 0 and
+ * products that are exact integers sums are reproduced exactly.
+ *
+ * Errors: every function returns WQ_OK (0) or a negative WQ_E_* code; nothing
+ * aborts or exits, and on an error no output is written. A caller that gets
+ * an error may fall back to its own CPU path, as the reference engine does
+ * when its GPU call fails (colibri-analysis "CUDA 后端", section 3.1).
+ *
+ * Threads: calls on one device must not overlap from several host threads.
+ * Calls on different devices are independent.
+ */
+#ifndef WQMM_H
+#define WQMM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQ_MAX_DEVICES 16   /* size of the static device table */
+#define WQ_GEMV_MAX_S 8     /* default largest S served by the register GEMV */
+
+enum wq_fmt { WQ_F32 = 0, WQ_I8 = 1, WQ_I4 = 2, WQ_I2 = 3 };
+
+enum wq_status {
+    WQ_OK = 0,
+    WQ_E_INVAL = -1,       /* bad argument (NULL pointer, size, format, device list) */
+    WQ_E_NODEV = -2,       /* no usable GPU, or the device is not gfx950-capable */
+    WQ_E_NOTINIT = -3,     /* device not opened by wq_init */
+    WQ_E_OOM = -4,         /* device memory (or WQ_MEM_LIMIT_BYTES budget) exhausted */
+    WQ_E_MISMATCH = -5,    /* re-upload with a different device/format/shape */
+    WQ_E_HIP = -6,         /* the HIP runtime reported an error */
+    WQ_E_FAULT = -7,       /* failure injected with WQ_FAULT (tests of caller fallback) */
+    WQ_E_UNSUPPORTED = -8  /* valid request this build cannot serve */
+};
+
+typedef struct wq_tensor wq_tensor; /* opaque resident weight tensor */
+typedef struct wq_group wq_group;   /* opaque set of tensors run in one launch */
+
+/*
+ * Open devices (colibri-analysis "CUDA 后端", section 1, coli_cuda_init: the
+ * ordinals are validated and each GPU gets its own context).
+ * devices: host array of ndev ordinals; NULL with ndev == 0 opens device 0.
+ * Rejects duplicates, negative or out-of-range ordinals and ndev >
+ * WQ_MAX_DEVICES (WQ_E_INVAL); no GPU or a non-gfx950 GPU gives WQ_E_NODEV.
+ * Calling it again is allowed: already-open devices are kept, and the
+ * environment knobs are read again (WQ_FORCE_PATH=gemv|tiled|auto,
+ * WQ_GEMV_MAX_S, WQ_MEM_LIMIT_BYTES, WQ_FAULT=upload|launch, WQ_VERBOSE=1
+ * prints one line per device on stderr).
+ */
+int wq_init(const int *devices, int ndev);
+
+/*
+ * Free and total device memory in bytes (colibri-analysis "CUDA 后端",
+ * section 1, coli_cuda_mem_info). free_b/total_b: host pointers, either may be
+ * NULL. WQ_E_NOTINIT if the device was not opened.
+ */
+int wq_mem_info(int device, size_t *free_b, size_t *total_b);
+
+/* Bytes of one packed host row: ceil(I*bits/8); -1 for a bad fmt or I < 0.
+ * Host-only, needs no device. */
+long wq_row_bytes(int fmt, long I);
+
+/*
+ * Upload a weight tensor once and keep it resident (colibri-analysis
+ * "CUDA 后端", section 1, coli_cuda_tensor_upload; uploads happen lazily and
+ * once, colibri docs "CUDA backend (Linux)", introduction).
+ *   t:      in/out handle. *t == NULL: allocate, copy w and scales, set *t.
+ *           *t != NULL: nothing is copied; the call only checks that device,
+ *           fmt, O and I match the resident tensor (WQ_E_MISMATCH if not).
+ *   w:      host pointer to O packed rows of wq_row_bytes(fmt, I) bytes.
+ *   scales: host pointer to O floats; may be NULL only for WQ_F32 (scale 1).
+ * The copy is synchronous: the caller may free w and scales on return. The
+ * library owns the device copy until wq_tensor_free.
+ * Errors: WQ_E_INVAL (NULL t or w, bad fmt, O <= 0, I <= 0, missing scales),
+ * WQ_E_NOTINIT, WQ_E_OOM, WQ_E_HIP, WQ_E_FAULT (WQ_FAULT=upload).
+ */
+int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const void *w,
+                     const float *scales);
+
+/*
+ * Lazy upload plus a synchronous matmul on host buffers (colibri-analysis
+ * "CUDA 后端", section 1, coli_cuda_matmul: upload on first use, copy x in,
+ * run, copy y back, all blocking).
+ * Same tensor arguments as wq_tensor_upload; x: host [S, I] floats, y: host
+ * [S, O] floats (written). S == 0 uploads (if needed) and returns WQ_OK.
+ */
+int wq_matmul(wq_tensor **t, int device, int fmt, int O, int I, const void *w,
+              const float *scales, const float *x, int S, float *y);
+
+/* Synchronous matmul with an already-resident tensor; x, y host pointers. */
+int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
+
+/*
+ * Stream-ordered matmul on device buffers: one kernel launch on hip_stream
+ * (a hipStream_t; NULL = the device's null stream), no copies, no host
+ * synchronisation, no allocation. x_dev: device [S, I] floats, y_dev: device
+ * [S, O] floats, both on the tensor's device and 4-byte aligned. The call
+ * returns once the launch is queued; y_dev is valid after the stream reaches
+ * it. May be captured into a HIP graph.
+ */
+int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, void *hip_stream);
+
+/*
+ * Build a group of G resident tensors that run together in one launch (the
+ * grouped expert matmul of a mixture-of-experts decode step; grouped expert
+ * handling at prefill is described in colibri docs "CUDA backend (Linux)",
+ * section "The GPU-resident pipeline"). All tensors must be on the same
+ * device and share one format. The work split (balanced by weight bytes) is
+ * built once here and kept on the device. The group references the tensors:
+ * free the group before any of its tensors.
+ */
+int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
+
+/*
+ * Run every tensor of the group: y_dev[g] = matmul(ts[g], x_dev[g], S[g]).
+ * x_dev, S, y_dev: host arrays of G entries (device pointers inside);
+ * S[g] == 0 skips tensor g. One kernel launch on hip_stream when every
+ * S[g] <= the GEMV limit and every row fits the register GEMV; otherwise one
+ * launch per tensor, still stream-ordered and allocation-free.
+ */
+int wq_grouped_matmul_dev(wq_group *group, const float *const *x_dev, const int *S,
+                          float *const *y_dev, void *hip_stream);
+
+int wq_grouped_free(wq_group *group);
+
+/* Release a resident tensor (colibri-analysis "CUDA 后端", section 1,
+ * coli_cuda_tensor_free). NULL is a no-op. */
+int wq_tensor_free(wq_tensor *t);
+
+/* Static description of a status code; never NULL. */
+const char *wq_strerror(int code);
+
+/*
+ * Introspection for tests and tools: the kernel path wq_matmul_dev would take
+ * for (fmt, O, I, S) on this build, written as a NUL-terminated string into
+ * buf (e.g. "gemv fmt=2 smax=1 lw=16 k=3 team=1 r=2 grid=512 block=256").
+ * Host-only: needs no device. Returns WQ_OK or WQ_E_INVAL.
+ */
+int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQMM_H */

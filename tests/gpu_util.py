@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: device buffers with canaries, the bound check."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+import weight_only_quantized_matmul_amd as wq
+
+DEV = 0
+CANARY = np.float32(-1.2345678e-33).view(np.uint32)  # unlikely bit pattern, finite
+GUARD = 256  # floats of canary before and after every output
+
+
+def banner(msg: str):
+    """Name the case on stdout before a GPU step, flushed, so a fault report says where."""
+    sys.stdout.write("[gpu] %s\n" % msg)
+    sys.stdout.flush()
+
+
+def init():
+    wq.wq_init([DEV])
+
+
+def reinit_with_env(**env):
+    """Set WQ_* knobs (None removes one) and re-read them in the library."""
+    for k, v in env.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = str(v)
+    wq.wq_init([DEV])
+
+
+def upload(p):
+    return wq.wq_tensor_upload(None, DEV, p.fmt, p.O, p.I, p.w, p.scales)
+
+
+def guarded_output(S: int, O: int):
+    """(buffer, y view [S, O]); the view is surrounded by GUARD canary floats."""
+    buf = torch.empty(S * O + 2 * GUARD, dtype=torch.int32, device="cuda:%d" % DEV)
+    buf.fill_(int(np.int32(CANARY.view(np.int32))))
+    y = buf[GUARD:GUARD + S * O].view(torch.float32).view(S, O)
+    return buf, y
+
+
+def check_canaries(buf, S: int, O: int):
+    h = buf.cpu().numpy().view(np.uint32)
+    assert np.all(h[:GUARD] == CANARY), "write before the output buffer"
+    assert np.all(h[GUARD + S * O:] == CANARY), "write past the output buffer"
+
+
+def run_dev(t, x: np.ndarray, stream=None, x_offset: int = 0) -> np.ndarray:
+    """wq_matmul_dev on device copies of x; checks the canaries; returns y on the host.
+
+    x_offset > 0 places x at that many floats into a larger buffer (misaligned start).
+    """
+    S = x.shape[0]
+    xb = torch.zeros(x.size + x_offset, dtype=torch.float32, device="cuda:%d" % DEV)
+    xb[x_offset:] = torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).to(xb.device)
+    xd = xb[x_offset:].view(S, x.shape[1])
+    buf, y = guarded_output(S, t.O)
+    wq.wq_matmul_dev(t, xd, y, stream=stream)
+    torch.cuda.synchronize()
+    check_canaries(buf, S, t.O)
+    return y.cpu().numpy().copy()
+
+
+def bound_ratio(y: np.ndarray, y_ref: np.ndarray, A: np.ndarray) -> float:
+    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+    return float(np.max(err / (1e-5 * A + 1e-30))) if err.size else 0.0
+
+
+def assert_within_bound(y, y_ref, A, what=""):
+    assert y.shape == y_ref.shape, (y.shape, y_ref.shape)
+    assert np.all(np.isfinite(y)), "%s: non-finite output" % what
+    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+    bound = 1e-5 * A + 1e-30
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d of %d elements outside |y-y_ref| <= 1e-5*A + 1e-30; first %s; "
+                             "worst err/bound %.3g" % (what, int(bad.sum()), bad.size, idx.tolist(),
+                                                        float(np.max(err / bound))))

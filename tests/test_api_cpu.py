@@ -1,0 +1,178 @@
+"""C-ABI checks that need no GPU: exports, argument validation, plans, status strings."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import weight_only_quantized_matmul_amd as wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wqmm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("wq_init", "wq_mem_info", "wq_tensor_upload", "wq_matmul", "wq_matmul_t",
+                 "wq_matmul_dev", "wq_grouped_create", "wq_grouped_matmul_dev", "wq_grouped_free",
+                 "wq_tensor_free", "wq_strerror"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", wq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (wq_[a-z_]+)\b", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(wq.lib, n)
+
+
+def test_header_compiles_as_c_and_links():
+    prog = r'''
+#include "wqmm.h"
+#include <stdio.h>
+int main(void) {
+    int (*fns[])(void) = {0};
+    (void)fns;
+    printf("%ld %s\n", wq_row_bytes(WQ_I4, 7), wq_strerror(WQ_E_MISMATCH));
+    return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "t.c")
+        exe = os.path.join(tmp, "t")
+        open(c, "w").write(prog)
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), c,
+                        "-o", exe, wq.LIB_PATH, "-Wl,-rpath," + os.path.dirname(wq.LIB_PATH)],
+                       check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+        assert out.split()[0] == "4"
+
+
+def test_strerror_covers_every_code():
+    codes = [wq.WQ_OK, wq.WQ_E_INVAL, wq.WQ_E_NODEV, wq.WQ_E_NOTINIT, wq.WQ_E_OOM,
+             wq.WQ_E_MISMATCH, wq.WQ_E_HIP, wq.WQ_E_FAULT, wq.WQ_E_UNSUPPORTED]
+    texts = [wq.wq_strerror(c) for c in codes]
+    assert all(texts) and len(set(texts)) == len(texts)
+    assert "unknown" in wq.wq_strerror(12345)
+
+
+def test_row_bytes():
+    assert [wq.wq_row_bytes(f, 9) for f in range(4)] == [36, 9, 5, 3]
+    assert wq.wq_row_bytes(7, 9) == -1
+    assert wq.wq_row_bytes(wq.WQ_I4, -1) == -1
+
+
+def _plan(fmt, O, I, S):
+    s = wq.wq_describe_plan(fmt, O, I, S)
+    kind, *kv = s.split()
+    return kind, dict(item.split("=") for item in kv)
+
+
+@pytest.mark.parametrize("fmt,O,I,S", [
+    (wq.WQ_I4, 12288, 6144, 1), (wq.WQ_I2, 16384, 8192, 1), (wq.WQ_I2, 16384, 8192, 4),
+    (wq.WQ_I2, 16384, 8192, 8), (wq.WQ_I4, 2048, 6144, 1), (wq.WQ_I4, 6144, 2048, 1),
+    (wq.WQ_I8, 256, 512, 1), (wq.WQ_F32, 256, 512, 1), (wq.WQ_I4, 256, 512, 3), (wq.WQ_I2, 256, 512, 8),
+    (wq.WQ_I8, 7, 33, 5), (wq.WQ_F32, 1, 1, 1), (wq.WQ_I2, 3, 5, 2), (wq.WQ_F32, 100, 3000, 8),
+])
+def test_gemv_plan_invariants(fmt, O, I, S):
+    kind, p = _plan(fmt, O, I, S)
+    assert kind == "gemv"
+    p = {k: int(v) for k, v in p.items()}
+    stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
+    assert p["smax"] >= S and p["smax"] in (1, 2, 4, 8)
+    assert 1 <= p["team"] <= 8 and p["block"] <= 512 and p["block"] % 64 == 0
+    assert 1 <= p["k"] <= p["kmax"]
+    assert 64 * p["lw"] * p["team"] * p["k"] >= stride          # every byte of a row is covered
+    assert 64 * p["lw"] * p["team"] * (p["k"] - 1) < stride     # no empty slot
+    teams = p["grid"] * p["block"] // (64 * p["team"])
+    assert teams * p["rows_per_team"] >= O                      # every row is owned
+    assert (p["grid"] - 1) * p["block"] // (64 * p["team"]) * p["rows_per_team"] < O  # no idle block
+    assert p["rows_per_team"] % p["r"] == 0
+
+
+def test_headline_plan_shape():
+    kind, p = _plan(wq.WQ_I4, 12288, 6144, 1)
+    assert kind == "gemv" and p["team"] == "1" and p["k"] == "3" and p["lw"] == "16"
+
+
+@pytest.mark.parametrize("fmt,O,I,S", [(wq.WQ_I8, 6144, 6144, 512), (wq.WQ_I4, 100, 200, 9),
+                                       (wq.WQ_F32, 64, 300000, 8)])
+def test_tiled_plan(fmt, O, I, S):
+    kind, p = _plan(fmt, O, I, S)
+    assert kind == "tiled"
+    assert int(p["tiles_s"]) * int(p["bm"]) >= S and int(p["tiles_o"]) * int(p["bn"]) >= O
+    assert int(p["grid"]) == int(p["tiles_s"]) * int(p["tiles_o"])
+
+
+def test_plan_rejects_bad_arguments():
+    buf = ctypes.create_string_buffer(64)
+    assert wq.lib.wq_describe_plan(9, 4, 4, 1, buf, 64) == wq.WQ_E_INVAL
+    assert wq.lib.wq_describe_plan(0, 0, 4, 1, buf, 64) == wq.WQ_E_INVAL
+    assert wq.lib.wq_describe_plan(0, 4, 4, -1, buf, 64) == wq.WQ_E_INVAL
+    assert wq.lib.wq_describe_plan(0, 4, 4, 1, None, 64) == wq.WQ_E_INVAL
+
+
+# --- argument validation happens before any HIP call -------------------------------------
+
+
+def test_validation_without_device():
+    L = wq.lib
+    h = ctypes.c_void_p(None)
+    w = np.zeros(64, np.uint8)
+    sc = np.ones(4, np.float32)
+    assert L.wq_tensor_upload(None, 0, 1, 4, 16, w.ctypes.data, sc.ctypes.data) == wq.WQ_E_INVAL
+    assert L.wq_tensor_upload(ctypes.byref(h), 0, 9, 4, 16, w.ctypes.data, sc.ctypes.data) == wq.WQ_E_INVAL
+    assert L.wq_tensor_upload(ctypes.byref(h), 0, 1, 0, 16, w.ctypes.data, sc.ctypes.data) == wq.WQ_E_INVAL
+    assert L.wq_tensor_upload(ctypes.byref(h), 0, 1, 4, 0, w.ctypes.data, sc.ctypes.data) == wq.WQ_E_INVAL
+    assert L.wq_tensor_upload(ctypes.byref(h), -1, 1, 4, 16, w.ctypes.data, sc.ctypes.data) == wq.WQ_E_INVAL
+    assert L.wq_tensor_upload(ctypes.byref(h), 16, 1, 4, 16, w.ctypes.data, sc.ctypes.data) == wq.WQ_E_INVAL
+    assert L.wq_tensor_upload(ctypes.byref(h), 0, 1, 4, 16, None, sc.ctypes.data) == wq.WQ_E_INVAL
+    assert L.wq_tensor_upload(ctypes.byref(h), 0, 1, 4, 16, w.ctypes.data, None) == wq.WQ_E_INVAL
+    # valid arguments, device never opened
+    rc = L.wq_tensor_upload(ctypes.byref(h), 5, 1, 4, 16, w.ctypes.data, sc.ctypes.data)
+    assert rc == wq.WQ_E_NOTINIT and h.value is None
+    assert L.wq_matmul_t(None, None, 1, None) == wq.WQ_E_INVAL
+    assert L.wq_matmul_dev(None, None, 1, None, None) == wq.WQ_E_INVAL
+    assert L.wq_matmul(None, 0, 1, 4, 16, None, None, None, -1, None) == wq.WQ_E_INVAL
+    assert L.wq_matmul(ctypes.byref(h), 0, 1, 4, 16, w.ctypes.data, sc.ctypes.data, None, 2, None) == wq.WQ_E_INVAL
+    assert L.wq_grouped_create(None, 1, ctypes.byref(h)) == wq.WQ_E_INVAL
+    assert L.wq_grouped_matmul_dev(None, None, None, None, None) == wq.WQ_E_INVAL
+    assert L.wq_tensor_free(None) == wq.WQ_OK
+    assert L.wq_grouped_free(None) == wq.WQ_OK
+    assert L.wq_mem_info(-1, None, None) == wq.WQ_E_INVAL
+    assert L.wq_mem_info(7, None, None) == wq.WQ_E_NOTINIT
+
+
+def test_init_rejects_bad_device_lists():
+    L = wq.lib
+    dup = (ctypes.c_int * 2)(0, 0)
+    neg = (ctypes.c_int * 1)(-1)
+    big = (ctypes.c_int * 1)(16)
+    many = (ctypes.c_int * 17)(*range(17))
+    assert L.wq_init(dup, 2) == wq.WQ_E_INVAL
+    assert L.wq_init(neg, 1) == wq.WQ_E_INVAL
+    assert L.wq_init(big, 1) == wq.WQ_E_INVAL
+    assert L.wq_init(many, 17) == wq.WQ_E_INVAL
+    assert L.wq_init(None, 2) == wq.WQ_E_INVAL
+    assert L.wq_init(None, -1) == wq.WQ_E_INVAL
+
+
+def test_init_without_gpu_reports_nodev():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; the no-device path is exercised on GPU-less hosts")
+    assert wq.lib.wq_init(None, 0) == wq.WQ_E_NODEV

@@ -1,0 +1,163 @@
+"""GPU tests of the C ABI around the kernels: host-pointer calls, lazy upload,
+re-upload validation, memory info, injected failures, graph capture."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU hosts
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gpu_util as gu  # noqa: E402
+import weight_only_quantized_matmul_amd as wq  # noqa: E402
+
+I8, I4, I2 = 1, 2, 3
+
+
+@pytest.fixture(autouse=True)
+def device():
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+    yield
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+
+
+def test_mem_info():
+    free, total = wq.wq_mem_info(0)
+    assert 0 < free <= total
+    assert total > 200 * 2**30  # MI355X carries 288 GB of HBM3E
+
+
+def test_lazy_matmul_uploads_once_and_matches_oracle():
+    p = synth.ragged(I4, 500, 1000, 3, seed=11)
+    gu.banner("wq_matmul lazy")
+    t, y = wq.wq_matmul(None, 0, p.fmt, p.O, p.I, p.w, p.scales, p.x)
+    try:
+        y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+        gu.assert_within_bound(y, y_ref, A, "wq_matmul")
+        # second call with the handle: no upload; garbage weights are not even read
+        t2, y2 = wq.wq_matmul(t, 0, p.fmt, p.O, p.I, None, None, p.x)
+        assert t2 is t
+        np.testing.assert_array_equal(y, y2)
+        y3 = wq.wq_matmul_t(t, p.x)
+        np.testing.assert_array_equal(y, y3)
+        # the device-pointer path gives the same bits
+        np.testing.assert_array_equal(gu.run_dev(t, p.x), y)
+    finally:
+        wq.wq_tensor_free(t)
+
+
+def test_reupload_validates_only():
+    p = synth.ragged(I8, 10, 20, 1, seed=12)
+    t = wq.wq_tensor_upload(None, 0, p.fmt, p.O, p.I, p.w, p.scales)
+    try:
+        assert wq.wq_tensor_upload(t, 0, p.fmt, p.O, p.I, None, None) is t
+        for bad in [(0, I4, p.O, p.I), (0, p.fmt, p.O + 1, p.I), (0, p.fmt, p.O, p.I + 1)]:
+            with pytest.raises(wq.WqError) as e:
+                wq.wq_tensor_upload(t, *bad, None, None)
+            assert e.value.code == wq.WQ_E_MISMATCH
+    finally:
+        wq.wq_tensor_free(t)
+
+
+def test_s_zero_is_a_noop():
+    p = synth.ragged(I2, 10, 20, 1, seed=13)
+    t = gu.upload(p)
+    try:
+        x = np.zeros((0, p.I), np.float32)
+        assert wq.wq_matmul_t(t, x).shape == (0, p.O)
+        assert wq.lib.wq_matmul_dev(t.ptr, None, 0, None, None) == wq.WQ_OK
+    finally:
+        wq.wq_tensor_free(t)
+
+
+def test_host_call_large_then_small_reuses_scratch():
+    big = synth.ragged(I4, 3000, 4000, 8, seed=14)
+    small = synth.ragged(I4, 3000, 4000, 1, seed=15)
+    small.w, small.scales = big.w, big.scales
+    t = gu.upload(big)
+    try:
+        for p in (big, small, big):
+            y = wq.wq_matmul_t(t, p.x)
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+            gu.assert_within_bound(y, y_ref, A, "host S=%d" % p.S)
+    finally:
+        wq.wq_tensor_free(t)
+
+
+def test_injected_launch_failure_leaves_output_untouched():
+    p = synth.ragged(I4, 64, 128, 2, seed=16)
+    t = gu.upload(p)
+    try:
+        gu.reinit_with_env(WQ_FAULT="launch")
+        xd = torch.from_numpy(p.x).cuda()
+        buf, y = gu.guarded_output(p.S, p.O)
+        with pytest.raises(wq.WqError) as e:
+            wq.wq_matmul_dev(t, xd, y)
+        assert e.value.code == wq.WQ_E_FAULT
+        torch.cuda.synchronize()
+        gu.check_canaries(buf, 0, p.O)  # nothing written at all
+        with pytest.raises(wq.WqError):
+            wq.wq_matmul_t(t, p.x)
+    finally:
+        gu.reinit_with_env(WQ_FAULT=None)
+        wq.wq_tensor_free(t)
+
+
+def test_injected_upload_failure_and_memory_budget():
+    p = synth.ragged(I4, 64, 128, 1, seed=17)
+    gu.reinit_with_env(WQ_FAULT="upload")
+    with pytest.raises(wq.WqError) as e:
+        gu.upload(p)
+    assert e.value.code == wq.WQ_E_FAULT
+    gu.reinit_with_env(WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=1000)
+    with pytest.raises(wq.WqError) as e:
+        gu.upload(p)  # 64*64 + 256 bytes > 1000
+    assert e.value.code == wq.WQ_E_OOM
+    gu.reinit_with_env(WQ_MEM_LIMIT_BYTES=None)
+    t = gu.upload(p)
+    wq.wq_tensor_free(t)
+
+
+def test_grouped_rejects_mixed_formats():
+    a = gu.upload(synth.ragged(I4, 8, 16, 1, seed=18))
+    b = gu.upload(synth.ragged(I8, 8, 16, 1, seed=19))
+    try:
+        with pytest.raises(wq.WqError) as e:
+            wq.wq_grouped_create([a, b])
+        assert e.value.code == wq.WQ_E_INVAL
+    finally:
+        wq.wq_tensor_free(a)
+        wq.wq_tensor_free(b)
+
+
+def test_graph_capture_replays_match_eager():
+    p = synth.ragged(I4, 4096, 2048, 1, seed=20)
+    t = gu.upload(p)
+    try:
+        x = torch.from_numpy(p.x).cuda()
+        y_eager = torch.empty((p.S, p.O), device="cuda")
+        wq.wq_matmul_dev(t, x, y_eager)
+        torch.cuda.synchronize()
+        y_graph = torch.zeros_like(y_eager)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            wq.wq_matmul_dev(t, x, y_graph)
+        torch.cuda.synchronize()
+        for i in range(4):
+            y_graph.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_graph, y_eager), "replay %d differs" % i
+            wq.wq_matmul_dev(t, x, y_eager)  # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        wq.wq_tensor_free(t)

@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: for every output element |y_gpu - y_ref| <= 1e-5 * sum_i |scale*q*x| + 1e-30
+(the oracle returns that magnitude alongside y); bit-exact where the exact
+result is representable (one-hot activations, all-zero code rows, zero scales,
+integer activations). Outputs are written between canary guards.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU hosts
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gpu_util as gu  # noqa: E402
+import weight_only_quantized_matmul_amd as wq  # noqa: E402
+
+F32, I8, I4, I2 = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_GEMV_MAX_S=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+    yield
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_GEMV_MAX_S=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+
+
+def check_problem(p, what, x_offset=0, rows=None):
+    t = gu.upload(p)
+    try:
+        gu.banner("%s fmt=%d O=%d I=%d S=%d plan=%s" % (what, p.fmt, p.O, p.I, p.S,
+                                                        wq.wq_describe_plan(p.fmt, p.O, p.I, p.S)))
+        y = gu.run_dev(t, p.x, x_offset=x_offset)
+    finally:
+        wq.wq_tensor_free(t)
+    if rows is None:
+        y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x, I=p.I)
+        gu.assert_within_bound(y, y_ref, A, what)
+    else:
+        y_ref, A = oracle.matmul_rows(p.fmt, p.w, p.scales, p.x, rows, I=p.I)
+        gu.assert_within_bound(y[:, rows], y_ref, A, what)
+    return y
+
+
+# ---------------------------------------------------------------------------------------
+# the five workloads
+
+
+@pytest.mark.parametrize("fmt", [F32, I8, I4, I2])
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8])
+def test_tiny_all_formats(fmt, S):
+    p = synth.tiny(fmt, S=S)
+    check_problem(p, "tiny")
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_tiny_f32_integer_weights_and_null_scales(S):
+    p = synth.tiny(F32, S=S, f32_variant="int8")
+    check_problem(p, "tiny-f32-int8")
+    p.scales = None
+    check_problem(p, "tiny-f32-null-scales")
+
+
+def test_tiny_cross_format_same_codes_identical():
+    """The same int8 draw presented as f32 (exact integers) and int8 gives the same bits."""
+    p8 = synth.tiny(I8, S=1)
+    pf = synth.tiny(F32, S=1, f32_variant="int8")
+    pf.x, pf.scales = p8.x, p8.scales
+    t8, tf = gu.upload(p8), gu.upload(pf)
+    try:
+        y8 = gu.run_dev(t8, p8.x)
+        yf = gu.run_dev(tf, pf.x)
+    finally:
+        wq.wq_tensor_free(t8)
+        wq.wq_tensor_free(tf)
+    y_ref, A = oracle.matmul(I8, p8.w, p8.scales, p8.x)
+    gu.assert_within_bound(y8, y_ref, A, "i8")
+    gu.assert_within_bound(yf, y_ref, A, "f32")
+
+
+def test_dense_gemv_int4_full():
+    check_problem(synth.dense_gemv(S=1), "dense_gemv")
+
+
+@pytest.mark.parametrize("S", [1, 4, 8])
+def test_int2_gemv_full(S):
+    check_problem(synth.int2_gemv(S=S), "int2_gemv")
+
+
+def test_prefill_int8_s512_sampled():
+    p = synth.prefill(S=512)
+    t = gu.upload(p)
+    try:
+        gu.banner("prefill plan=%s" % wq.wq_describe_plan(p.fmt, p.O, p.I, p.S))
+        y = gu.run_dev(t, p.x)
+    finally:
+        wq.wq_tensor_free(t)
+    g = synth.rng(777)
+    # every output row o for a sample of activation rows s (incl. the ragged last tile) ...
+    s_rows = np.unique(np.concatenate([g.choice(512, 40, replace=False), [0, 63, 64, 511]]))
+    y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x[s_rows])
+    gu.assert_within_bound(y[s_rows], y_ref, A, "prefill rows")
+    # ... and every s for a sample of output columns
+    o_cols = np.unique(np.concatenate([g.choice(6144, 48, replace=False), [0, 63, 64, 6143]]))
+    y_ref2, A2 = oracle.matmul_rows(p.fmt, p.w, p.scales, p.x, o_cols)
+    gu.assert_within_bound(y[:, o_cols], y_ref2, A2, "prefill cols")
+
+
+def test_moe_decode_grouped_one_launch():
+    probs = synth.moe_decode()
+    ts = [gu.upload(p) for p in probs]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x).cuda() for p in probs]
+        bufs, ys = zip(*[gu.guarded_output(p.S, p.O) for p in probs])
+        gu.banner("moe grouped G=%d" % len(probs))
+        wq.wq_grouped_matmul_dev(g, xs, list(ys))
+        torch.cuda.synchronize()
+        got = []
+        for p, b, y in zip(probs, bufs, ys):
+            gu.check_canaries(b, p.S, p.O)
+            got.append(y.cpu().numpy())
+        # bit-identical to the one-tensor launches (same lane/column split and reduction order)
+        for p, t, yg in zip(probs, ts, got):
+            y1 = gu.run_dev(t, p.x)
+            np.testing.assert_array_equal(yg, y1)
+        for p, yg in zip(probs, got):
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+            gu.assert_within_bound(yg, y_ref, A, p.name)
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
+def test_grouped_mixed_S_and_skips():
+    probs = synth.moe_decode(n_experts=3, S=1)
+    g0 = synth.rng(5)
+    # give experts different activation counts, one skipped
+    Ss = [3, 3, 3, 0, 0, 0, 7, 7, 7]
+    for p, S in zip(probs, Ss):
+        p.x = synth.activations(g0, S, p.I) if S else None
+    ts = [gu.upload(p) for p in probs]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x).cuda() if p.x is not None else None for p in probs]
+        outs = [gu.guarded_output(max(p.x.shape[0], 1) if p.x is not None else 1, p.O) for p in probs]
+        ys = [o[1] if p.x is not None else None for o, p in zip(outs, probs)]
+        gu.banner("grouped mixed S")
+        wq.wq_grouped_matmul_dev(g, xs, ys)
+        torch.cuda.synchronize()
+        for p, (b, y) in zip(probs, outs):
+            if p.x is None:
+                gu.check_canaries(b, 0, p.O)  # untouched
+                continue
+            gu.check_canaries(b, p.x.shape[0], p.O)
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, p.name)
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
+# ---------------------------------------------------------------------------------------
+# ragged shapes, both paths
+
+
+RAGGED = [
+    (F32, 1, 1, 1), (F32, 7, 13, 3), (F32, 33, 257, 9), (F32, 300, 1000, 17),
+    (I8, 1, 1, 1), (I8, 5, 17, 2), (I8, 65, 1025, 8), (I8, 129, 700, 33), (I8, 200, 96, 70),
+    (I4, 1, 1, 1), (I4, 3, 5, 4), (I4, 17, 33, 7), (I4, 1000, 1027, 1), (I4, 70, 2049, 12),
+    (I2, 1, 3, 1), (I2, 9, 5, 2), (I2, 31, 129, 5), (I2, 600, 4097, 8), (I2, 50, 515, 65),
+    (I4, 2500, 40000, 1), (I2, 100, 65000, 2), (F32, 40, 20000, 1),
+]
+
+
+@pytest.mark.parametrize("fmt,O,I,S", RAGGED)
+def test_ragged_shapes(fmt, O, I, S):
+    p = synth.ragged(fmt, O, I, S, seed=1000 + O * 7 + I * 3 + S)
+    check_problem(p, "ragged")
+
+
+@pytest.mark.parametrize("fmt,O,I,S", [(I4, 37, 301, 3), (I2, 20, 77, 1), (I8, 9, 43, 12), (F32, 11, 19, 2)])
+def test_misaligned_activations(fmt, O, I, S):
+    p = synth.ragged(fmt, O, I, S, seed=55 + O)
+    check_problem(p, "misaligned-x", x_offset=1)
+
+
+@pytest.mark.parametrize("path", ["gemv", "tiled"])
+@pytest.mark.parametrize("fmt,O,I,S", [(I4, 300, 777, 1), (I2, 64, 1024, 8), (I8, 128, 513, 5),
+                                       (F32, 33, 100, 8), (I4, 129, 64, 2)])
+def test_forced_paths_agree(path, fmt, O, I, S):
+    p = synth.ragged(fmt, O, I, S, seed=90 + O + S)
+    try:
+        gu.reinit_with_env(WQ_FORCE_PATH=path)
+        check_problem(p, "forced-" + path)
+    finally:
+        gu.reinit_with_env(WQ_FORCE_PATH=None)
+
+
+@pytest.mark.parametrize("S", [8, 9, 16])
+def test_gemv_tiled_crossover(S):
+    p = synth.ragged(I4, 257, 1111, S, seed=31337 + S)
+    check_problem(p, "crossover")
+
+
+# ---------------------------------------------------------------------------------------
+# bit-exact pins on the GPU
+
+
+@pytest.mark.parametrize("fmt,I", [(I8, 256), (I4, 512), (I2, 1024)])
+@pytest.mark.parametrize("S", [1, 8, 24])
+def test_exhaustive_codes_one_hot_bit_exact(fmt, I, S):
+    row = np.arange(256, dtype=np.uint8)[None, :]
+    O = 5
+    w = np.repeat(row, O, axis=0)
+    sc = np.array([1.0, 0.0137, 3.5, 0.001, 123.25], dtype=np.float32)
+    g = synth.rng(fmt * 10 + S)
+    p = synth.Problem("exhaustive", fmt, O, I, w, sc, None)
+    t = gu.upload(p)
+    try:
+        for c0 in range(0, I, S * 8):
+            cols = np.arange(c0, min(I, c0 + S * 8), 8)[:S]
+            cols = (cols + g.integers(0, 8, size=cols.size)).clip(max=I - 1)
+            x = np.zeros((cols.size, I), np.float32)
+            x[np.arange(cols.size), cols] = 1.0
+            y = gu.run_dev(t, x)
+            y_ref, _ = oracle.matmul(fmt, w, sc, x)
+            np.testing.assert_array_equal(y, y_ref)
+    finally:
+        wq.wq_tensor_free(t)
+
+
+@pytest.mark.parametrize("fmt,zero", [(I8, 0x00), (I4, 0x88), (I2, 0xAA), (F32, 0x00)])
+@pytest.mark.parametrize("S", [1, 8, 40])
+def test_zero_code_rows_and_zero_scales_exact(fmt, zero, S):
+    p = synth.ragged(fmt, 67, 900, S, seed=4000 + fmt + S)
+    p.w[5] = zero
+    p.w[60] = zero
+    p.scales[7] = 0.0
+    p.scales[66] = 0.0
+    y = check_problem(p, "zeros")
+    for o in (5, 60, 7, 66):
+        assert np.all(y[:, o] == 0.0), o
+
+
+@pytest.mark.parametrize("fmt", [I8, I4, I2, F32])
+@pytest.mark.parametrize("S", [1, 3, 8, 20])
+def test_integer_activations_bit_exact(fmt, S):
+    p = synth.ragged(fmt, 150, 1500, S, seed=5000 + fmt + S)
+    if fmt == F32:  # f32 weights holding small integers keep every partial sum exact
+        p.w = synth.f32_from_int8(synth.int8_uniform(synth.rng(5), p.O, p.I, -20, 20))
+    p.x = synth.rng(6 + S).integers(-4, 5, size=(S, p.I)).astype(np.float32)
+    t = gu.upload(p)
+    try:
+        y = gu.run_dev(t, p.x)
+    finally:
+        wq.wq_tensor_free(t)
+    y_ref, _ = oracle.matmul(fmt, p.w, p.scales, p.x)
+    np.testing.assert_array_equal(y, y_ref)
+
+
+def test_deterministic_repeat():
+    p = synth.ragged(I4, 5000, 3000, 1, seed=99)
+    t = gu.upload(p)
+    try:
+        y1 = gu.run_dev(t, p.x)
+        y2 = gu.run_dev(t, p.x)
+    finally:
+        wq.wq_tensor_free(t)
+    np.testing.assert_array_equal(y1, y2)

@@ -1,0 +1,595 @@
+// libwqmm runtime: device table, resident tensors, groups, dispatch and the
+// C ABI declared in include/wqmm.h.
+//
+// Shape of the contract (colibri-analysis "CUDA 后端", section 1): a
+// self-contained extern "C" library that opens devices, reports memory,
+// uploads a quantized [O, I] tensor once (re-uploads only validate), runs the
+// matmul and frees tensors; every GPU failure is reported to the caller, who
+// may fall back to the CPU (same page, section 3.1). Startup problems (no
+// device, bad ordinals) are errors, not a silent CPU mode (colibri docs
+// "CUDA backend (Linux)", introduction).
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "wq_internal.h"
+
+namespace {
+
+struct DeviceCtx {
+    bool open = false;
+    hipStream_t stream = nullptr;  // library stream for the host-pointer calls
+    int cus = 0;
+    size_t total_mem = 0;
+    char name[256] = {0};
+    char arch[64] = {0};
+    float *d_x = nullptr;
+    size_t x_cap = 0;  // bytes
+    float *d_y = nullptr;
+    size_t y_cap = 0;  // bytes
+    size_t lib_bytes = 0;  // device bytes held by tensors and groups
+    std::mutex mu;
+};
+
+struct Config {
+    int force_path = 0;  // 0 auto, 1 gemv, 2 tiled
+    int gemv_max_s = WQ_GEMV_MAX_S;
+    long long mem_limit = 0;  // 0: none
+    int fault = 0;            // 0 none, 1 upload, 2 launch
+    int verbose = 0;
+    int waves_per_cu = 8;
+};
+
+DeviceCtx g_dev[WQ_MAX_DEVICES];
+Config g_cfg;
+std::mutex g_init_mu;
+
+constexpr int kDefaultCUs = 256;  // MI355X; used by the host-only plan description
+
+void read_env(Config &c) {
+    c = Config();
+    if (const char *v = getenv("WQ_FORCE_PATH")) {
+        if (!strcmp(v, "gemv")) c.force_path = 1;
+        else if (!strcmp(v, "tiled")) c.force_path = 2;
+    }
+    if (const char *v = getenv("WQ_GEMV_MAX_S")) {
+        int n = atoi(v);
+        if (n >= 0 && n <= 8) c.gemv_max_s = n;
+    }
+    if (const char *v = getenv("WQ_MEM_LIMIT_BYTES")) c.mem_limit = atoll(v);
+    if (const char *v = getenv("WQ_FAULT")) {
+        if (!strcmp(v, "upload")) c.fault = 1;
+        else if (!strcmp(v, "launch")) c.fault = 2;
+    }
+    if (const char *v = getenv("WQ_VERBOSE")) c.verbose = atoi(v);
+    if (const char *v = getenv("WQ_WAVES_PER_CU")) {
+        int n = atoi(v);
+        if (n >= 1 && n <= 32) c.waves_per_cu = n;
+    }
+}
+
+// Makes `dev` current for the scope, restoring the caller's device after.
+struct DeviceGuard {
+    int prev = -1;
+    bool switched = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev) {
+            switched = hipSetDevice(dev) == hipSuccess;
+        }
+    }
+    ~DeviceGuard() {
+        if (switched) (void)hipSetDevice(prev);
+    }
+};
+
+bool valid_fmt(int fmt) { return fmt >= WQ_F32 && fmt <= WQ_I2; }
+
+bool tensor_ok(const wq_tensor *t) { return t != nullptr && t->magic == wq::kTensorMagic; }
+
+bool device_open(int dev) { return dev >= 0 && dev < WQ_MAX_DEVICES && g_dev[dev].open; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return WQ_OK;
+    if (e == hipErrorOutOfMemory) return WQ_E_OOM;
+    return WQ_E_HIP;
+}
+
+int dev_alloc(DeviceCtx &d, void **p, size_t bytes) {
+    if (g_cfg.mem_limit > 0 && (long long)(d.lib_bytes + bytes) > g_cfg.mem_limit) return WQ_E_OOM;
+    if (hipMalloc(p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        return WQ_E_OOM;
+    }
+    d.lib_bytes += bytes;
+    return WQ_OK;
+}
+
+void dev_free(DeviceCtx &d, void *p, size_t bytes) {
+    if (p) {
+        (void)hipFree(p);
+        d.lib_bytes -= std::min(d.lib_bytes, bytes);
+    }
+}
+
+// Which path a call takes. Returns 1 (gemv) or 2 (tiled).
+int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp) {
+    if (g_cfg.force_path != 2 && S <= g_cfg.gemv_max_s) {
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu);
+        if (gp->ok) return 1;
+    }
+    if (g_cfg.force_path == 1) {
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu);
+        if (gp->ok) return 1;
+    }
+    return 2;
+}
+
+int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t st) {
+    const DeviceCtx &d = g_dev[t->device];
+    wq::GemvPlan gp;
+    if (choose_path(t->fmt, t->O, t->I, S, d.cus, &gp) == 1) {
+        wq::GemvArgs a;
+        a.w = t->d_w;
+        a.scales = t->d_scales;
+        a.x = x;
+        a.y = y;
+        a.stride = t->stride;
+        a.O = t->O;
+        a.I = t->I;
+        a.S = S;
+        a.k = gp.k;
+        a.team = gp.team;
+        a.teams_per_block = gp.teams_per_block;
+        a.rows_per_team = gp.rows_per_team;
+        return hip_status(wq::launch_gemv(gp, a, st));
+    }
+    const wq::TiledPlan tp = wq::plan_tiled(t->fmt, t->O, t->I, S);
+    wq::TiledArgs a;
+    a.w = t->d_w;
+    a.scales = t->d_scales;
+    a.x = x;
+    a.y = y;
+    a.stride = t->stride;
+    a.O = t->O;
+    a.I = t->I;
+    a.S = S;
+    a.tiles_s = tp.tiles_s;
+    a.tiles_o = tp.tiles_o;
+    return hip_status(wq::launch_tiled(t->fmt, tp, a, st));
+}
+
+int ensure_scratch(DeviceCtx &d, size_t xb, size_t yb) {
+    if (xb > d.x_cap) {
+        if (d.d_x) (void)hipFree(d.d_x);
+        d.d_x = nullptr;
+        d.x_cap = 0;
+        if (hipMalloc((void **)&d.d_x, xb) != hipSuccess) {
+            (void)hipGetLastError();
+            return WQ_E_OOM;
+        }
+        d.x_cap = xb;
+    }
+    if (yb > d.y_cap) {
+        if (d.d_y) (void)hipFree(d.d_y);
+        d.d_y = nullptr;
+        d.y_cap = 0;
+        if (hipMalloc((void **)&d.d_y, yb) != hipSuccess) {
+            (void)hipGetLastError();
+            return WQ_E_OOM;
+        }
+        d.y_cap = yb;
+    }
+    return WQ_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int wq_init(const int *devices, int ndev) {
+    if (ndev < 0 || ndev > WQ_MAX_DEVICES) return WQ_E_INVAL;
+    if (ndev > 0 && devices == nullptr) return WQ_E_INVAL;
+    int list[WQ_MAX_DEVICES];
+    int n = ndev;
+    if (ndev == 0) {
+        list[0] = 0;
+        n = 1;
+    } else {
+        for (int i = 0; i < ndev; ++i) {
+            if (devices[i] < 0 || devices[i] >= WQ_MAX_DEVICES) return WQ_E_INVAL;
+            for (int j = 0; j < i; ++j)
+                if (devices[j] == devices[i]) return WQ_E_INVAL;
+            list[i] = devices[i];
+        }
+    }
+    std::lock_guard<std::mutex> lk(g_init_mu);
+    read_env(g_cfg);
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return WQ_E_NODEV;
+    }
+    for (int i = 0; i < n; ++i)
+        if (list[i] >= count) return WQ_E_INVAL;
+    for (int i = 0; i < n; ++i) {
+        DeviceCtx &d = g_dev[list[i]];
+        if (d.open) continue;
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, list[i]) != hipSuccess) return WQ_E_HIP;
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return WQ_E_NODEV;
+        DeviceGuard guard(list[i]);
+        hipStream_t st = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return WQ_E_HIP;
+        d.stream = st;
+        d.cus = prop.multiProcessorCount;
+        d.total_mem = prop.totalGlobalMem;
+        snprintf(d.name, sizeof d.name, "%s", prop.name);
+        snprintf(d.arch, sizeof d.arch, "%s", prop.gcnArchName);
+        d.open = true;
+        if (g_cfg.verbose)
+            fprintf(stderr, "wqmm: device %d: %s (%s), %.1f GiB, %d CUs\n", list[i], d.name, d.arch,
+                    d.total_mem / 1073741824.0, d.cus);
+    }
+    return WQ_OK;
+}
+
+int wq_mem_info(int device, size_t *free_b, size_t *total_b) {
+    if (device < 0 || device >= WQ_MAX_DEVICES) return WQ_E_INVAL;
+    if (!device_open(device)) return WQ_E_NOTINIT;
+    DeviceGuard guard(device);
+    size_t f = 0, t = 0;
+    if (hipMemGetInfo(&f, &t) != hipSuccess) return WQ_E_HIP;
+    if (free_b) *free_b = f;
+    if (total_b) *total_b = t;
+    return WQ_OK;
+}
+
+long wq_row_bytes(int fmt, long I) { return wq::row_bytes(fmt, I); }
+
+int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const void *w, const float *scales) {
+    if (t == nullptr) return WQ_E_INVAL;
+    if (!valid_fmt(fmt) || O <= 0 || I <= 0 || device < 0 || device >= WQ_MAX_DEVICES) return WQ_E_INVAL;
+    if (*t != nullptr) {
+        const wq_tensor *r = *t;
+        if (!tensor_ok(r)) return WQ_E_INVAL;
+        if (r->device != device || r->fmt != fmt || r->O != O || r->I != I) return WQ_E_MISMATCH;
+        return WQ_OK;
+    }
+    if (w == nullptr) return WQ_E_INVAL;
+    if (scales == nullptr && fmt != WQ_F32) return WQ_E_INVAL;
+    if (!device_open(device)) return WQ_E_NOTINIT;
+    if (g_cfg.fault == 1) return WQ_E_FAULT;
+    DeviceCtx &d = g_dev[device];
+    std::lock_guard<std::mutex> lk(d.mu);
+    DeviceGuard guard(device);
+
+    const long rb = wq::row_bytes(fmt, I);
+    const long stride = wq::round_up(rb, wq::kRowAlign);
+    const size_t wbytes = (size_t)O * stride;
+    const size_t sbytes = (size_t)O * sizeof(float);
+    void *dw = nullptr, *ds = nullptr;
+    int rc = dev_alloc(d, &dw, wbytes);
+    if (rc != WQ_OK) return rc;
+    rc = dev_alloc(d, &ds, sbytes);
+    if (rc != WQ_OK) {
+        dev_free(d, dw, wbytes);
+        return rc;
+    }
+    hipError_t e = hipSuccess;
+    if (stride != rb) {
+        e = hipMemsetAsync(dw, 0, wbytes, d.stream);
+        if (e == hipSuccess)
+            e = hipMemcpy2DAsync(dw, stride, w, rb, rb, O, hipMemcpyHostToDevice, d.stream);
+    } else {
+        e = hipMemcpyAsync(dw, w, wbytes, hipMemcpyHostToDevice, d.stream);
+    }
+    std::vector<float> ones;
+    if (e == hipSuccess) {
+        const float *src = scales;
+        if (src == nullptr) {
+            ones.assign(O, 1.0f);
+            src = ones.data();
+        }
+        e = hipMemcpyAsync(ds, src, sbytes, hipMemcpyHostToDevice, d.stream);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(d.stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        dev_free(d, dw, wbytes);
+        dev_free(d, ds, sbytes);
+        return hip_status(e);
+    }
+    wq_tensor *nt = new (std::nothrow) wq_tensor;
+    if (!nt) {
+        dev_free(d, dw, wbytes);
+        dev_free(d, ds, sbytes);
+        return WQ_E_OOM;
+    }
+    nt->magic = wq::kTensorMagic;
+    nt->device = device;
+    nt->fmt = fmt;
+    nt->O = O;
+    nt->I = I;
+    nt->rb = rb;
+    nt->stride = stride;
+    nt->d_w = (uint8_t *)dw;
+    nt->d_scales = (float *)ds;
+    nt->bytes = wbytes + sbytes;
+    *t = nt;
+    return WQ_OK;
+}
+
+int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y) {
+    if (!tensor_ok(t) || S < 0) return WQ_E_INVAL;
+    if (S == 0) return WQ_OK;
+    if (x == nullptr || y == nullptr) return WQ_E_INVAL;
+    if (!device_open(t->device)) return WQ_E_NOTINIT;
+    if (g_cfg.fault == 2) return WQ_E_FAULT;
+    DeviceCtx &d = g_dev[t->device];
+    std::lock_guard<std::mutex> lk(d.mu);
+    DeviceGuard guard(t->device);
+    const size_t xb = (size_t)S * t->I * sizeof(float);
+    const size_t yb = (size_t)S * t->O * sizeof(float);
+    int rc = ensure_scratch(d, xb, yb);
+    if (rc != WQ_OK) return rc;
+    hipError_t e = hipMemcpyAsync(d.d_x, x, xb, hipMemcpyHostToDevice, d.stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_status(e);
+    }
+    rc = run_matmul(t, d.d_x, S, d.d_y, d.stream);
+    if (rc != WQ_OK) {
+        (void)hipStreamSynchronize(d.stream);
+        return rc;
+    }
+    e = hipMemcpyAsync(y, d.d_y, yb, hipMemcpyDeviceToHost, d.stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(d.stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_status(e);
+    }
+    return WQ_OK;
+}
+
+int wq_matmul(wq_tensor **t, int device, int fmt, int O, int I, const void *w, const float *scales,
+              const float *x, int S, float *y) {
+    if (S < 0) return WQ_E_INVAL;
+    if (S > 0 && (x == nullptr || y == nullptr)) return WQ_E_INVAL;
+    int rc = wq_tensor_upload(t, device, fmt, O, I, w, scales);
+    if (rc != WQ_OK) return rc;
+    return wq_matmul_t(*t, x, S, y);
+}
+
+int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, void *hip_stream) {
+    if (!tensor_ok(t) || S < 0) return WQ_E_INVAL;
+    if (S == 0) return WQ_OK;
+    if (x_dev == nullptr || y_dev == nullptr) return WQ_E_INVAL;
+    if (((uintptr_t)x_dev & 3) || ((uintptr_t)y_dev & 3)) return WQ_E_INVAL;
+    if (!device_open(t->device)) return WQ_E_NOTINIT;
+    if (g_cfg.fault == 2) return WQ_E_FAULT;
+    DeviceGuard guard(t->device);
+    return run_matmul(t, x_dev, S, y_dev, (hipStream_t)hip_stream);
+}
+
+int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
+    if (ts == nullptr || group == nullptr || G <= 0) return WQ_E_INVAL;
+    for (int i = 0; i < G; ++i)
+        if (!tensor_ok(ts[i])) return WQ_E_INVAL;
+    const int dev = ts[0]->device, fmt = ts[0]->fmt;
+    for (int i = 1; i < G; ++i)
+        if (ts[i]->device != dev || ts[i]->fmt != fmt) return WQ_E_INVAL;
+    if (!device_open(dev)) return WQ_E_NOTINIT;
+    DeviceCtx &d = g_dev[dev];
+    std::lock_guard<std::mutex> lk(d.mu);
+    DeviceGuard guard(dev);
+
+    wq_group *g = new (std::nothrow) wq_group;
+    if (!g) return WQ_E_OOM;
+    g->magic = wq::kGroupMagic;
+    g->device = dev;
+    g->fmt = fmt;
+    g->G = G;
+    g->ts.assign(ts, ts + G);
+    g->d_desc = nullptr;
+    for (int i = 0; i < G; ++i) {
+        wq::GroupDesc gd;
+        gd.w = ts[i]->d_w;
+        gd.scales = ts[i]->d_scales;
+        gd.stride = ts[i]->stride;
+        gd.O = ts[i]->O;
+        gd.I = ts[i]->I;
+        g->h_desc.push_back(gd);
+    }
+    auto fail = [&](int rc) {
+        for (auto &b : g->buckets)
+            if (b.d_items) dev_free(d, b.d_items, (size_t)b.plan.n_items * sizeof(wq::WorkItem));
+        if (g->d_desc) dev_free(d, g->d_desc, (size_t)G * sizeof(wq::GroupDesc));
+        g->magic = 0;
+        delete g;
+        return rc;
+    };
+    int rc = dev_alloc(d, (void **)&g->d_desc, (size_t)G * sizeof(wq::GroupDesc));
+    if (rc != WQ_OK) return fail(rc);
+    hipError_t e = hipMemcpyAsync(g->d_desc, g->h_desc.data(), (size_t)G * sizeof(wq::GroupDesc),
+                                  hipMemcpyHostToDevice, d.stream);
+    if (e != hipSuccess) return fail(hip_status(e));
+    // Work tables for every S bucket, built now so later calls never allocate.
+    for (int bi = 0; bi < 4; ++bi) {
+        auto &bk = g->buckets[bi];
+        const int smax = 1 << bi;
+        const wq::GemvShape sh = wq::gemv_shape(fmt, smax);
+        bk = wq_group::Bucket();
+        bk.plan.smax = smax;
+        bk.plan.lw = sh.lw;
+        bk.plan.kmax = sh.kmax;
+        bk.plan.r = sh.r;
+        const long per_wave = 64L * sh.lw * sh.kmax;
+        long total = 0;
+        bool fits = true;
+        for (const auto &gd : g->h_desc) {
+            if (gd.stride > per_wave) fits = false;
+            total += (long)gd.O * gd.stride;
+        }
+        if (!fits) continue;
+        const long target_items = std::max(1L, (long)d.cus * g_cfg.waves_per_cu);
+        const long bytes_per_item = std::max(1L, (total + target_items - 1) / target_items);
+        std::vector<wq::WorkItem> items;
+        for (int c0 = 0; c0 < G; c0 += wq::kGroupMaxPerLaunch) {
+            bk.first_item.push_back((int)items.size());
+            const int c1 = std::min(G, c0 + wq::kGroupMaxPerLaunch);
+            for (int p = c0; p < c1; ++p) {
+                const auto &gd = g->h_desc[p];
+                long rows = (bytes_per_item + gd.stride - 1) / gd.stride;
+                rows = std::max<long>(sh.r, (rows + sh.r - 1) / sh.r * sh.r);
+                const int k = (int)((gd.stride + 64L * sh.lw - 1) / (64L * sh.lw));
+                for (long r0 = 0; r0 < gd.O; r0 += rows) {
+                    wq::WorkItem it;
+                    it.p = p - c0;
+                    it.row_begin = (int)r0;
+                    it.row_end = (int)std::min<long>(gd.O, r0 + rows);
+                    it.k = k;
+                    items.push_back(it);
+                }
+            }
+            bk.n_items.push_back((int)items.size() - bk.first_item.back());
+        }
+        bk.plan.n_items = (int)items.size();
+        rc = dev_alloc(d, (void **)&bk.d_items, items.size() * sizeof(wq::WorkItem));
+        if (rc != WQ_OK) return fail(rc);
+        e = hipMemcpyAsync(bk.d_items, items.data(), items.size() * sizeof(wq::WorkItem),
+                           hipMemcpyHostToDevice, d.stream);
+        if (e != hipSuccess) return fail(hip_status(e));
+        e = hipStreamSynchronize(d.stream);  // `items` goes out of scope
+        if (e != hipSuccess) return fail(hip_status(e));
+        bk.plan.ok = true;
+        bk.built = true;
+    }
+    e = hipStreamSynchronize(d.stream);
+    if (e != hipSuccess) return fail(hip_status(e));
+    *group = g;
+    return WQ_OK;
+}
+
+int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, float *const *y_dev,
+                          void *hip_stream) {
+    if (g == nullptr || g->magic != wq::kGroupMagic) return WQ_E_INVAL;
+    if (x_dev == nullptr || S == nullptr || y_dev == nullptr) return WQ_E_INVAL;
+    int smax = 0;
+    for (int i = 0; i < g->G; ++i) {
+        if (S[i] < 0) return WQ_E_INVAL;
+        if (S[i] > 0) {
+            if (x_dev[i] == nullptr || y_dev[i] == nullptr) return WQ_E_INVAL;
+            if (((uintptr_t)x_dev[i] & 3) || ((uintptr_t)y_dev[i] & 3)) return WQ_E_INVAL;
+            if (!tensor_ok(g->ts[i])) return WQ_E_INVAL;
+        }
+        smax = std::max(smax, S[i]);
+    }
+    if (smax == 0) return WQ_OK;
+    if (!device_open(g->device)) return WQ_E_NOTINIT;
+    if (g_cfg.fault == 2) return WQ_E_FAULT;
+    DeviceGuard guard(g->device);
+    hipStream_t st = (hipStream_t)hip_stream;
+    const int bucket = wq::gemv_smax_bucket(smax);
+    const int bi = bucket == 1 ? 0 : bucket == 2 ? 1 : bucket == 4 ? 2 : bucket == 8 ? 3 : -1;
+    const bool one_launch = g_cfg.force_path != 2 && smax <= g_cfg.gemv_max_s && bi >= 0 &&
+                            g->buckets[bi].plan.ok;
+    if (!one_launch) {
+        for (int i = 0; i < g->G; ++i) {
+            if (S[i] == 0) continue;
+            int rc = run_matmul(g->ts[i], x_dev[i], S[i], y_dev[i], st);
+            if (rc != WQ_OK) return rc;
+        }
+        return WQ_OK;
+    }
+    const auto &bk = g->buckets[bi];
+    for (size_t c = 0; c < bk.first_item.size(); ++c) {
+        const int c0 = (int)c * wq::kGroupMaxPerLaunch;
+        const int c1 = std::min(g->G, c0 + wq::kGroupMaxPerLaunch);
+        bool any = false;
+        wq::GroupedArgs a;
+        memset(&a, 0, sizeof a);
+        a.desc = g->d_desc + c0;
+        a.items = bk.d_items + bk.first_item[c];
+        a.n_items = bk.n_items[c];
+        for (int p = c0; p < c1; ++p) {
+            a.x[p - c0] = x_dev[p];
+            a.y[p - c0] = y_dev[p];
+            a.S[p - c0] = S[p];
+            any = any || S[p] > 0;
+        }
+        if (!any || a.n_items == 0) continue;
+        wq::GroupedPlan gp = bk.plan;
+        gp.grid = (a.n_items + 3) / 4;
+        gp.block = 256;
+        int rc = hip_status(wq::launch_grouped(g->fmt, gp, a, st));
+        if (rc != WQ_OK) return rc;
+    }
+    return WQ_OK;
+}
+
+int wq_grouped_free(wq_group *g) {
+    if (g == nullptr) return WQ_OK;
+    if (g->magic != wq::kGroupMagic) return WQ_E_INVAL;
+    DeviceCtx &d = g_dev[g->device];
+    std::lock_guard<std::mutex> lk(d.mu);
+    DeviceGuard guard(g->device);
+    for (auto &b : g->buckets)
+        if (b.d_items) dev_free(d, b.d_items, (size_t)b.plan.n_items * sizeof(wq::WorkItem));
+    if (g->d_desc) dev_free(d, g->d_desc, (size_t)g->G * sizeof(wq::GroupDesc));
+    g->magic = 0;
+    delete g;
+    return WQ_OK;
+}
+
+int wq_tensor_free(wq_tensor *t) {
+    if (t == nullptr) return WQ_OK;
+    if (!tensor_ok(t)) return WQ_E_INVAL;
+    DeviceCtx &d = g_dev[t->device];
+    std::lock_guard<std::mutex> lk(d.mu);
+    DeviceGuard guard(t->device);
+    dev_free(d, t->d_w, (size_t)t->O * t->stride);
+    dev_free(d, t->d_scales, (size_t)t->O * sizeof(float));
+    t->magic = 0;
+    delete t;
+    return WQ_OK;
+}
+
+const char *wq_strerror(int code) {
+    switch (code) {
+    case WQ_OK: return "success";
+    case WQ_E_INVAL: return "invalid argument";
+    case WQ_E_NODEV: return "no usable gfx950 device";
+    case WQ_E_NOTINIT: return "device not initialised (call wq_init)";
+    case WQ_E_OOM: return "out of device memory (or over WQ_MEM_LIMIT_BYTES)";
+    case WQ_E_MISMATCH: return "resident tensor differs from the re-upload request";
+    case WQ_E_HIP: return "HIP runtime error";
+    case WQ_E_FAULT: return "injected failure (WQ_FAULT)";
+    case WQ_E_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status code";
+    }
+}
+
+int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
+    if (!valid_fmt(fmt) || O <= 0 || I <= 0 || S < 0 || buf == nullptr || buflen == 0) return WQ_E_INVAL;
+    const int cus = device_open(0) ? g_dev[0].cus : kDefaultCUs;
+    if (S == 0) {
+        snprintf(buf, buflen, "none");
+        return WQ_OK;
+    }
+    wq::GemvPlan gp;
+    if (choose_path(fmt, O, I, S, cus, &gp) == 1) {
+        snprintf(buf, buflen, "gemv fmt=%d smax=%d lw=%d kmax=%d k=%d team=%d r=%d rows_per_team=%d grid=%d block=%d",
+                 fmt, gp.smax, gp.lw, gp.kmax, gp.k, gp.team, gp.r, gp.rows_per_team, gp.grid, gp.block);
+    } else {
+        const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S);
+        snprintf(buf, buflen, "tiled fmt=%d bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d grid=%d block=%d", fmt, tp.bm,
+                 tp.bn, tp.bk, tp.tiles_s, tp.tiles_o, tp.grid, tp.block);
+    }
+    return WQ_OK;
+}
+
+} // extern "C"
