@@ -101,7 +101,7 @@ def test_gemv_plan_invariants(fmt, O, I, S):
     teams = p["grid"] * p["block"] // (64 * p["team"])
     assert teams * p["rows_per_team"] >= O                      # every row is owned
     assert (p["grid"] - 1) * p["block"] // (64 * p["team"]) * p["rows_per_team"] < O  # no idle block
-    assert p["rows_per_team"] % p["r"] == 0
+    assert p["rows_per_team"] % p["d"] == 0
 
 
 def test_headline_plan_shape():

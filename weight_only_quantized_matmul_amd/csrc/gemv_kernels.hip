@@ -6,13 +6,18 @@
 //    weight_at; scale after the sum, same section, quant_matmul)
 //
 // Design (gfx950, wave64):
-//  * A "team" of 1..8 waves owns a set of consecutive output rows. Each lane
-//    owns fixed byte slices of every row: slot k covers bytes
-//    [(k*team_lanes + lane)*LW, +LW), so one wave-wide load is LW*64
-//    contiguous bytes (1 KiB for LW = 16) of the row, read once, non-temporal.
-//  * The activations of a lane's columns are loaded once into registers
-//    (SMAX rows of them) and reused for every row the team processes; the
-//    weight stream is the only per-row memory traffic.
+//  * A "team" of 1..8 waves owns rows [row_begin, row_begin + rows_per_team).
+//    Lane slot k covers the row bytes [(k*team_lanes + lane)*LW, +LW): one
+//    wave-wide load is LW*64 contiguous bytes (1 KiB for LW = 16), read once,
+//    non-temporal.
+//  * With the device layout (see wq_internal.h) the activations that meet a
+//    lane's weight fields are 4-element runs that are contiguous across the
+//    wave, so each lane's activations are staged once into registers with
+//    fully coalesced 16-byte loads and reused for every row of the team.
+//  * Each wave keeps D rows of weights in flight (a register ring): row r is
+//    reduced while rows r+1..r+D-1 are still arriving, and its registers are
+//    refilled with row r+D right after. Reloads in the steady state are
+//    unconditional so the wait counts stay exact.
 //  * Dequantization happens in registers on 32-bit words. For int4 and int2
 //    the code offset is folded out of the inner loop: codes are converted
 //    unshifted (byte masks + v_cvt_f32_ubyteN, with the activations of the
@@ -22,7 +27,9 @@
 //    zero gives exactly 0.
 //  * Lanes are reduced with DPP (quad_perm, row_shr, row_bcast) instead of an
 //    LDS tree; teams of several waves add their wave totals through LDS in a
-//    fixed order, so results are deterministic.
+//    fixed order, so results are deterministic. Row scales are read with
+//    scalar loads (the row index is wave-uniform), which do not wait on the
+//    weight stream.
 #include "wq_internal.h"
 
 namespace wq {
@@ -37,7 +44,7 @@ template <> struct FmtInfo<WQ_I8>  { static constexpr int EPW = 4;  static const
 template <> struct FmtInfo<WQ_I4>  { static constexpr int EPW = 8;  static constexpr int OFF = 8; };
 template <> struct FmtInfo<WQ_I2>  { static constexpr int EPW = 16; static constexpr int OFF = 2; };
 
-// Factor applied to the activation that meets element e (0..EPW-1) of a word,
+// Factor applied to the activation that meets field e (0..EPW-1) of a word,
 // compensating the unshifted field position used by the folded dequant.
 template <int FMT> __device__ constexpr float x_prescale(int e) {
     if (FMT == WQ_I4) return (e & 1) ? 0.0625f : 1.0f;
@@ -67,7 +74,7 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
-// acc[s] += sum over the EPW elements of one word of code * xw[e][s].
+// acc[s] += sum over the EPW fields of one word of code * xw[e][s].
 template <int FMT, int SMAX>
 __device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], float (&acc)[SMAX]) {
     if constexpr (FMT == WQ_F32) {
@@ -82,8 +89,8 @@ __device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], fl
             for (int s = 0; s < SMAX; ++s) acc[s] = __builtin_fmaf(q, xw[b][s], acc[s]);
         }
     } else if constexpr (FMT == WQ_I4) {
-        const uint32_t lo = opaque(w & 0x0F0F0F0Fu);  // even elements, code in bits 0..3 of each byte
-        const uint32_t hi = opaque(w & 0xF0F0F0F0u);  // odd elements, 16 * code
+        const uint32_t lo = opaque(w & 0x0F0F0F0Fu);  // even fields, code in bits 0..3 of each byte
+        const uint32_t hi = opaque(w & 0xF0F0F0F0u);  // odd fields, 16 * code
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float cl = (float)((lo >> (8 * b)) & 0xFFu);
@@ -132,147 +139,268 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
     return v;
 }
 
-// One team processes rows [row_begin, row_end).
-template <int FMT, int SMAX, int LW, int KMAX, int R>
-__device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long stride,
-                                          const float *__restrict__ scales,
-                                          const float *__restrict__ x, float *__restrict__ y, int O,
-                                          int I, int S, int K, int team, int tl, int wave_in_team,
-                                          int row_begin, int row_end, float *red) {
+// One team processes rows [row_begin, row_begin + rpt) (rows >= O are not
+// stored). red: LDS scratch of 2 * kMaxTeam * D * SMAX floats, used when
+// team > 1 (then the block is exactly one team).
+template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool XL = false>
+__device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long stride, int nfull,
+                                          const float *__restrict__ scales, const float *__restrict__ x,
+                                          float *__restrict__ y, int O, int I, int S, int team, int tl,
+                                          int wave_in_team, int row_begin, int rpt, float *red) {
+    // KMAX is the exact number of load slots per lane: every slot is loaded
+    // unconditionally (a slot past the row re-reads the row start, see
+    // below), which keeps the compiler's memory wait counts exact.
+    constexpr int K = KMAX;
     constexpr int EPW = FmtInfo<FMT>::EPW;
     constexpr int OFF = FmtInfo<FMT>::OFF;
     constexpr int WPC = LW / 4;     // 32-bit words per lane load
-    constexpr int EPC = WPC * EPW;  // elements per lane load
+    constexpr int EPC = WPC * EPW;  // fields per lane load
     const int team_lanes = team * 64;
     const int lane = threadIdx.x & 63;
+    const int row_last = min(O, row_begin + rpt) - 1;
 
-    // ---- stage this lane's activations in registers (pre-scaled), and sum(x)
+    // Byte offset of slot k inside a row. A lane whose slice starts past the
+    // row (only possible in the last slot) re-reads the row start: its
+    // activations are zero, so quantized codes contribute nothing; f32
+    // values are zeroed explicitly (inf * 0 would not vanish). Offsets are
+    // 32-bit so loads use a wave-uniform base plus a per-lane offset.
+    uint32_t cb[KMAX];
+    bool live[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const uint32_t c = (uint32_t)(k * team_lanes + tl) * LW;
+        live[k] = c < (uint32_t)stride;
+        cb[k] = live[k] ? c : 0u;
+    }
+
+    // ---- stage this lane's activations in registers (pre-scaled), and sum(x).
+    // Phase 1 issues every load in straight-line code (indices clamped into
+    // the row, so no lane branches); phase 2 masks, pre-scales and sums in
+    // place once the data is there.
     float xr[KMAX][EPC][SMAX];
+    // The 4-field runs of one slot lie in a single 16-byte granule, so their
+    // first elements form an arithmetic progression: step 256 inside a
+    // permuted block, step 4 in natural order (f32 rows, last partial block).
+    int xb[KMAX], xs_step[KMAX];
+    bool lane_in = true;  // every run of every slot of this lane lies inside x
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int c = (k * team_lanes + tl) * LW;  // this slot's first byte
+        if (FMT == WQ_F32 || c >= nfull * kBlockBytes) {
+            xb[k] = (FMT == WQ_F32) ? c / 4 : c * (EPW / 4);
+            xs_step[k] = 4;
+        } else {
+            const int r = c & (kBlockBytes - 1);
+            const int n0 = (r & 15) * (EPW / 4);  // first field of the slot in its granule
+            xb[k] = (c - r) * (EPW / 4) + 256 * (n0 >> 2) + 4 * (r >> 4);
+            xs_step[k] = 256;
+        }
+        lane_in = lane_in && live[k] && xb[k] + xs_step[k] * (EPC / 4 - 1) + 4 <= I;
+    }
+    // wave-uniform: no activation of this wave needs masking
+    const bool wave_in = __builtin_amdgcn_ballot_w64(!lane_in) == 0;
+#define WQ_XE(k, g) (xb[k] + xs_step[k] * (g))
+    if constexpr (XV) {  // x 16-byte aligned and I % 4 == 0: a run is entirely inside or outside the row
+        // (with XL, x points at the block's LDS copy of the activations)
+        const uint32_t last4 = (uint32_t)(I - 4) * 4u;  // clamp: runs past the row are masked below
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const uint32_t b4 = (uint32_t)xb[k] * 4u, st4 = (uint32_t)xs_step[k] * 4u;
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s)
+                if (s < S) {
+                    const char *xs = reinterpret_cast<const char *>(x + (long)s * I);  // wave-uniform base
+#pragma unroll
+                    for (int g = 0; g < EPC / 4; ++g) {
+                        const uint32_t off = min(b4 + st4 * (uint32_t)g, last4);
+                        const float4 t = *reinterpret_cast<const float4 *>(xs + off);
+                        xr[k][4 * g][s] = t.x;
+                        xr[k][4 * g + 1][s] = t.y;
+                        xr[k][4 * g + 2][s] = t.z;
+                        xr[k][4 * g + 3][s] = t.w;
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s)
+                if (s < S) {
+                    const float *xs = x + (long)s * I;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) {
+                        const int ei = WQ_XE(k, e / 4) + (e & 3);
+                        xr[k][e][s] = xs[(live[k] && ei < I) ? ei : 0];
+                    }
+                }
+    }
+    // Weight ring prologue, issued after the activation loads: the
+    // activations (cache hits) complete first and are prepared while the
+    // first rows stream in.
+    uint32_t ring[D][KMAX][WPC];
+    auto load_row = [&](uint32_t (&b)[KMAX][WPC], int row) {
+        const uint8_t *p = w + (long)min(row, row_last) * stride;  // wave-uniform
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) load_w<LW>(p + cb[k], b[k]);
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_row(ring[d], row_begin + d);
+
     float sx[SMAX];
 #pragma unroll
     for (int s = 0; s < SMAX; ++s) sx[s] = 0.0f;
-    const bool vec_ok = ((I & 3) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    if (wave_in) {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        const long cb = (long)(k * team_lanes + tl) * LW;
-        const long e0 = cb / 4 * EPW;
+        for (int k = 0; k < KMAX; ++k)
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) {
-            float v[EPC];
+            for (int s = 0; s < SMAX; ++s)
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) v[e] = 0.0f;
-            if (k < K && s < S) {
-                const float *xs = x + (long)s * I + e0;
-                if (vec_ok && e0 + EPC <= I) {
-#pragma unroll
-                    for (int e = 0; e < EPC; e += 4) {
-                        const float4 t = *reinterpret_cast<const float4 *>(xs + e);
-                        v[e] = t.x; v[e + 1] = t.y; v[e + 2] = t.z; v[e + 3] = t.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e)
-                        if (e0 + e < I) v[e] = xs[e];
+                for (int e = 0; e < EPC; ++e) {
+                    const float v = s < S ? xr[k][e][s] : 0.0f;
+                    xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
+                    if constexpr (OFF != 0) sx[s] += v;
                 }
-            }
+    } else {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                xr[k][e][s] = v[e] * x_prescale<FMT>(e % EPW);
-                if constexpr (OFF != 0) sx[s] += v[e];
-            }
-        }
+        for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    const int ei = WQ_XE(k, e / 4) + (e & 3);
+                    const bool in = s < S && live[k] && ei < I;
+                    const float v = in ? xr[k][e][s] : 0.0f;
+                    xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
+                    if constexpr (OFF != 0) sx[s] += v;
+                }
     }
+#undef WQ_XE
 
-    // ---- stream rows
-    for (int row0 = row_begin; row0 < row_end; row0 += R) {
-        uint32_t wv[R][KMAX][WPC];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int o = min(row0 + r, row_end - 1);
-            const uint8_t *p = w + (long)o * stride;
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                const long cb = (long)(k * team_lanes + tl) * LW;
-                if (k < K && cb < stride) {
-                    load_w<LW>(p + cb, wv[r][k]);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < WPC; ++j) wv[r][k][j] = 0u;
-                }
-            }
-        }
-        float acc[R][SMAX];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int s = 0; s < SMAX; ++s) acc[r][s] = 0.0f;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
+    // Partial sums of one row (wave total in lane 63).
+    auto row_partials = [&](uint32_t (&b)[KMAX][WPC], float (&part)[SMAX]) {
+        if constexpr (FMT == WQ_F32) {
 #pragma unroll
             for (int k = 0; k < KMAX; ++k)
-                if (k < K) {
+                if (!live[k]) {
 #pragma unroll
-                    for (int j = 0; j < WPC; ++j) word_fma<FMT, SMAX>(wv[r][k][j], &xr[k][j * EPW], acc[r]);
+                    for (int j = 0; j < WPC; ++j) b[k][j] = 0u;
                 }
+        }
+        float acc[SMAX];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int s = 0; s < SMAX; ++s) acc[s] = 0.0f;
 #pragma unroll
-            for (int s = 0; s < SMAX; ++s) {
-                float t = acc[r][s];
-                if constexpr (OFF != 0) t -= (float)OFF * sx[s];
-                acc[r][s] = wave_sum_lane63(t);
+        for (int k = 0; k < KMAX; ++k)
+            if (k < K) {
+#pragma unroll
+                for (int j = 0; j < WPC; ++j) word_fma<FMT, SMAX>(b[k][j], &xr[k][j * EPW], acc);
             }
-        if (team == 1) {
-            if (lane == 63) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int o = row0 + r;
-                    if (o < row_end) {
-                        const float sc = scales[o];
+        for (int s = 0; s < SMAX; ++s) {
+            float t = acc[s];
+            if constexpr (OFF != 0) t -= (float)OFF * sx[s];
+            part[s] = wave_sum_lane63(t);
+        }
+    };
+
+    // Finish D rows starting at row0: part[d][s] holds this wave's totals.
+    int pb = 0;
+    auto finish = [&](int row0, float (&part)[D][SMAX], int nvalid) {
+        if (team == 1) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (d < nvalid) {
+                    const int row = row0 + d;
+                    const float sc = scales[min(row, O - 1)];  // wave-uniform: scalar load
+                    if (lane == 63 && row <= row_last) {
 #pragma unroll
                         for (int s = 0; s < SMAX; ++s)
-                            if (s < S) y[(long)s * O + o] = sc * acc[r][s];
+                            if (s < S) y[(long)s * O + row] = sc * part[d][s];
                     }
                 }
             }
         } else {
+            float *rbuf = red + pb * (kMaxTeam * D * SMAX);
             if (lane == 63) {
 #pragma unroll
-                for (int r = 0; r < R; ++r)
+                for (int d = 0; d < D; ++d)
 #pragma unroll
-                    for (int s = 0; s < SMAX; ++s) red[(wave_in_team * R + r) * SMAX + s] = acc[r][s];
+                    for (int s = 0; s < SMAX; ++s) rbuf[(wave_in_team * D + d) * SMAX + s] = part[d][s];
             }
+            float sc[D];  // wave-uniform rows: scalar loads
+#pragma unroll
+            for (int d = 0; d < D; ++d) sc[d] = scales[min(row0 + d, O - 1)];
             __syncthreads();
-            if (wave_in_team == 0 && lane < R * SMAX) {
-                const int r = lane / SMAX, s = lane % SMAX;
+            if (wave_in_team == 0 && lane < D * SMAX) {
+                const int d = lane / SMAX, s = lane % SMAX;
+                const int row = row0 + d;
                 float t = 0.0f;
-                for (int wv2 = 0; wv2 < team; ++wv2) t += red[(wv2 * R + r) * SMAX + s];
-                const int o = row0 + r;
-                if (o < row_end && s < S) y[(long)s * O + o] = scales[o] * t;
+                for (int w2 = 0; w2 < team; ++w2) t += rbuf[(w2 * D + d) * SMAX + s];
+                float scd = sc[0];
+#pragma unroll
+                for (int j = 1; j < D; ++j) scd = (d == j) ? sc[j] : scd;
+                if (d < nvalid && row <= row_last && s < S) y[(long)s * O + row] = scd * t;
             }
-            __syncthreads();
+            pb ^= 1;
         }
+    };
+
+    // ---- stream rows through the ring
+    int i = 0;
+    for (; i + D < rpt; i += D) {
+        float part[D][SMAX];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            row_partials(ring[d], part[d]);
+            load_row(ring[d], row_begin + i + d + D);
+        }
+        finish(row_begin + i, part, D);
+    }
+    {
+        float part[D][SMAX];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (i + d < rpt) {
+                row_partials(ring[d], part[d]);
+            } else {
+#pragma unroll
+                for (int s = 0; s < SMAX; ++s) part[d][s] = 0.0f;
+            }
+        }
+        finish(row_begin + i, part, rpt - i);
     }
 }
 
-constexpr int kMaxTeam = 8;
-
-template <int FMT, int SMAX, int LW, int KMAX, int R>
+// XL: the block first copies the S x I activations into LDS (one coalesced
+// pass per block instead of one per wave) and the waves stage their
+// registers from there; used when x fits (host check) and XV holds.
+template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool XL>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
-    __shared__ float red[kMaxTeam * R * SMAX];
+    __shared__ float red[2 * kMaxTeam * D * SMAX];
+    extern __shared__ __attribute__((aligned(16))) float xl[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int team_in_block = wave / a.team;
     const int wave_in_team = wave - team_in_block * a.team;
     const int team_id = blockIdx.x * a.teams_per_block + team_in_block;
     const int row_begin = team_id * a.rows_per_team;
+    const float *xsrc = a.x;
+    if constexpr (XL) {
+        const int n4 = a.S * a.I / 4;
+        const float4 *src = reinterpret_cast<const float4 *>(a.x);
+        float4 *dst = reinterpret_cast<float4 *>(xl);
+        for (int i = threadIdx.x; i < n4; i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+        xsrc = xl;
+    }
     if (row_begin >= a.O) return;  // uniform over the team (and the block when team > 1)
-    const int row_end = min(a.O, row_begin + a.rows_per_team);
-    team_rows<FMT, SMAX, LW, KMAX, R>(a.w, a.stride, a.scales, a.x, a.y, a.O, a.I, a.S, a.k, a.team,
-                                      wave_in_team * 64 + lane, wave_in_team, row_begin, row_end, red);
+    team_rows<FMT, SMAX, LW, KS, D, XV, XL>(a.w, a.stride, a.nfull, a.scales, xsrc, a.y, a.O, a.I, a.S, a.team,
+                                            wave_in_team * 64 + lane, wave_in_team, row_begin, a.rows_per_team,
+                                            red);
 }
 
-template <int FMT, int SMAX, int LW, int KMAX, int R>
+template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV>
 __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -283,23 +411,43 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
     const int S = a.S[p];
     if (S <= 0) return;
     const GroupDesc d = a.desc[p];
-    team_rows<FMT, SMAX, LW, KMAX, R>(d.w, d.stride, d.scales, a.x[p], a.y[p], d.O, d.I, S, it.k, 1, lane, 0,
-                                      it.row_begin, it.row_end, nullptr);
+    const int r0 = __builtin_amdgcn_readfirstlane(it.row_begin);
+    const int nr = __builtin_amdgcn_readfirstlane(it.row_end - it.row_begin);
+    // exact slot count of this problem's rows (wave-uniform)
+    switch (__builtin_amdgcn_readfirstlane(it.k)) {
+#define WQ_GROUP_K(KS)                                                                                        \
+    case KS:                                                                                                  \
+        if constexpr (KS <= KMAX)                                                                             \
+            team_rows<FMT, SMAX, LW, KS, D, XV>(d.w, d.stride, d.nfull, d.scales, a.x[p], a.y[p], d.O, d.I, S, 1, \
+                                                lane, 0, r0, nr, nullptr);                                    \
+        break;
+        WQ_GROUP_K(1) WQ_GROUP_K(2) WQ_GROUP_K(3) WQ_GROUP_K(4)
+#undef WQ_GROUP_K
+    default: break;
+    }
 }
 
 // ---- compiled shapes -------------------------------------------------------
-// (fmt, S bucket) -> bytes per lane load, load slots, rows in flight.
-// Register budget: KMAX * (LW/4 * EPW) * SMAX activation registers
-// (64 for f32/int8, 128 for int4/int2).
+// (fmt, S bucket) -> bytes per lane load, load slots, ring depth.
+// Registers: activations KMAX * (LW/4 * EPW) * SMAX, ring D * KMAX * LW/4.
 #define WQ_SHAPES(X)                                   \
-    X(WQ_F32, 1, 16, 16, 1) X(WQ_F32, 2, 16, 8, 2)     \
+    X(WQ_F32, 1, 16, 4, 2) X(WQ_F32, 2, 16, 4, 2)      \
     X(WQ_F32, 4, 16, 4, 2) X(WQ_F32, 8, 16, 2, 2)      \
     X(WQ_I8, 1, 16, 4, 2) X(WQ_I8, 2, 16, 2, 2)        \
     X(WQ_I8, 4, 16, 1, 4) X(WQ_I8, 8, 8, 1, 4)         \
     X(WQ_I4, 1, 16, 4, 2) X(WQ_I4, 2, 16, 2, 2)        \
     X(WQ_I4, 4, 16, 1, 4) X(WQ_I4, 8, 8, 1, 4)         \
-    X(WQ_I2, 1, 16, 2, 4) X(WQ_I2, 2, 16, 1, 4)        \
+    X(WQ_I2, 1, 16, 2, 2) X(WQ_I2, 2, 16, 1, 4)        \
     X(WQ_I2, 4, 8, 1, 4) X(WQ_I2, 8, 4, 1, 4)
+
+__global__ void relayout_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int fmt, int O,
+                                long rb, long stride, int nfull) {
+    const long n = (long)O * stride;
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const long o = i / stride, p = i - o * stride;
+        dst[i] = p < rb ? src[o * rb + natural_byte_of(fmt, p, nfull)] : (uint8_t)0;
+    }
+}
 
 } // namespace
 
@@ -312,8 +460,8 @@ int gemv_smax_bucket(int S) {
 }
 
 GemvShape gemv_shape(int fmt, int smax) {
-#define WQ_SHAPE_CASE(F, SM, LW, KM, R) \
-    if (fmt == F && smax == SM) return GemvShape{LW, KM, R};
+#define WQ_SHAPE_CASE(F, SM, LW, KM, D) \
+    if (fmt == F && smax == SM) return GemvShape{LW, KM, D};
     WQ_SHAPES(WQ_SHAPE_CASE)
 #undef WQ_SHAPE_CASE
     return GemvShape{0, 0, 0};
@@ -328,50 +476,83 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu) {
     if (sh.lw == 0) return p;
     p.lw = sh.lw;
     p.kmax = sh.kmax;
-    p.r = sh.r;
+    p.d = sh.d;
     const long stride = round_up(row_bytes(fmt, I), kRowAlign);
     const long per_wave = 64L * sh.lw * sh.kmax;
-    long team = (stride + per_wave - 1) / per_wave;
+    const long team = (stride + per_wave - 1) / per_wave;
     if (team > kMaxTeam) return p;  // row too long for the register GEMV
     p.team = (int)team;
     p.k = (int)((stride + 64L * p.lw * p.team - 1) / (64L * p.lw * p.team));
     p.teams_per_block = (p.team == 1) ? 4 : 1;
     p.block = 64 * p.team * p.teams_per_block;
-    // teams: enough waves to keep HBM busy, each with at least R rows
+    // teams: enough waves to keep HBM busy, rows per team a multiple of the ring depth
     const long want_teams = std::max(1L, (long)cus * waves_per_cu / p.team);
-    const long max_teams = (O + p.r - 1) / p.r;
-    long teams = std::min(want_teams, max_teams);
-    long rpt = (O + teams - 1) / teams;
-    rpt = (rpt + p.r - 1) / p.r * p.r;
-    teams = (O + rpt - 1) / rpt;
+    long teams = std::min(want_teams, ((long)O + p.d - 1) / p.d);
+    long rpt = ((long)O + teams - 1) / teams;
+    rpt = (rpt + p.d - 1) / p.d * p.d;
+    teams = ((long)O + rpt - 1) / rpt;
     p.rows_per_team = (int)rpt;
     p.grid = (int)((teams + p.teams_per_block - 1) / p.teams_per_block);
     p.ok = true;
     return p;
 }
 
-hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st) {
-#define WQ_LAUNCH_CASE(F, SM, LW, KM, R)                                                   \
-    if (p.fmt == F && p.smax == SM) {                                                      \
-        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KM, R>), dim3(p.grid), dim3(p.block), 0, \
-                           st, a);                                                         \
-        return hipGetLastError();                                                          \
+template <int F, int SM, int LW, int KM, int D>
+hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStream_t st) {
+    // exact slot count: 1..KM; activations through LDS when they fit
+    const size_t xbytes = (size_t)a.S * a.I * sizeof(float);
+    const bool xl = xv && xbytes <= (size_t)kXLdsMaxBytes;
+#define WQ_K(KS)                                                                                          \
+    if constexpr (KS <= KM) {                                                                             \
+        if (p.k == KS) {                                                                                  \
+            if (xl)                                                                                       \
+                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, true, true>), dim3(p.grid), dim3(p.block), \
+                                   xbytes, st, a);                                                        \
+            else if (xv)                                                                                  \
+                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, true, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
+            else                                                                                          \
+                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, false, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
+            return hipGetLastError();                                                                     \
+        }                                                                                                 \
     }
+    WQ_K(1) WQ_K(2) WQ_K(3) WQ_K(4)
+#undef WQ_K
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st) {
+    const bool xv = (a.I % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
+#define WQ_LAUNCH_CASE(F, SM, LW, KM, D) \
+    if (p.fmt == F && p.smax == SM) return launch_gemv_k<F, SM, LW, KM, D>(p, a, xv, st);
     WQ_SHAPES(WQ_LAUNCH_CASE)
 #undef WQ_LAUNCH_CASE
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, hipStream_t st) {
-#define WQ_GLAUNCH_CASE(F, SM, LW, KM, R)                                                      \
-    if (fmt == F && p.smax == SM) {                                                            \
-        hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, R>), dim3(p.grid), dim3(p.block), 0, \
-                           st, a);                                                             \
-        return hipGetLastError();                                                              \
+hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, hipStream_t st) {
+#define WQ_GLAUNCH_CASE(F, SM, LW, KM, D)                                                                 \
+    if (fmt == F && p.smax == SM) {                                                                       \
+        if (xv)                                                                                           \
+            hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, true>), dim3(p.grid), dim3(p.block), 0,  \
+                               st, a);                                                                    \
+        else                                                                                              \
+            hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, false>), dim3(p.grid), dim3(p.block), 0, \
+                               st, a);                                                                    \
+        return hipGetLastError();                                                                         \
     }
     WQ_SHAPES(WQ_GLAUNCH_CASE)
 #undef WQ_GLAUNCH_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_relayout(int fmt, const uint8_t *src, uint8_t *dst, int O, long rb, long stride, int nfull,
+                           hipStream_t st) {
+    const long n = (long)O * stride;
+    const int block = 256;
+    const long want = (n + block - 1) / block;
+    const int grid = (int)std::min<long>(std::max<long>(want, 1), 65536);
+    hipLaunchKernelGGL(relayout_kernel, dim3(grid), dim3(block), 0, st, src, dst, fmt, O, rb, stride, nfull);
+    return hipGetLastError();
 }
 
 } // namespace wq

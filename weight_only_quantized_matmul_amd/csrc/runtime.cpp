@@ -138,6 +138,7 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
         a.x = x;
         a.y = y;
         a.stride = t->stride;
+        a.nfull = t->nfull;
         a.O = t->O;
         a.I = t->I;
         a.S = S;
@@ -154,6 +155,7 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
     a.x = x;
     a.y = y;
     a.stride = t->stride;
+    a.nfull = t->nfull;
     a.O = t->O;
     a.I = t->I;
     a.S = S;
@@ -279,13 +281,32 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
         dev_free(d, dw, wbytes);
         return rc;
     }
+    const int nfull = wq::full_blocks(fmt, rb);
     hipError_t e = hipSuccess;
-    if (stride != rb) {
-        e = hipMemsetAsync(dw, 0, wbytes, d.stream);
-        if (e == hipSuccess)
-            e = hipMemcpy2DAsync(dw, stride, w, rb, rb, O, hipMemcpyHostToDevice, d.stream);
+    if (nfull == 0) {
+        // natural order: copy rows into the padded stride
+        if (stride != rb) {
+            e = hipMemsetAsync(dw, 0, wbytes, d.stream);
+            if (e == hipSuccess)
+                e = hipMemcpy2DAsync(dw, stride, w, rb, rb, O, hipMemcpyHostToDevice, d.stream);
+        } else {
+            e = hipMemcpyAsync(dw, w, wbytes, hipMemcpyHostToDevice, d.stream);
+        }
     } else {
-        e = hipMemcpyAsync(dw, w, wbytes, hipMemcpyHostToDevice, d.stream);
+        // stage the natural rows, then permute 1 KiB blocks into the device layout
+        void *tmp = nullptr;
+        if (hipMalloc(&tmp, (size_t)O * rb) != hipSuccess) {
+            (void)hipGetLastError();
+            dev_free(d, dw, wbytes);
+            dev_free(d, ds, sbytes);
+            return WQ_E_OOM;
+        }
+        e = hipMemcpyAsync(tmp, w, (size_t)O * rb, hipMemcpyHostToDevice, d.stream);
+        if (e == hipSuccess)
+            e = wq::launch_relayout(fmt, (const uint8_t *)tmp, (uint8_t *)dw, O, rb, stride, nfull, d.stream);
+        hipError_t e2 = hipStreamSynchronize(d.stream);
+        if (e == hipSuccess) e = e2;
+        (void)hipFree(tmp);
     }
     std::vector<float> ones;
     if (e == hipSuccess) {
@@ -316,6 +337,7 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
     nt->I = I;
     nt->rb = rb;
     nt->stride = stride;
+    nt->nfull = nfull;
     nt->d_w = (uint8_t *)dw;
     nt->d_scales = (float *)ds;
     nt->bytes = wbytes + sbytes;
@@ -400,8 +422,10 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
         gd.w = ts[i]->d_w;
         gd.scales = ts[i]->d_scales;
         gd.stride = ts[i]->stride;
+        gd.nfull = ts[i]->nfull;
         gd.O = ts[i]->O;
         gd.I = ts[i]->I;
+        gd.pad = 0;
         g->h_desc.push_back(gd);
     }
     auto fail = [&](int rc) {
@@ -426,7 +450,7 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
         bk.plan.smax = smax;
         bk.plan.lw = sh.lw;
         bk.plan.kmax = sh.kmax;
-        bk.plan.r = sh.r;
+        bk.plan.d = sh.d;
         const long per_wave = 64L * sh.lw * sh.kmax;
         long total = 0;
         bool fits = true;
@@ -444,7 +468,7 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
             for (int p = c0; p < c1; ++p) {
                 const auto &gd = g->h_desc[p];
                 long rows = (bytes_per_item + gd.stride - 1) / gd.stride;
-                rows = std::max<long>(sh.r, (rows + sh.r - 1) / sh.r * sh.r);
+                rows = std::max<long>(sh.d, (rows + sh.d - 1) / sh.d * sh.d);
                 const int k = (int)((gd.stride + 64L * sh.lw - 1) / (64L * sh.lw));
                 for (long r0 = 0; r0 < gd.O; r0 += rows) {
                     wq::WorkItem it;
@@ -522,10 +546,13 @@ int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, 
             any = any || S[p] > 0;
         }
         if (!any || a.n_items == 0) continue;
+        bool xv = true;
+        for (int p = c0; p < c1; ++p)
+            if (S[p] > 0 && ((g->h_desc[p].I % 4) != 0 || ((uintptr_t)x_dev[p] & 15) != 0)) xv = false;
         wq::GroupedPlan gp = bk.plan;
         gp.grid = (a.n_items + 3) / 4;
         gp.block = 256;
-        int rc = hip_status(wq::launch_grouped(g->fmt, gp, a, st));
+        int rc = hip_status(wq::launch_grouped(g->fmt, gp, a, xv, st));
         if (rc != WQ_OK) return rc;
     }
     return WQ_OK;
@@ -582,8 +609,8 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
     }
     wq::GemvPlan gp;
     if (choose_path(fmt, O, I, S, cus, &gp) == 1) {
-        snprintf(buf, buflen, "gemv fmt=%d smax=%d lw=%d kmax=%d k=%d team=%d r=%d rows_per_team=%d grid=%d block=%d",
-                 fmt, gp.smax, gp.lw, gp.kmax, gp.k, gp.team, gp.r, gp.rows_per_team, gp.grid, gp.block);
+        snprintf(buf, buflen, "gemv fmt=%d smax=%d lw=%d kmax=%d k=%d team=%d d=%d rows_per_team=%d grid=%d block=%d",
+                 fmt, gp.smax, gp.lw, gp.kmax, gp.k, gp.team, gp.d, gp.rows_per_team, gp.grid, gp.block);
     } else {
         const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S);
         snprintf(buf, buflen, "tiled fmt=%d bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d grid=%d block=%d", fmt, tp.bm,

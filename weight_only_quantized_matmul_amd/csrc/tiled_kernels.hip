@@ -11,9 +11,12 @@
 // contraction, so it runs on the matrix cores:
 //  * a 256-thread block owns a 64 (s) x 64 (o) output tile; its four waves
 //    each own a 32 x 32 quarter made of 2 x 2 v_mfma_f32_16x16x4_f32 tiles;
-//  * per 32-column K step the block stages the x tile (fp32) and the weight
-//    tile, dequantized once to exact fp32 values, in LDS (double-buffered,
-//    rows padded by 4 floats so a 16-lane row group reads 16 distinct banks);
+//  * the contraction runs over the weight fields in device order (see the
+//    layout in wq_internal.h); per 32-position K step the block stages the
+//    matching activations (gathered as runs of four consecutive elements)
+//    and the weight tile, dequantized once to exact fp32 values, in LDS
+//    (double-buffered, rows padded by 4 floats so a 16-lane row group reads
+//    16 distinct banks);
 //  * within a 16-column group lane group g = lane/16 reads columns
 //    4g..4g+3 with one 128-bit LDS read and feeds them to four MFMAs, so each
 //    MFMA sees one column per lane group; A and B use the same column order;
@@ -66,21 +69,26 @@ __device__ __forceinline__ void load_w8(const uint8_t *__restrict__ row, long st
     }
 }
 
-__device__ __forceinline__ void load_x8(const float *__restrict__ x, int S, int I, bool vec_ok, int s, long k0,
-                                        float (&v)[8]) {
+// Activations for the 8 field positions [P0, P0 + 8) of a row (two runs of
+// four consecutive elements, located through the device layout).
+template <int FMT>
+__device__ __forceinline__ void load_x8(const float *__restrict__ x, int S, int I, int nfull, bool vec_ok, int s,
+                                        long P0, float (&v)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.0f;
     if (s >= S) return;
-    const float *xs = x + (long)s * I + k0;
-    if (vec_ok && k0 + 8 <= I) {
-        const float4 a = *reinterpret_cast<const float4 *>(xs);
-        const float4 b = *reinterpret_cast<const float4 *>(xs + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
+    const float *xs = x + (long)s * I;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (k0 + e < I) v[e] = xs[e];
+    for (int h = 0; h < 2; ++h) {
+        const long e0 = elem_of_pos4(FMT, P0 + 4 * h, nfull);
+        if (vec_ok && e0 + 4 <= I) {
+            const float4 a = *reinterpret_cast<const float4 *>(xs + e0);
+            v[4 * h] = a.x; v[4 * h + 1] = a.y; v[4 * h + 2] = a.z; v[4 * h + 3] = a.w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e0 + u < I) v[4 * h + u] = xs[e0 + u];
+        }
     }
 }
 
@@ -113,7 +121,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledArgs a) {
 
     float xv[8], wq[8];
     auto fetch = [&](long k0) {
-        load_x8(a.x, a.S, a.I, vec_ok, s0 + lrow, k0 + lcol, xv);
+        load_x8<FMT>(a.x, a.S, a.I, a.nfull, vec_ok, s0 + lrow, k0 + lcol, xv);
         if (wrow_ok) {
             load_w8<FMT>(wrow_p, a.stride, k0 + lcol, wq);
         } else {
@@ -134,7 +142,10 @@ __global__ __launch_bounds__(256) void tiled_kernel(TiledArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nk = (a.I + BK - 1) / BK;
+    // every field position of a row, in device order (the layout permutes
+    // elements inside 1 KiB blocks; positions past I may hold real elements)
+    const long npos = (FMT == WQ_F32) ? (long)a.I : (long)(a.stride) * (FMT == WQ_I8 ? 1 : FMT == WQ_I4 ? 2 : 4);
+    const int nk = (int)((npos + BK - 1) / BK);
     fetch(0);
     stash(0);
     __syncthreads();

@@ -1,5 +1,6 @@
-// Internal declarations of libwqmm: tensor/group objects, launch plans and
-// kernel argument blocks shared by the runtime and the kernel files.
+// Internal declarations of libwqmm: tensor/group objects, the device weight
+// layout, launch plans and kernel argument blocks shared by the runtime and
+// the kernel files.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +17,8 @@ constexpr uint32_t kTensorMagic = 0x57515431u; // "WQT1"
 constexpr uint32_t kGroupMagic = 0x57514731u;  // "WQG1"
 constexpr int kRowAlign = 16;                  // device row stride alignment (bytes)
 constexpr int kGroupMaxPerLaunch = 64;         // problems passed by value per grouped launch
+constexpr int kMaxTeam = 8;                    // waves that may share one row
+constexpr int kXLdsMaxBytes = 64 * 1024;       // activations staged through LDS up to this size
 
 // Bits per stored element, by format code.
 inline int fmt_bits(int fmt) {
@@ -36,6 +39,64 @@ inline long row_bytes(int fmt, long I) {
 
 inline long round_up(long v, long a) { return (v + a - 1) / a * a; }
 
+// ---------------------------------------------------------------------------
+// Device weight layout (library-private).
+//
+// Rows are stored one after another with a stride rounded up to 16 bytes
+// (padding zeroed). f32 rows keep their natural order. For int8/int4/int2
+// every complete 1024-byte block of a row is a permutation of its bytes:
+// with epb elements per byte and G = 16 * epb elements per 16-byte granule,
+// field n (0 <= n < G, low bits of a byte first, bytes in order) of granule
+// lambda (0 <= lambda < 64) holds element
+//
+//     block_base + 256 * (n / 4) + 4 * lambda + (n % 4).
+//
+// A wave whose 64 lanes read the 64 granules of a block therefore needs, for
+// each n / 4, the 256 consecutive activations [block_base + 256 m, +256):
+// every activation load is one fully coalesced 1 KiB access, and the
+// activations live in registers in the same order as the weight fields.
+// Four consecutive fields n = 4m .. 4m+3 are four consecutive elements, and
+// each stored byte holds whole consecutive elements, so the permutation moves
+// bytes only. The last partial block of a row (if any) keeps natural order.
+constexpr int kBlockBytes = 1024;
+
+// Elements per byte, or 0 for f32 (4 bytes per element).
+__host__ __device__ inline int elems_per_byte(int fmt) {
+    return fmt == WQ_I8 ? 1 : fmt == WQ_I4 ? 2 : fmt == WQ_I2 ? 4 : 0;
+}
+
+// Full permuted blocks per row.
+__host__ __device__ inline int full_blocks(int fmt, long rb) {
+    return elems_per_byte(fmt) == 0 ? 0 : (int)(rb / kBlockBytes);
+}
+
+// Source byte (natural order, within the row) of device byte p.
+__host__ __device__ inline long natural_byte_of(int fmt, long p, int nfull) {
+    const int epb = elems_per_byte(fmt);
+    if (epb == 0 || p >= (long)nfull * kBlockBytes) return p;
+    const long base = p / kBlockBytes * kBlockBytes;
+    const int r = (int)(p - base);
+    const int lambda = r >> 4, q = r & 15;
+    const int n0 = q * epb;                                 // first field of the byte
+    const long e0 = 256L * (n0 >> 2) + 4 * lambda + (n0 & 3); // element within the block
+    return base + e0 / epb;
+}
+
+// Element index of the first of four consecutive fields starting at field
+// position P (P a multiple of 4) of a row; positions count fields in device
+// order (P = byte * epb + field; for f32, P = byte / 4).
+__host__ __device__ inline long elem_of_pos4(int fmt, long P, int nfull) {
+    const int epb = elems_per_byte(fmt);
+    if (epb == 0) return P;
+    const long per_block = (long)kBlockBytes * epb;
+    if (P >= (long)nfull * per_block) return P;
+    const long b = P / per_block;
+    const int r = (int)(P - b * per_block);
+    const int G = 16 * epb;
+    const int lambda = r / G, n = r % G;
+    return b * per_block + 256L * (n >> 2) + 4 * lambda;
+}
+
 } // namespace wq
 
 struct wq_tensor {
@@ -43,6 +104,7 @@ struct wq_tensor {
     int device, fmt, O, I;
     long rb;      // packed host row bytes
     long stride;  // device row stride (rb rounded up to kRowAlign; padding zeroed)
+    int nfull;    // permuted 1 KiB blocks per row
     uint8_t *d_w;
     float *d_scales;
     size_t bytes; // device bytes held (weights + scales)
@@ -59,7 +121,7 @@ struct GemvPlan {
     int lw = 0;     // bytes per lane per weight load (16, 8 or 4)
     int kmax = 0;   // load slots per lane per row compiled in
     int k = 0;      // load slots used for this row length
-    int r = 0;      // rows in flight per team iteration
+    int d = 0;      // rows in flight per wave (ring depth)
     int team = 0;   // waves cooperating on one row
     int teams_per_block = 0;
     int block = 0;
@@ -74,6 +136,7 @@ struct GemvArgs {
     const float *x;
     float *y;
     long stride;
+    int nfull;
     int O, I, S;
     int k;             // load slots per lane per row
     int team;          // waves per team
@@ -82,9 +145,9 @@ struct GemvArgs {
 };
 
 // Kernel shape for (fmt, S bucket): bytes per lane load, compiled slot count
-// and rows in flight. Row coverage per wave = 64 * lw * kmax bytes.
+// and ring depth. Row coverage per wave = 64 * lw * kmax bytes.
 struct GemvShape {
-    int lw, kmax, r;
+    int lw, kmax, d;
 };
 GemvShape gemv_shape(int fmt, int smax);
 int gemv_smax_bucket(int S); // 1,2,4,8 or 0 if S > 8
@@ -99,7 +162,9 @@ struct GroupDesc {
     const uint8_t *w;
     const float *scales;
     long stride;
+    int nfull;
     int O, I;
+    int pad;
 };
 
 struct WorkItem {
@@ -121,11 +186,12 @@ struct GroupedArgs {
 
 struct GroupedPlan {
     bool ok = false;
-    int smax = 0, lw = 0, kmax = 0, r = 0;
+    int smax = 0, lw = 0, kmax = 0, d = 0;
     int n_items = 0, grid = 0, block = 256;
 };
 
-hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, hipStream_t st);
+// xv: every activation pointer 16-byte aligned and every I a multiple of 4.
+hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // LDS-tiled dequant + fp32 MFMA path (any S).
@@ -136,6 +202,7 @@ struct TiledArgs {
     const float *x;
     float *y;
     long stride;
+    int nfull;
     int O, I, S;
     int tiles_s, tiles_o;
 };
@@ -147,6 +214,11 @@ struct TiledPlan {
 
 TiledPlan plan_tiled(int fmt, int O, int I, int S);
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Upload: natural packed rows (O x rb, device) -> device layout (O x stride).
+hipError_t launch_relayout(int fmt, const uint8_t *src, uint8_t *dst, int O, long rb, long stride, int nfull,
+                           hipStream_t st);
 
 } // namespace wq
 
