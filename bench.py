@@ -49,7 +49,37 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (10 times) for counter calibration")
     return ap.parse_args()
+
+
+COUNTER_SUMMARY = {"dense_gemv": "profiles/gemv_int4_dense_gemv_hbm_counters.txt"}
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv_kernels.hip", "tiled_kernels.hip", "wq_internal.h"):
+        with open(os.path.join(ROOT, "weight_only_quantized_matmul_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(workload):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary (copy-calibrated),
+    or None when there is none or the kernels changed since it was taken."""
+    path = COUNTER_SUMMARY.get(workload)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    sha, traffic = None, None
+    with open(os.path.join(ROOT, path)) as f:
+        for line in f:
+            if line.startswith("kernel source sha256[:16]:"):
+                sha = line.rsplit(":", 1)[1].strip()
+            elif line.startswith("traffic_bytes_per_launch:"):
+                traffic = int(line.split(":", 1)[1])
+    return traffic if sha == kernel_source_hash() else None
 
 
 def problems_for(name):
@@ -74,8 +104,18 @@ def main():
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": 4 * n,
+                          "copy_calibration_bytes_written_per_launch": 4 * n, "launches": 10}), flush=True)
+        return
 
     import weight_only_quantized_matmul_amd as wq
 
@@ -150,7 +190,7 @@ def main():
         unit = "GB/s"
         roof = {"bound": "hbm", "achieved": alg_bytes / per_launch / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = traffic_from_counters(args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
