@@ -75,8 +75,10 @@ typedef struct wq_group wq_group;   /* opaque set of tensors run in one launch *
  * WQ_MAX_DEVICES (WQ_E_INVAL); no GPU or a non-gfx950 GPU gives WQ_E_NODEV.
  * Calling it again is allowed: already-open devices are kept, and the
  * environment knobs are read again (WQ_FORCE_PATH=gemv|tiled|auto,
- * WQ_GEMV_MAX_S, WQ_MEM_LIMIT_BYTES, WQ_FAULT=upload|launch, WQ_VERBOSE=1
- * prints one line per device on stderr).
+ * WQ_GEMV_MAX_S, WQ_MEM_LIMIT_BYTES, WQ_FAULT=upload|launch,
+ * WQ_TILED_MODE=bf16x3|fp32, WQ_TILED_SHAPE=BMxBNxBK (a compiled tile shape:
+ * 128x96x64, 128x96x32, 64x64x64, 64x64x32), WQ_VERBOSE=1 prints one line
+ * per device on stderr).
  */
 int wq_init(const int *devices, int ndev);
 
@@ -122,12 +124,20 @@ int wq_matmul(wq_tensor **t, int device, int fmt, int O, int I, const void *w,
 int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
 
 /*
- * Stream-ordered matmul on device buffers: one kernel launch on hip_stream
- * (a hipStream_t; NULL = the device's null stream), no copies, no host
- * synchronisation, no allocation. x_dev: device [S, I] floats, y_dev: device
- * [S, O] floats, both on the tensor's device and 4-byte aligned. The call
- * returns once the launch is queued; y_dev is valid after the stream reaches
- * it. May be captured into a HIP graph.
+ * Stream-ordered matmul on device buffers, queued on hip_stream (a
+ * hipStream_t; NULL = the device's null stream): no copies and no host
+ * synchronisation. x_dev: device [S, I] floats, y_dev: device [S, O] floats,
+ * both on the tensor's device and 4-byte aligned. The call returns once the
+ * work is queued; y_dev is valid after the stream reaches it.
+ * S <= the GEMV limit: one kernel launch, no workspace. Larger S with a
+ * quantized format (tiled path, bf16x3 mode): two launches that use the
+ * device's workspace (3 * round_up(S, 128) * round_up(fields per row, 64)
+ * bf16 values; wq_describe_plan prints the size). The workspace grows on
+ * demand: growth waits for the device to go idle and allocates; a call being
+ * captured into a HIP graph never grows it and returns WQ_E_UNSUPPORTED
+ * instead, so run the largest S once before capturing. The workspace is
+ * shared by every call on the device: tiled calls on different streams must
+ * not overlap in time.
  */
 int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, void *hip_stream);
 
@@ -147,7 +157,8 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
  * x_dev, S, y_dev: host arrays of G entries (device pointers inside);
  * S[g] == 0 skips tensor g. One kernel launch on hip_stream when every
  * S[g] <= the GEMV limit and every row fits the register GEMV; otherwise one
- * launch per tensor, still stream-ordered and allocation-free.
+ * wq_matmul_dev per tensor, still stream-ordered (the tiled ones share the
+ * device workspace, in stream order).
  */
 int wq_grouped_matmul_dev(wq_group *group, const float *const *x_dev, const int *S,
                           float *const *y_dev, void *hip_stream);

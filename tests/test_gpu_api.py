@@ -22,9 +22,9 @@ I8, I4, I2 = 1, 2, 3
 
 @pytest.fixture(autouse=True)
 def device():
-    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None, WQ_TILED_SHAPE=None)
     yield
-    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None, WQ_TILED_SHAPE=None)
 
 
 def test_mem_info():
@@ -161,3 +161,83 @@ def test_graph_capture_replays_match_eager():
             torch.cuda.synchronize()
     finally:
         wq.wq_tensor_free(t)
+
+
+def _capture(t, x, y):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        wq.wq_matmul_dev(t, x, y)
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_capture_tiled_after_warmup():
+    """The tiled path (split pre-pass + MFMA kernel, device workspace) replays like eager."""
+    p = synth.ragged(I8, 1000, 1500, 100, seed=21)
+    t = gu.upload(p)
+    try:
+        x = torch.from_numpy(p.x).cuda()
+        y_eager = torch.empty((p.S, p.O), device="cuda")
+        gu.banner("capture tiled warmup: %s" % wq.wq_describe_plan(I8, p.O, p.I, p.S))
+        wq.wq_matmul_dev(t, x, y_eager)  # sizes the workspace outside the capture
+        torch.cuda.synchronize()
+        y_ref, A = oracle.matmul(I8, p.w, p.scales, p.x)
+        gu.assert_within_bound(y_eager.cpu().numpy(), y_ref, A, "eager tiled")
+        y_graph = torch.zeros_like(y_eager)
+        g = _capture(t, x, y_graph)
+        for i in range(4):
+            y_graph.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_graph, y_eager), "replay %d differs" % i
+            wq.wq_matmul_dev(t, x, y_eager)  # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        wq.wq_tensor_free(t)
+
+
+def test_capture_refuses_workspace_growth():
+    """A captured call never allocates: a larger S than any eager call so far is refused."""
+    p = synth.ragged(I4, 300, 20000, 4000, seed=22)  # more workspace than every other test uses
+    t = gu.upload(p)
+    try:
+        plan = wq.wq_describe_plan(I4, p.O, p.I, p.S)
+        assert "mode=bf16x3" in plan, plan
+        x = torch.from_numpy(p.x).cuda()
+        y = torch.zeros((p.S, p.O), device="cuda")
+        gu.banner("capture refused: " + plan)
+        with pytest.raises(wq.WqError) as ei:
+            _capture(t, x, y)
+        assert ei.value.code == wq.WQ_E_UNSUPPORTED
+        torch.cuda.synchronize()
+        # the same call eagerly grows the workspace and is correct
+        wq.wq_matmul_dev(t, x, y)
+        torch.cuda.synchronize()
+        rows = np.arange(0, p.O, 37)
+        yh = y.cpu().numpy()
+        y_ref, A = oracle.matmul_rows(I4, p.w, p.scales, p.x, rows)
+        gu.assert_within_bound(yh[:, rows], y_ref, A, "after growth")
+    finally:
+        wq.wq_tensor_free(t)
+
+
+@pytest.mark.parametrize("shape", ["128x96x64", "128x96x32", "64x64x64", "64x64x32"])
+@pytest.mark.parametrize("fmt,O,I,S", [(I8, 200, 700, 150), (I4, 97, 2100, 20), (I2, 130, 4500, 70)])
+def test_forced_tile_shapes(shape, fmt, O, I, S):
+    p = synth.ragged(fmt, O, I, S, seed=23 + O + S)
+    t = gu.upload(p)
+    try:
+        gu.reinit_with_env(WQ_FORCE_PATH="tiled", WQ_TILED_SHAPE=shape)
+        plan = wq.wq_describe_plan(fmt, O, I, S)
+        bm, bn, bk = shape.split("x")
+        assert "bm=%s bn=%s bk=%s" % (bm, bn, bk) in plan, plan
+        gu.banner("forced shape " + plan)
+        y = gu.run_dev(t, p.x)
+    finally:
+        wq.wq_tensor_free(t)
+        gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_SHAPE=None)
+    y_ref, A = oracle.matmul(fmt, p.w, p.scales, p.x)
+    gu.assert_within_bound(y, y_ref, A, "shape " + shape)

@@ -27,9 +27,11 @@ F32, I8, I4, I2 = 0, 1, 2, 3
 
 @pytest.fixture(scope="module", autouse=True)
 def device():
-    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_GEMV_MAX_S=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_GEMV_MAX_S=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None,
+                       WQ_TILED_MODE=None)
     yield
-    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_GEMV_MAX_S=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None)
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_GEMV_MAX_S=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None,
+                       WQ_TILED_MODE=None)
 
 
 def check_problem(p, what, x_offset=0, rows=None):
@@ -210,6 +212,63 @@ def test_forced_paths_agree(path, fmt, O, I, S):
 def test_gemv_tiled_crossover(S):
     p = synth.ragged(I4, 257, 1111, S, seed=31337 + S)
     check_problem(p, "crossover")
+
+
+TILED_MODE_CASES = [
+    (I4, 6200, 333, 130),   # 128 x 96 tiles: 2 x 65 of them, ragged in s, o and i
+    (I8, 6144, 1024, 256),  # 128 x 96 tiles, exact multiples
+    (I2, 300, 4100, 40),    # 64 x 64 tiles, one permuted block plus a natural tail
+    (I4, 70, 2048, 9),      # 64 x 64 tiles, two permuted blocks
+    (F32, 500, 999, 33),    # f32 weights always take fp32 operands
+]
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
+@pytest.mark.parametrize("fmt,O,I,S", TILED_MODE_CASES)
+def test_tiled_modes(mode, fmt, O, I, S):
+    p = synth.ragged(fmt, O, I, S, seed=7100 + O + I + S)
+    # activations over a wide exponent range exercise all three bf16 parts
+    g = synth.rng(7200 + S)
+    p.x = (p.x * np.exp2(g.integers(-24, 25, size=p.x.shape))).astype(np.float32)
+    try:
+        gu.reinit_with_env(WQ_FORCE_PATH="tiled", WQ_TILED_MODE=mode)
+        plan = wq.wq_describe_plan(fmt, O, I, S)
+        assert plan.startswith("tiled")
+        assert ("mode=bf16x3" in plan) == (mode == "bf16x3" and fmt != F32), plan
+        check_problem(p, "tiled-" + mode)
+    finally:
+        gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_MODE=None)
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
+@pytest.mark.parametrize("fmt", [I8, I4, I2])
+def test_tiled_one_hot_full_mantissa(mode, fmt):
+    """One nonzero activation per row, with a full 24-bit significand.
+
+    Each output is scale * q * v rounded twice, so it is within two units in the
+    last place of the exact value. Dropping any of the three bf16 parts of v
+    would cost at least 2^-16 relative.
+    """
+    O, I, S = 40, 3000, 24
+    p = synth.ragged(fmt, O, I, S, seed=7300 + fmt)
+    g = synth.rng(7400 + fmt)
+    cols = g.integers(0, I, size=S)
+    mant = g.integers(1 << 23, 1 << 24, size=S).astype(np.float64)
+    v = (mant * np.exp2(g.integers(-40, 20, size=S)) * g.choice([-1.0, 1.0], size=S)).astype(np.float32)
+    x = np.zeros((S, I), np.float32)
+    x[np.arange(S), cols] = v
+    t = gu.upload(p)
+    try:
+        gu.reinit_with_env(WQ_FORCE_PATH="tiled", WQ_TILED_MODE=mode)
+        gu.banner("one-hot full mantissa fmt=%d mode=%s" % (fmt, mode))
+        y = gu.run_dev(t, x)
+    finally:
+        wq.wq_tensor_free(t)
+        gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_MODE=None)
+    y_ref, _ = oracle.matmul(fmt, p.w, p.scales, x)
+    ref = y_ref.astype(np.float64)
+    err = np.abs(y.astype(np.float64) - ref)
+    assert np.all(err <= 2.0 ** -22 * np.abs(ref)), float(np.max(err / np.maximum(np.abs(ref), 1e-300)))
 
 
 # ---------------------------------------------------------------------------------------

@@ -208,7 +208,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             const uint32_t b4 = (uint32_t)xb[k] * 4u, st4 = (uint32_t)xs_step[k] * 4u;
 #pragma unroll
             for (int s = 0; s < SMAX; ++s)
-                if (s < S) {
+                if (SMAX == 1 || s < S) {
                     const char *xs = reinterpret_cast<const char *>(x + (long)s * I);  // wave-uniform base
 #pragma unroll
                     for (int g = 0; g < EPC / 4; ++g) {
@@ -219,6 +219,9 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                         xr[k][4 * g + 2][s] = t.z;
                         xr[k][4 * g + 3][s] = t.w;
                     }
+                } else {  // activation rows past S contribute zero
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) xr[k][e][s] = 0.0f;
                 }
         }
     } else {
@@ -226,13 +229,16 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
         for (int k = 0; k < KMAX; ++k)
 #pragma unroll
             for (int s = 0; s < SMAX; ++s)
-                if (s < S) {
+                if (SMAX == 1 || s < S) {
                     const float *xs = x + (long)s * I;
 #pragma unroll
                     for (int e = 0; e < EPC; ++e) {
                         const int ei = WQ_XE(k, e / 4) + (e & 3);
                         xr[k][e][s] = xs[(live[k] && ei < I) ? ei : 0];
                     }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) xr[k][e][s] = 0.0f;
                 }
     }
     // Weight ring prologue, issued after the activation loads: the
@@ -257,7 +263,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             for (int s = 0; s < SMAX; ++s)
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) {
-                    const float v = s < S ? xr[k][e][s] : 0.0f;
+                    const float v = xr[k][e][s];
                     xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
                     if constexpr (OFF != 0) sx[s] += v;
                 }
@@ -269,7 +275,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) {
                     const int ei = WQ_XE(k, e / 4) + (e & 3);
-                    const bool in = s < S && live[k] && ei < I;
+                    const bool in = live[k] && ei < I;
                     const float v = in ? xr[k][e][s] : 0.0f;
                     xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
                     if constexpr (OFF != 0) sx[s] += v;

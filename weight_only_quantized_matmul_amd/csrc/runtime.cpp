@@ -30,8 +30,10 @@ struct DeviceCtx {
     size_t x_cap = 0;  // bytes
     float *d_y = nullptr;
     size_t y_cap = 0;  // bytes
-    size_t lib_bytes = 0;  // device bytes held by tensors and groups
-    std::mutex mu;
+    uint16_t *d_ws = nullptr;  // tiled bf16x3 activation planes, shared by every call on the device
+    size_t ws_cap = 0;         // bytes
+    size_t lib_bytes = 0;      // device bytes held by tensors, groups and the workspace
+    std::recursive_mutex mu;
 };
 
 struct Config {
@@ -41,6 +43,8 @@ struct Config {
     int fault = 0;            // 0 none, 1 upload, 2 launch
     int verbose = 0;
     int waves_per_cu = 8;
+    int tiled_mode = wq::kTiledBF16X3;  // quantized weights: exact bf16 split of x
+    int tiled_shape = 0;                // 0: by size; else bm * 1000000 + bn * 1000 + bk
 };
 
 DeviceCtx g_dev[WQ_MAX_DEVICES];
@@ -65,6 +69,14 @@ void read_env(Config &c) {
         else if (!strcmp(v, "launch")) c.fault = 2;
     }
     if (const char *v = getenv("WQ_VERBOSE")) c.verbose = atoi(v);
+    if (const char *v = getenv("WQ_TILED_MODE")) {
+        if (!strcmp(v, "fp32")) c.tiled_mode = wq::kTiledF32;
+        else if (!strcmp(v, "bf16x3")) c.tiled_mode = wq::kTiledBF16X3;
+    }
+    if (const char *v = getenv("WQ_TILED_SHAPE")) {
+        int bm = 0, bn = 0, bk = 0;
+        if (sscanf(v, "%dx%dx%d", &bm, &bn, &bk) == 3) c.tiled_shape = bm * 1000000 + bn * 1000 + bk;
+    }
     if (const char *v = getenv("WQ_WAVES_PER_CU")) {
         int n = atoi(v);
         if (n >= 1 && n <= 32) c.waves_per_cu = n;
@@ -128,8 +140,38 @@ int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp) {
     return 2;
 }
 
+// The device workspace, grown to at least `bytes`. Growth waits for all
+// queued work (the old buffer may still be read) and is refused while `st`
+// is being captured into a graph.
+int ensure_workspace(DeviceCtx &d, size_t bytes, hipStream_t st, uint16_t **out) {
+    std::lock_guard<std::recursive_mutex> lk(d.mu);
+    if (bytes > d.ws_cap) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+            (void)hipGetLastError();
+            return WQ_E_HIP;
+        }
+        if (cs != hipStreamCaptureStatusNone) return WQ_E_UNSUPPORTED;
+        if (d.d_ws) {
+            if (hipDeviceSynchronize() != hipSuccess) {
+                (void)hipGetLastError();
+                return WQ_E_HIP;
+            }
+            dev_free(d, d.d_ws, d.ws_cap);
+            d.d_ws = nullptr;
+            d.ws_cap = 0;
+        }
+        const size_t cap = (size_t)wq::round_up((long)bytes, 2L << 20);
+        int rc = dev_alloc(d, (void **)&d.d_ws, cap);
+        if (rc != WQ_OK) return rc;
+        d.ws_cap = cap;
+    }
+    *out = d.d_ws;
+    return WQ_OK;
+}
+
 int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t st) {
-    const DeviceCtx &d = g_dev[t->device];
+    DeviceCtx &d = g_dev[t->device];
     wq::GemvPlan gp;
     if (choose_path(t->fmt, t->O, t->I, S, d.cus, &gp) == 1) {
         wq::GemvArgs a;
@@ -148,7 +190,7 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
         a.rows_per_team = gp.rows_per_team;
         return hip_status(wq::launch_gemv(gp, a, st));
     }
-    const wq::TiledPlan tp = wq::plan_tiled(t->fmt, t->O, t->I, S);
+    const wq::TiledPlan tp = wq::plan_tiled(t->fmt, t->O, t->I, S, g_cfg.tiled_mode, g_cfg.tiled_shape);
     wq::TiledArgs a;
     a.w = t->d_w;
     a.scales = t->d_scales;
@@ -161,6 +203,15 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
     a.S = S;
     a.tiles_s = tp.tiles_s;
     a.tiles_o = tp.tiles_o;
+    a.xp = nullptr;
+    a.plane = (long)tp.sp * tp.kp;
+    a.kp = tp.kp;
+    if (tp.ws_bytes > 0) {
+        uint16_t *ws = nullptr;
+        int rc = ensure_workspace(d, tp.ws_bytes, st, &ws);
+        if (rc != WQ_OK) return rc;
+        a.xp = ws;
+    }
     return hip_status(wq::launch_tiled(t->fmt, tp, a, st));
 }
 
@@ -266,7 +317,7 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
     if (!device_open(device)) return WQ_E_NOTINIT;
     if (g_cfg.fault == 1) return WQ_E_FAULT;
     DeviceCtx &d = g_dev[device];
-    std::lock_guard<std::mutex> lk(d.mu);
+    std::lock_guard<std::recursive_mutex> lk(d.mu);
     DeviceGuard guard(device);
 
     const long rb = wq::row_bytes(fmt, I);
@@ -352,7 +403,7 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y) {
     if (!device_open(t->device)) return WQ_E_NOTINIT;
     if (g_cfg.fault == 2) return WQ_E_FAULT;
     DeviceCtx &d = g_dev[t->device];
-    std::lock_guard<std::mutex> lk(d.mu);
+    std::lock_guard<std::recursive_mutex> lk(d.mu);
     DeviceGuard guard(t->device);
     const size_t xb = (size_t)S * t->I * sizeof(float);
     const size_t yb = (size_t)S * t->O * sizeof(float);
@@ -406,7 +457,7 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
         if (ts[i]->device != dev || ts[i]->fmt != fmt) return WQ_E_INVAL;
     if (!device_open(dev)) return WQ_E_NOTINIT;
     DeviceCtx &d = g_dev[dev];
-    std::lock_guard<std::mutex> lk(d.mu);
+    std::lock_guard<std::recursive_mutex> lk(d.mu);
     DeviceGuard guard(dev);
 
     wq_group *g = new (std::nothrow) wq_group;
@@ -562,7 +613,7 @@ int wq_grouped_free(wq_group *g) {
     if (g == nullptr) return WQ_OK;
     if (g->magic != wq::kGroupMagic) return WQ_E_INVAL;
     DeviceCtx &d = g_dev[g->device];
-    std::lock_guard<std::mutex> lk(d.mu);
+    std::lock_guard<std::recursive_mutex> lk(d.mu);
     DeviceGuard guard(g->device);
     for (auto &b : g->buckets)
         if (b.d_items) dev_free(d, b.d_items, (size_t)b.plan.n_items * sizeof(wq::WorkItem));
@@ -576,7 +627,7 @@ int wq_tensor_free(wq_tensor *t) {
     if (t == nullptr) return WQ_OK;
     if (!tensor_ok(t)) return WQ_E_INVAL;
     DeviceCtx &d = g_dev[t->device];
-    std::lock_guard<std::mutex> lk(d.mu);
+    std::lock_guard<std::recursive_mutex> lk(d.mu);
     DeviceGuard guard(t->device);
     dev_free(d, t->d_w, (size_t)t->O * t->stride);
     dev_free(d, t->d_scales, (size_t)t->O * sizeof(float));
@@ -612,9 +663,11 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
         snprintf(buf, buflen, "gemv fmt=%d smax=%d lw=%d kmax=%d k=%d team=%d d=%d rows_per_team=%d grid=%d block=%d",
                  fmt, gp.smax, gp.lw, gp.kmax, gp.k, gp.team, gp.d, gp.rows_per_team, gp.grid, gp.block);
     } else {
-        const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S);
-        snprintf(buf, buflen, "tiled fmt=%d bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d grid=%d block=%d", fmt, tp.bm,
-                 tp.bn, tp.bk, tp.tiles_s, tp.tiles_o, tp.grid, tp.block);
+        const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S, g_cfg.tiled_mode, g_cfg.tiled_shape);
+        snprintf(buf, buflen,
+                 "tiled fmt=%d mode=%s bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d grid=%d block=%d workspace=%zu", fmt,
+                 tp.mode == wq::kTiledBF16X3 ? "bf16x3" : "fp32", tp.bm, tp.bn, tp.bk, tp.tiles_s, tp.tiles_o,
+                 tp.grid, tp.block, tp.ws_bytes);
     }
     return WQ_OK;
 }

@@ -1,4 +1,4 @@
-// LDS-tiled dequant + fp32 MFMA path for S beyond the register GEMV.
+// LDS-tiled dequant + MFMA path for S beyond the register GEMV.
 //
 // y[s,o] = scale[o] * sum_i dequant(W[o,i]) * x[s,i]
 //   (colibri "第 8 章 · 02 CUDA/Metal/Vulkan 三后端", section 四, qmatmul.comp
@@ -9,21 +9,34 @@
 //
 // With many activation rows the work is a dense [S x I] * [I x O]
 // contraction, so it runs on the matrix cores:
-//  * a 256-thread block owns a 64 (s) x 64 (o) output tile; its four waves
-//    each own a 32 x 32 quarter made of 2 x 2 v_mfma_f32_16x16x4_f32 tiles;
+//  * a 256-thread block owns a BM (s) x BN (o) output tile, BM = 32*WM and
+//    BN = 32*WN; its four waves (2 x 2) each own WM x WN 16x16 fragments;
 //  * the contraction runs over the weight fields in device order (see the
-//    layout in wq_internal.h); per 32-position K step the block stages the
-//    matching activations (gathered as runs of four consecutive elements)
-//    and the weight tile, dequantized once to exact fp32 values, in LDS
-//    (double-buffered, rows padded by 4 floats so a 16-lane row group reads
-//    16 distinct banks);
-//  * within a 16-column group lane group g = lane/16 reads columns
-//    4g..4g+3 with one 128-bit LDS read and feeds them to four MFMAs, so each
-//    MFMA sees one column per lane group; A and B use the same column order;
+//    layout in wq_internal.h); per BK-position step the block stages the
+//    matching activations and the weight tile, dequantized once, in LDS
+//    (double-buffered, rows padded by 16 bytes) while the next step's global
+//    data is already in registers;
 //  * the per-row scale is applied in the epilogue, after the sum;
 //  * tiles are handed out XCD by XCD (blocks are dispatched round-robin over
 //    the 8 XCDs), consecutive tiles of one XCD sharing a weight tile so it is
 //    fetched into that XCD's L2 once.
+//
+// Two operand modes:
+//  * fp32 (any weight format, the only one for f32 weights): activations are
+//    gathered from x in runs of four consecutive elements, operands stay
+//    fp32, v_mfma_f32_16x16x4_f32 (lane group g = lane/16 reads positions
+//    4g..4g+3 of a 16-position group with one 128-bit LDS read and feeds them
+//    to four MFMAs; A and B use the same order, so the sum is unchanged);
+//  * bf16x3 (quantized weights): a pre-pass splits every activation exactly
+//    into three bf16 parts by truncation (x = b1 + b2 + b3: b1 keeps the top
+//    8 significant bits, b2 the next 8 of the remainder, b3 the last 8) and
+//    writes them as three planes in the weights' field order; the integer
+//    codes are exact in bf16, and v_mfma_f32_16x16x32_bf16 accumulates
+//    b1*q + b2*q + b3*q in fp32 with every product exact: fp32-level
+//    results at the bf16 matrix rate, and the split is done once per
+//    activation instead of once per output tile.
+#include <climits>
+
 #include "wq_internal.h"
 
 namespace wq {
@@ -32,14 +45,50 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 64, BN = 64, BK = 32, LDK = BK + 4;
+// XCD-aware tile order: block b runs on XCD b % 8; XCD x owns a contiguous
+// range of tiles, walked with s fastest so consecutive tiles share W.
+__device__ __forceinline__ void tile_origin(const TiledArgs &a, int bm, int bn, int &s0, int &o0) {
+    const int nt = a.tiles_s * a.tiles_o;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, local = b >> 3;
+    const int base = nt >> 3, extra = nt & 7;
+    const int t = xcd * base + min(xcd, extra) + local;
+    s0 = (t % a.tiles_s) * bm;
+    o0 = (t / a.tiles_s) * bn;
+}
 
-// Weight bytes covering 8 consecutive elements, dequantized to exact floats.
+// Epilogue: lane holds rows 4*(lane/16) + r, column lane % 16 of each 16x16
+// fragment; the row scale multiplies the finished sum.
+template <int WM, int WN>
+__device__ __forceinline__ void store_tile(const TiledArgs &a, const f32x4 (&acc)[WM][WN], int s0, int o0, int wm,
+                                           int wn, int g, int li) {
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+        const int o = o0 + wn * 16 * WN + n * 16 + li;
+        if (o >= a.O) continue;
+        const float sc = a.scales[o];
+#pragma unroll
+        for (int m = 0; m < WM; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = s0 + wm * 16 * WM + m * 16 + 4 * g + r;
+                if (s < a.S) a.y[(long)s * a.O + o] = sc * acc[m][n][r];
+            }
+    }
+}
+
+// ===========================================================================
+// fp32 mode
+
+constexpr int BK32 = 32;
+
+// Weight fields at the 8 positions [P0, P0 + 8) of a row, dequantized.
 template <int FMT>
-__device__ __forceinline__ void load_w8(const uint8_t *__restrict__ row, long stride, long k0, float (&q)[8]) {
+__device__ __forceinline__ void load_w8(const uint8_t *__restrict__ row, long stride, long P0, float (&q)[8]) {
     if constexpr (FMT == WQ_F32) {
-        const long bo = k0 * 4;
+        const long bo = P0 * 4;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             u32x4 v = {0u, 0u, 0u, 0u};
@@ -51,17 +100,17 @@ __device__ __forceinline__ void load_w8(const uint8_t *__restrict__ row, long st
         }
     } else if constexpr (FMT == WQ_I8) {
         u32x2 v = {0u, 0u};
-        if (k0 < stride) v = *reinterpret_cast<const u32x2 *>(row + k0);
+        if (P0 < stride) v = *reinterpret_cast<const u32x2 *>(row + P0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = (float)(int)(int8_t)((e < 4 ? v.x : v.y) >> (8 * (e & 3)));
     } else if constexpr (FMT == WQ_I4) {
-        const long bo = k0 / 2;
+        const long bo = P0 / 2;
         uint32_t v = 0x88888888u;
         if (bo < stride) v = *reinterpret_cast<const uint32_t *>(row + bo);
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = (float)((int)((v >> (4 * e)) & 0xFu) - 8);
     } else {
-        const long bo = k0 / 4;
+        const long bo = P0 / 4;
         uint32_t v = 0xAAAAu;
         if (bo < stride) v = *reinterpret_cast<const uint16_t *>(row + bo);
 #pragma unroll
@@ -92,125 +141,464 @@ __device__ __forceinline__ void load_x8(const float *__restrict__ x, int S, int 
     }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256) void tiled_kernel(TiledArgs a) {
-    __shared__ __attribute__((aligned(16))) float As[2][BM][LDK];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BN][LDK];
+template <int WM, int WN>
+struct F32Cfg {
+    static constexpr int BM = 32 * WM, BN = 32 * WN;
+    static constexpr int LDA = BK32 + 4;                  // floats per LDS row
+    static constexpr int A_FLOATS = BM * LDA, B_FLOATS = BN * LDA;
+    static constexpr int STAGE_FLOATS = A_FLOATS + B_FLOATS;
+    static constexpr int LDS_BYTES = 2 * STAGE_FLOATS * 4;
+    static constexpr int XU = BM * BK32 / 8 / 256;          // activation units (8 positions) per thread
+    static constexpr int WU = (BN * BK32 / 8 + 255) / 256;  // weight units per thread (last may be partial)
+};
 
-    // XCD-aware tile order: block b runs on XCD b % 8; XCD x owns a contiguous
-    // range of tiles, walked with s fastest so consecutive tiles share W.
-    const int nt = a.tiles_s * a.tiles_o;
-    const int b = blockIdx.x;
-    const int xcd = b & 7, local = b >> 3;
-    const int base = nt >> 3, extra = nt & 7;
-    const int t = xcd * base + min(xcd, extra) + local;
-    const int ts = t % a.tiles_s, to = t / a.tiles_s;
-    const int s0 = ts * BM, o0 = to * BN;
+template <int FMT, int WM, int WN>
+__global__ __launch_bounds__(256) void tiled_f32_kernel(TiledArgs a) {
+    using C = F32Cfg<WM, WN>;
+    constexpr int BM = C::BM, BN = C::BN, LDA = C::LDA;
+    extern __shared__ __attribute__((aligned(16))) float ldsf[];
 
+    int s0, o0;
+    tile_origin(a, BM, BN, s0, o0);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int lrow = tid >> 2;        // staging row 0..63
-    const int lcol = (tid & 3) * 8;   // staging column 0,8,16,24
+    const int g = lane >> 4, li = lane & 15;
 
     const bool vec_ok = ((a.I & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
-    const int wrow = o0 + lrow;
-    const uint8_t *wrow_p = a.w + (long)min(wrow, a.O - 1) * a.stride;
-    const bool wrow_ok = wrow < a.O;
-
-    float xv[8], wq[8];
-    auto fetch = [&](long k0) {
-        load_x8<FMT>(a.x, a.S, a.I, a.nfull, vec_ok, s0 + lrow, k0 + lcol, xv);
-        if (wrow_ok) {
-            load_w8<FMT>(wrow_p, a.stride, k0 + lcol, wq);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wq[e] = 0.0f;
-        }
-    };
-    auto stash = [&](int buf) {
-        *reinterpret_cast<float4 *>(&As[buf][lrow][lcol]) = make_float4(xv[0], xv[1], xv[2], xv[3]);
-        *reinterpret_cast<float4 *>(&As[buf][lrow][lcol + 4]) = make_float4(xv[4], xv[5], xv[6], xv[7]);
-        *reinterpret_cast<float4 *>(&Bs[buf][lrow][lcol]) = make_float4(wq[0], wq[1], wq[2], wq[3]);
-        *reinterpret_cast<float4 *>(&Bs[buf][lrow][lcol + 4]) = make_float4(wq[4], wq[5], wq[6], wq[7]);
-    };
-
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
     // every field position of a row, in device order (the layout permutes
     // elements inside 1 KiB blocks; positions past I may hold real elements)
     const long npos = (FMT == WQ_F32) ? (long)a.I : (long)(a.stride) * (FMT == WQ_I8 ? 1 : FMT == WQ_I4 ? 2 : 4);
-    const int nk = (int)((npos + BK - 1) / BK);
+    const int nk = (int)((npos + BK32 - 1) / BK32);
+
+    // staging: unit u covers tile row u / 4, positions 8 * (u % 4) .. +8 of the K step
+    float xv[C::XU][8], wv[C::WU][8];
+    auto fetch = [&](long k0) {
+#pragma unroll
+        for (int j = 0; j < C::XU; ++j) {
+            const int u = tid + 256 * j;
+            load_x8<FMT>(a.x, a.S, a.I, a.nfull, vec_ok, s0 + u / 4, k0 + 8 * (u % 4), xv[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < C::WU; ++j) {
+            const int u = tid + 256 * j;
+            const int row = o0 + u / 4;
+            if (u < BN * 4 && row < a.O) {
+                load_w8<FMT>(a.w + (long)row * a.stride, a.stride, k0 + 8 * (u % 4), wv[j]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wv[j][e] = 0.0f;
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+        float *As = ldsf + buf * C::STAGE_FLOATS;
+        float *Bs = As + C::A_FLOATS;
+#pragma unroll
+        for (int j = 0; j < C::XU; ++j) {
+            const int u = tid + 256 * j;
+            float *d = As + (u / 4) * LDA + 8 * (u % 4);
+            *reinterpret_cast<float4 *>(d) = make_float4(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+            *reinterpret_cast<float4 *>(d + 4) = make_float4(xv[j][4], xv[j][5], xv[j][6], xv[j][7]);
+        }
+#pragma unroll
+        for (int j = 0; j < C::WU; ++j) {
+            const int u = tid + 256 * j;
+            if (u < BN * 4) {
+                float *d = Bs + (u / 4) * LDA + 8 * (u % 4);
+                *reinterpret_cast<float4 *>(d) = make_float4(wv[j][0], wv[j][1], wv[j][2], wv[j][3]);
+                *reinterpret_cast<float4 *>(d + 4) = make_float4(wv[j][4], wv[j][5], wv[j][6], wv[j][7]);
+            }
+        }
+    };
+
+    f32x4 acc[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
     fetch(0);
     stash(0);
     __syncthreads();
-    const int g = lane >> 4, li = lane & 15;
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) fetch((long)(kt + 1) * BK);
+        if (kt + 1 < nk) fetch((long)(kt + 1) * BK32);
+        const float *As = ldsf + buf * C::STAGE_FLOATS;
+        const float *Bs = As + C::A_FLOATS;
 #pragma unroll
-        for (int kg = 0; kg < BK / 16; ++kg) {
-            f32x4 av[2], bv[2];
+        for (int kg = 0; kg < BK32 / 16; ++kg) {
+            f32x4 av[WM], bv[WN];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                av[mi] = *reinterpret_cast<const f32x4 *>(&As[buf][wm * 32 + mi * 16 + li][kg * 16 + 4 * g]);
+            for (int m = 0; m < WM; ++m)
+                av[m] = *reinterpret_cast<const f32x4 *>(As + (wm * 16 * WM + m * 16 + li) * LDA + kg * 16 + 4 * g);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                bv[ni] = *reinterpret_cast<const f32x4 *>(&Bs[buf][wn * 32 + ni * 16 + li][kg * 16 + 4 * g]);
+            for (int n = 0; n < WN; ++n)
+                bv[n] = *reinterpret_cast<const f32x4 *>(Bs + (wn * 16 * WN + n * 16 + li) * LDA + kg * 16 + 4 * g);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
+                for (int m = 0; m < WM; ++m)
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi][j], bv[ni][j], acc[mi][ni], 0, 0, 0);
+                    for (int n = 0; n < WN; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][j], bv[n][j], acc[m][n], 0, 0, 0);
         }
         if (kt + 1 < nk) stash(buf ^ 1);
         __syncthreads();
     }
+    store_tile<WM, WN>(a, acc, s0, o0, wm, wn, g, li);
+}
 
-    // epilogue: lane holds rows 4*(lane/16) + r, column lane % 16 of each 16x16 tile
+// ===========================================================================
+// bf16x3 mode
+
+// Upper halves of two fp32 bit patterns whose values are exact in bf16.
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t lo_bits, uint32_t hi_bits) {
+    return (lo_bits >> 16) | (hi_bits & 0xFFFF0000u);
+}
+
+// Activations -> three bf16 planes in device field order. Thread q of row s
+// covers positions 4q .. 4q+3 (four consecutive elements of x); rows past S,
+// elements past I and positions past the row's fields are written as zeros,
+// so every element of the planes is rewritten on every call.
+template <int FMT>
+__global__ __launch_bounds__(256) void split_x_kernel(const float *__restrict__ x, int S, int I, int nfull,
+                                                      int vec_ok, int sp, int kp, long plane,
+                                                      uint16_t *__restrict__ xp) {
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    if (4 * q >= kp) return;
+    const long P = 4L * q;
+    const long e0 = elem_of_pos4(FMT, P, nfull);
+    for (int s = blockIdx.y; s < sp; s += gridDim.y) {
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (s < S) {
+            const float *xs = x + (long)s * I;
+            if (vec_ok && e0 + 4 <= I) {
+                const float4 t = *reinterpret_cast<const float4 *>(xs + e0);
+                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+            } else {
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-        const int o = o0 + wn * 32 + ni * 16 + li;
-        if (o >= a.O) continue;
-        const float sc = a.scales[o];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = s0 + wm * 32 + mi * 16 + 4 * g + r;
-                if (s < a.S) a.y[(long)s * a.O + o] = sc * acc[mi][ni][r];
+                for (int u = 0; u < 4; ++u)
+                    if (e0 + u < I) v[u] = xs[e0 + u];
             }
+        }
+        uint32_t b1[4], b2[4], b3[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t h = __float_as_uint(v[u]) & 0xFFFF0000u;
+            const float r = v[u] - __uint_as_float(h);  // exact
+            const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
+            b1[u] = h;
+            b2[u] = m;
+            b3[u] = __float_as_uint(r - __uint_as_float(m));  // exact, at most 8 significant bits
+        }
+        const long off = (long)s * kp + P;
+        *reinterpret_cast<u32x2 *>(xp + off) = u32x2{bf16_pair(b1[0], b1[1]), bf16_pair(b1[2], b1[3])};
+        *reinterpret_cast<u32x2 *>(xp + plane + off) = u32x2{bf16_pair(b2[0], b2[1]), bf16_pair(b2[2], b2[3])};
+        *reinterpret_cast<u32x2 *>(xp + 2 * plane + off) = u32x2{bf16_pair(b3[0], b3[1]), bf16_pair(b3[2], b3[3])};
     }
+}
+
+// Raw weight bits for the 8 field positions [P0, P0 + 8) of a row (P0 a
+// multiple of 8). Positions past the row's stride are read from the row's
+// last bytes instead: the activation planes are zero there, so whatever
+// codes are read contribute exact zeros.
+template <int FMT>
+struct RawW;
+template <>
+struct RawW<WQ_I8> {
+    u32x2 v;
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ row, long stride, long P0) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(row + min(P0, stride - 8)));
+    }
+    __device__ __forceinline__ int code(int e) const {
+        return (int)(int8_t)((e < 4 ? v.x : v.y) >> (8 * (e & 3)));
+    }
+};
+template <>
+struct RawW<WQ_I4> {
+    uint32_t v;
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ row, long stride, long P0) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(row + min(P0 / 2, stride - 4)));
+    }
+    // nibble c stands for c - 8: flipping its top bit gives the same value as
+    // a signed 4-bit field
+    __device__ __forceinline__ int code(int e) const {
+        return (int)((v ^ 0x88888888u) << (28 - 4 * e)) >> 28;
+    }
+};
+template <>
+struct RawW<WQ_I2> {
+    uint32_t v;
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ row, long stride, long P0) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(row + min(P0 / 4, stride - 2)));
+    }
+    // code c stands for c - 2: the same value as a signed 2-bit field with
+    // its top bit flipped
+    __device__ __forceinline__ int code(int e) const {
+        return (int)((v ^ 0xAAAAu) << (30 - 2 * e)) >> 30;
+    }
+};
+
+// Eight decoded codes as bf16 (exact: |code| <= 128 has at most 8 significant bits).
+template <int FMT>
+__device__ __forceinline__ u32x4 codes_bf16x8(const RawW<FMT> &w) {
+    uint32_t f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = __float_as_uint((float)w.code(e));
+    return u32x4{bf16_pair(f[0], f[1]), bf16_pair(f[2], f[3]), bf16_pair(f[4], f[5]), bf16_pair(f[6], f[7])};
+}
+
+template <int WM, int WN, int BK>
+struct X3Cfg {
+    static constexpr int BM = 32 * WM, BN = 32 * WN;
+    static constexpr int LDA = BK + 8;          // bf16 per LDS row (16 bytes of padding)
+    static constexpr int CH = BK / 8;           // 16-byte chunks per row per step
+    static constexpr int APL = BM * LDA;        // one activation plane of a stage (bf16)
+    static constexpr int AU = 3 * BM * CH / 256;       // activation chunks per thread
+    static constexpr int WU = (BN * CH + 255) / 256;   // weight chunks per thread
+    static constexpr int BROWS = WU * 256 / CH;        // B rows written (>= BN; the rest is never read)
+    static constexpr int STAGE = 3 * APL + BROWS * LDA;
+    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static_assert((3 * BM * CH) % 256 == 0, "activation chunks must spread evenly");
+    static_assert((WU * 256) % CH == 0 && BROWS >= BN, "weight chunks must fill whole rows");
+};
+
+template <int FMT, int WM, int WN, int BK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void tiled_x3_kernel(TiledArgs a) {
+    using C = X3Cfg<WM, WN, BK>;
+    constexpr int BM = C::BM, BN = C::BN, LDA = C::LDA, CH = C::CH, APL = C::APL;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds16[];
+
+    int s0, o0;
+    tile_origin(a, BM, BN, s0, o0);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int g = lane >> 4, li = lane & 15;
+    const int nk = a.kp / BK;
+
+    // Weight rows past O are read from row O - 1: they only feed output
+    // columns that are never stored.
+    u32x4 ag[C::AU];
+    RawW<FMT> wg[C::WU];
+    auto fetch = [&](int kt) {
+        const long k0 = (long)kt * BK;
+#pragma unroll
+        for (int j = 0; j < C::AU; ++j) {
+            const int u = tid + 256 * j;
+            const int pl = u / (BM * CH), r = (u / CH) % BM, c = u % CH;
+            ag[j] = *reinterpret_cast<const u32x4 *>(a.xp + pl * a.plane + (long)(s0 + r) * a.kp + k0 + 8 * c);
+        }
+#pragma unroll
+        for (int j = 0; j < C::WU; ++j) {
+            const int u = tid + 256 * j;
+            const int row = min(o0 + u / CH, a.O - 1);
+            wg[j].load(a.w + (long)row * a.stride, a.stride, k0 + 8 * (u % CH));
+        }
+    };
+    auto stash = [&](int buf) {
+        uint16_t *st = lds16 + buf * C::STAGE;
+#pragma unroll
+        for (int j = 0; j < C::AU; ++j) {
+            const int u = tid + 256 * j;
+            const int pl = u / (BM * CH), r = (u / CH) % BM, c = u % CH;
+            *reinterpret_cast<u32x4 *>(st + pl * APL + r * LDA + 8 * c) = ag[j];
+        }
+#pragma unroll
+        for (int j = 0; j < C::WU; ++j) {
+            const int u = tid + 256 * j;
+            *reinterpret_cast<u32x4 *>(st + 3 * APL + (u / CH) * LDA + 8 * (u % CH)) = codes_bf16x8<FMT>(wg[j]);
+        }
+    };
+
+    f32x4 acc[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // fragments of one 32-position sub-step: A (three planes) and B
+    constexpr int KK = BK / 32;
+    auto frags = [&](int buf, int kk, bf16x8 (&av)[WM][3], bf16x8 (&bv)[WN]) {
+        const uint16_t *As = lds16 + buf * C::STAGE;
+        const uint16_t *Bs = As + 3 * APL;
+#pragma unroll
+        for (int n = 0; n < WN; ++n)
+            bv[n] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * 16 * WN + n * 16 + li) * LDA + 32 * kk + 8 * g);
+#pragma unroll
+        for (int m = 0; m < WM; ++m)
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+                av[m][pl] = *reinterpret_cast<const bf16x8 *>(As + pl * APL + (wm * 16 * WM + m * 16 + li) * LDA +
+                                                              32 * kk + 8 * g);
+    };
+    auto mma = [&](const bf16x8 (&av)[WM][3], const bf16x8 (&bv)[WN]) {
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+            for (int m = 0; m < WM; ++m)
+#pragma unroll
+                for (int n = 0; n < WN; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][pl], bv[n], acc[m][n], 0, 0, 0);
+    };
+
+    // Software pipeline, per K step kt (LDS buffer kt & 1 holds step kt):
+    //   region A: all fragment reads of the step; MFMAs of the first
+    //             sub-steps interleaved with the later reads
+    //   region B: MFMAs of the last sub-step interleaved with storing step
+    //             kt + 1 (fetched one step earlier) into the other buffer,
+    //             which the previous barrier released, and with the global
+    //             loads of step kt + 2
+    // In-order issue overlaps VALU, LDS and memory instructions with the
+    // matrix core only when they sit between MFMAs in program order; the
+    // sched_group_barrier sequences below ask the scheduler for that.
+    constexpr int NMMA = 3 * WM * WN;       // MFMAs per sub-step
+    constexpr int NREAD = 3 * WM + WN;      // fragment reads per sub-step
+    constexpr int NWRITE = C::AU + C::WU;   // LDS stores per step
+    constexpr int NLOAD = C::AU + C::WU;    // global loads per step
+    // the last two steps fetch (clamped) data that is stored but never read
+    fetch(0);
+    stash(0);
+    fetch(min(1, nk - 1));
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        bf16x8 av[KK][WM][3], bv[KK][WN];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) frags(buf, kk, av[kk], bv[kk]);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) mma(av[kk], bv[kk]);
+        __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+#pragma unroll
+        for (int i = 0; i < (KK - 1) * NMMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < (KK - 1) * NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        stash(buf ^ 1);
+        fetch(min(kt + 2, nk - 1));
+        mma(av[KK - 1], bv[KK - 1]);
+#pragma unroll
+        for (int i = 0; i < NMMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            if (i < NWRITE) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            if (i < NLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    }
+    store_tile<WM, WN>(a, acc, s0, o0, wm, wn, g, li);
+}
+
+// ===========================================================================
+// launch
+
+template <typename K>
+hipError_t raise_lds_limit(K kernel, int bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               bytes);
+}
+
+template <int FMT, int WM, int WN>
+hipError_t launch_f32(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
+    using C = F32Cfg<WM, WN>;
+    static_assert(C::LDS_BYTES <= 160 * 1024, "tile does not fit in LDS");
+    static const hipError_t lim = raise_lds_limit(&tiled_f32_kernel<FMT, WM, WN>, C::LDS_BYTES);
+    if (lim != hipSuccess) return lim;
+    hipLaunchKernelGGL((tiled_f32_kernel<FMT, WM, WN>), dim3(p.grid), dim3(256), C::LDS_BYTES, st, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int WM, int WN, int BK>
+hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
+    using C = X3Cfg<WM, WN, BK>;
+    static_assert(C::LDS_BYTES <= 160 * 1024, "tile does not fit in LDS");
+    static const hipError_t lim = raise_lds_limit(&tiled_x3_kernel<FMT, WM, WN, BK>, C::LDS_BYTES);
+    if (lim != hipSuccess) return lim;
+    const int vec_ok = ((a.I & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
+    const dim3 sgrid((unsigned)((p.kp / 4 + 255) / 256), (unsigned)std::min(p.sp, 65535));
+    hipLaunchKernelGGL((split_x_kernel<FMT>), sgrid, dim3(256), 0, st, a.x, a.S, a.I, a.nfull, vec_ok, p.sp, p.kp,
+                       (long)p.sp * p.kp, const_cast<uint16_t *>(a.xp));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WM, WN, BK>), dim3(p.grid), dim3(256), C::LDS_BYTES, st, a);
+    return hipGetLastError();
+}
+
+// Compiled tile shapes {bm, bn, bk}; the first entry is the large-problem
+// default, the last the small-problem default.
+struct Shape {
+    int bm, bn, bk;
+};
+constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 32}, {64, 64, 64}, {64, 64, 32}};
+constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
+
+template <int FMT>
+hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
+    if constexpr (FMT != WQ_F32) {
+        if (p.mode == kTiledBF16X3) {
+            if (p.bm == 128) {
+                if (p.bk == 64) return launch_x3<FMT, 4, 3, 64>(p, a, st);
+                return launch_x3<FMT, 4, 3, 32>(p, a, st);
+            }
+            if (p.bk == 64) return launch_x3<FMT, 2, 2, 64>(p, a, st);
+            return launch_x3<FMT, 2, 2, 32>(p, a, st);
+        }
+    }
+    if (p.bm == 128) return launch_f32<FMT, 4, 3>(p, a, st);
+    return launch_f32<FMT, 2, 2>(p, a, st);
 }
 
 } // namespace
 
-TiledPlan plan_tiled(int fmt, int O, int I, int S) {
-    (void)fmt;
-    (void)I;
+TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape) {
     TiledPlan p;
+    // the bf16 split needs exact integer codes (quantized formats); f32 weights stay fp32
+    p.mode = (fmt != WQ_F32 && mode == kTiledBF16X3) ? kTiledBF16X3 : kTiledF32;
+    // plane sizes are kept in int: rows near the int limit take the fp32 mode
+    if ((long)S > INT_MAX - kTiledSAlign || (long)I > INT_MAX / 2 - 4 * kTiledKAlign) p.mode = kTiledF32;
+    // big tiles (128 x 96, 4 x 3 fragments per wave) when there are enough of them
+    const long big = (long)((S + 127) / 128) * ((O + 95) / 96);
+    const bool use_big = S >= 128 && big >= 128;
+    Shape sh;
+    if (p.mode == kTiledBF16X3) {
+        sh = use_big ? kX3Shapes[0] : kX3Shapes[3];
+        for (const Shape &c : kX3Shapes)
+            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk) sh = c;
+    } else {
+        sh = use_big ? kF32Shapes[0] : kF32Shapes[1];
+        for (const Shape &c : kF32Shapes)
+            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk) sh = c;
+    }
+    p.bm = sh.bm;
+    p.bn = sh.bn;
+    p.bk = sh.bk;
     p.tiles_s = (S + p.bm - 1) / p.bm;
     p.tiles_o = (O + p.bn - 1) / p.bn;
     p.grid = p.tiles_s * p.tiles_o;
+    if (p.mode == kTiledBF16X3) {
+        const long stride = round_up(row_bytes(fmt, I), kRowAlign);
+        const long npos = stride * elems_per_byte(fmt);
+        p.kp = (int)round_up(npos, kTiledKAlign);
+        p.sp = (int)round_up(S, kTiledSAlign);
+        p.ws_bytes = (size_t)3 * p.sp * p.kp * sizeof(uint16_t);
+    }
     return p;
 }
 
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     switch (fmt) {
-    case WQ_F32: hipLaunchKernelGGL(tiled_kernel<WQ_F32>, dim3(p.grid), dim3(p.block), 0, st, a); break;
-    case WQ_I8: hipLaunchKernelGGL(tiled_kernel<WQ_I8>, dim3(p.grid), dim3(p.block), 0, st, a); break;
-    case WQ_I4: hipLaunchKernelGGL(tiled_kernel<WQ_I4>, dim3(p.grid), dim3(p.block), 0, st, a); break;
-    case WQ_I2: hipLaunchKernelGGL(tiled_kernel<WQ_I2>, dim3(p.grid), dim3(p.block), 0, st, a); break;
+    case WQ_F32: return launch_fmt<WQ_F32>(p, a, st);
+    case WQ_I8: return launch_fmt<WQ_I8>(p, a, st);
+    case WQ_I4: return launch_fmt<WQ_I4>(p, a, st);
+    case WQ_I2: return launch_fmt<WQ_I2>(p, a, st);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 } // namespace wq

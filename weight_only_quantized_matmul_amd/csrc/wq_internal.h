@@ -194,7 +194,7 @@ struct GroupedPlan {
 hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// LDS-tiled dequant + fp32 MFMA path (any S).
+// LDS-tiled dequant + MFMA path (any S).
 
 struct TiledArgs {
     const uint8_t *w;
@@ -205,14 +205,27 @@ struct TiledArgs {
     int nfull;
     int O, I, S;
     int tiles_s, tiles_o;
+    // bf16x3 mode: workspace holding the three activation planes
+    const uint16_t *xp;
+    long plane;  // bf16 elements per plane (sp * kp)
+    int kp;      // bf16 elements per plane row
 };
+
+constexpr int kTiledF32 = 0;     // fp32 operands, v_mfma_f32_16x16x4_f32
+constexpr int kTiledBF16X3 = 1;  // exact 3-way bf16 split of x, v_mfma_f32_16x16x32_bf16
+constexpr int kTiledKAlign = 64; // plane rows padded (with zeros) to this many positions
+constexpr int kTiledSAlign = 128; // planes padded (with zero rows) to this many rows
 
 struct TiledPlan {
+    int mode = kTiledF32;
     int bm = 64, bn = 64, bk = 32;
     int tiles_s = 0, tiles_o = 0, grid = 0, block = 256;
+    int sp = 0, kp = 0;   // bf16x3: plane rows and row length
+    size_t ws_bytes = 0;  // device workspace the call needs (bf16x3: 3 planes)
 };
 
-TiledPlan plan_tiled(int fmt, int O, int I, int S);
+// shape: 0 picks by size; bm * 1000000 + bn * 1000 + bk forces a compiled tile shape
+TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape);
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
