@@ -77,8 +77,8 @@ typedef struct wq_group wq_group;   /* opaque set of tensors run in one launch *
  * environment knobs are read again (WQ_FORCE_PATH=gemv|tiled|auto,
  * WQ_GEMV_MAX_S, WQ_MEM_LIMIT_BYTES, WQ_FAULT=upload|launch,
  * WQ_TILED_MODE=bf16x3|fp32, WQ_TILED_SHAPE=BMxBNxBK (a compiled tile shape:
- * 128x96x64, 128x96x32, 64x64x64, 64x64x32), WQ_VERBOSE=1 prints one line
- * per device on stderr).
+ * 128x96x64 or 64x64x64 in bf16x3 mode, 128x96x32 or 64x64x32 in fp32 mode),
+ * WQ_VERBOSE=1 prints one line per device on stderr).
  */
 int wq_init(const int *devices, int ndev);
 

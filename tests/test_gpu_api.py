@@ -22,9 +22,11 @@ I8, I4, I2 = 1, 2, 3
 
 @pytest.fixture(autouse=True)
 def device():
-    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None, WQ_TILED_SHAPE=None)
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None, WQ_TILED_SHAPE=None,
+                       WQ_TILED_MODE=None)
     yield
-    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None, WQ_TILED_SHAPE=None)
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_FAULT=None, WQ_MEM_LIMIT_BYTES=None, WQ_TILED_SHAPE=None,
+                       WQ_TILED_MODE=None)
 
 
 def test_mem_info():
@@ -224,20 +226,21 @@ def test_capture_refuses_workspace_growth():
         wq.wq_tensor_free(t)
 
 
-@pytest.mark.parametrize("shape", ["128x96x64", "128x96x32", "64x64x64", "64x64x32"])
+@pytest.mark.parametrize("mode,shape", [("bf16x3", "128x96x64"), ("bf16x3", "64x64x64"),
+                                        ("fp32", "128x96x32"), ("fp32", "64x64x32")])
 @pytest.mark.parametrize("fmt,O,I,S", [(I8, 200, 700, 150), (I4, 97, 2100, 20), (I2, 130, 4500, 70)])
-def test_forced_tile_shapes(shape, fmt, O, I, S):
+def test_forced_tile_shapes(mode, shape, fmt, O, I, S):
     p = synth.ragged(fmt, O, I, S, seed=23 + O + S)
     t = gu.upload(p)
     try:
-        gu.reinit_with_env(WQ_FORCE_PATH="tiled", WQ_TILED_SHAPE=shape)
+        gu.reinit_with_env(WQ_FORCE_PATH="tiled", WQ_TILED_MODE=mode, WQ_TILED_SHAPE=shape)
         plan = wq.wq_describe_plan(fmt, O, I, S)
         bm, bn, bk = shape.split("x")
-        assert "bm=%s bn=%s bk=%s" % (bm, bn, bk) in plan, plan
+        assert "mode=%s bm=%s bn=%s bk=%s" % (mode, bm, bn, bk) in plan, plan
         gu.banner("forced shape " + plan)
         y = gu.run_dev(t, p.x)
     finally:
         wq.wq_tensor_free(t)
-        gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_SHAPE=None)
+        gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_MODE=None, WQ_TILED_SHAPE=None)
     y_ref, A = oracle.matmul(fmt, p.w, p.scales, p.x)
     gu.assert_within_bound(y, y_ref, A, "shape " + shape)

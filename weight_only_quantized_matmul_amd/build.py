@@ -27,6 +27,10 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
     # packed fp32 VALU forms are kept out of every code object
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in arch VGPRs: with AGPR accumulators the register
+    # allocator rotates the tiled kernels' loop-carried accumulators and
+    # copies them back every K step (about 90 extra VALU ops per step)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -258,46 +258,61 @@ __device__ __forceinline__ uint32_t bf16_pair(uint32_t lo_bits, uint32_t hi_bits
     return (lo_bits >> 16) | (hi_bits & 0xFFFF0000u);
 }
 
-// Activations -> three bf16 planes in device field order. Thread q of row s
-// covers positions 4q .. 4q+3 (four consecutive elements of x); rows past S,
-// elements past I and positions past the row's fields are written as zeros,
-// so every element of the planes is rewritten on every call.
+// Activations -> three bf16 planes in device field order, each stored
+// fragment-major: the block for rows [16 sg, 16 sg + 16) and positions
+// [32 kc, 32 kc + 32) is 1 KiB, holding at 16-byte slot l = li + 16 g the
+// eight positions 32 kc + 8 g .. +8 of row 16 sg + li. That is the operand
+// layout of v_mfma_f32_16x16x32_bf16, so the MFMA kernel loads a fragment
+// as one contiguous, fully coalesced 1 KiB access. Thread t fills slot t % 64
+// of block t / 64 (blocks ordered with kc fastest); rows past S, elements
+// past I and positions past the row's fields are written as zeros, so every
+// element of the planes is rewritten on every call.
 template <int FMT>
 __global__ __launch_bounds__(256) void split_x_kernel(const float *__restrict__ x, int S, int I, int nfull,
                                                       int vec_ok, int sp, int kp, long plane,
                                                       uint16_t *__restrict__ xp) {
-    const int q = blockIdx.x * 256 + threadIdx.x;
-    if (4 * q >= kp) return;
-    const long P = 4L * q;
-    const long e0 = elem_of_pos4(FMT, P, nfull);
-    for (int s = blockIdx.y; s < sp; s += gridDim.y) {
-        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (s < S) {
-            const float *xs = x + (long)s * I;
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    const int kcs = kp / 32;
+    if (t >= (long)sp / 16 * kcs * 64) return;
+    const int l = (int)(t & 63), li = l & 15, g = l >> 4;
+    const long blk = t >> 6;
+    const int s = (int)(blk / kcs) * 16 + li;
+    const long P = (blk % kcs) * 32 + 8 * g;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    if (s < S) {
+        const float *xs = x + (long)s * I;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const long e0 = elem_of_pos4(FMT, P + 4 * h, nfull);
             if (vec_ok && e0 + 4 <= I) {
-                const float4 t = *reinterpret_cast<const float4 *>(xs + e0);
-                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+                const float4 q = *reinterpret_cast<const float4 *>(xs + e0);
+                v[4 * h] = q.x; v[4 * h + 1] = q.y; v[4 * h + 2] = q.z; v[4 * h + 3] = q.w;
             } else {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (e0 + u < I) v[u] = xs[e0 + u];
+                    if (e0 + u < I) v[4 * h + u] = xs[e0 + u];
             }
         }
-        uint32_t b1[4], b2[4], b3[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t h = __float_as_uint(v[u]) & 0xFFFF0000u;
-            const float r = v[u] - __uint_as_float(h);  // exact
-            const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
-            b1[u] = h;
-            b2[u] = m;
-            b3[u] = __float_as_uint(r - __uint_as_float(m));  // exact, at most 8 significant bits
-        }
-        const long off = (long)s * kp + P;
-        *reinterpret_cast<u32x2 *>(xp + off) = u32x2{bf16_pair(b1[0], b1[1]), bf16_pair(b1[2], b1[3])};
-        *reinterpret_cast<u32x2 *>(xp + plane + off) = u32x2{bf16_pair(b2[0], b2[1]), bf16_pair(b2[2], b2[3])};
-        *reinterpret_cast<u32x2 *>(xp + 2 * plane + off) = u32x2{bf16_pair(b3[0], b3[1]), bf16_pair(b3[2], b3[3])};
     }
+    uint32_t b1[8], b2[8], b3[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t hb = __float_as_uint(v[e]) & 0xFFFF0000u;
+        const float r = v[e] - __uint_as_float(hb);  // exact
+        const uint32_t mb = __float_as_uint(r) & 0xFFFF0000u;
+        b1[e] = hb;
+        b2[e] = mb;
+        b3[e] = __float_as_uint(r - __uint_as_float(mb));  // exact, at most 8 significant bits
+    }
+    const long off = t * 8;
+    *reinterpret_cast<u32x4 *>(xp + off) =
+        u32x4{bf16_pair(b1[0], b1[1]), bf16_pair(b1[2], b1[3]), bf16_pair(b1[4], b1[5]), bf16_pair(b1[6], b1[7])};
+    *reinterpret_cast<u32x4 *>(xp + plane + off) =
+        u32x4{bf16_pair(b2[0], b2[1]), bf16_pair(b2[2], b2[3]), bf16_pair(b2[4], b2[5]), bf16_pair(b2[6], b2[7])};
+    *reinterpret_cast<u32x4 *>(xp + 2 * plane + off) =
+        u32x4{bf16_pair(b3[0], b3[1]), bf16_pair(b3[2], b3[3]), bf16_pair(b3[4], b3[5]), bf16_pair(b3[6], b3[7])};
 }
 
 // Raw weight bits for the 8 field positions [P0, P0 + 8) of a row (P0 a
@@ -350,25 +365,32 @@ __device__ __forceinline__ u32x4 codes_bf16x8(const RawW<FMT> &w) {
     return u32x4{bf16_pair(f[0], f[1]), bf16_pair(f[2], f[3]), bf16_pair(f[4], f[5]), bf16_pair(f[6], f[7])};
 }
 
-template <int WM, int WN, int BK>
+// bf16x3 tile: the block's WAVES waves are stacked along s. Wave w owns rows
+// [16*WM*w, 16*WM*(w+1)) of the block's BM = 16*WM*WAVES rows and all
+// BN = 16*WN columns, so its activation rows are its own: their fragments
+// are loaded from the planes straight into registers (MFMA operand layout,
+// one step ahead), and only the dequantized weight tile, shared by all the
+// waves, goes through LDS. Eight waves per block give two waves per SIMD,
+// which hide each other's load latency.
+template <int WAVES, int WM, int WN>
 struct X3Cfg {
-    static constexpr int BM = 32 * WM, BN = 32 * WN;
-    static constexpr int LDA = BK + 8;          // bf16 per LDS row (16 bytes of padding)
-    static constexpr int CH = BK / 8;           // 16-byte chunks per row per step
-    static constexpr int APL = BM * LDA;        // one activation plane of a stage (bf16)
-    static constexpr int AU = 3 * BM * CH / 256;       // activation chunks per thread
-    static constexpr int WU = (BN * CH + 255) / 256;   // weight chunks per thread
-    static constexpr int BROWS = WU * 256 / CH;        // B rows written (>= BN; the rest is never read)
-    static constexpr int STAGE = 3 * APL + BROWS * LDA;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BM = 16 * WM * WAVES, BN = 16 * WN, BK = 64;
+    // 16-byte operand reads (lane l: row l % 16, chunk l / 16) hit distinct
+    // banks when the row stride is an odd multiple of 32 bytes: 160 here
+    static constexpr int LDB = BK + 16;              // bf16 per LDS row
+    static constexpr int CH = BK / 8;                // 16-byte chunks per row per step
+    static constexpr int WU = (BN * CH + THREADS - 1) / THREADS; // weight chunks per thread
+    static constexpr int BROWS = WU * THREADS / CH;  // LDS rows written (>= BN; the rest are never read)
+    static constexpr int STAGE = BROWS * LDB;        // bf16 per stage
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static_assert((3 * BM * CH) % 256 == 0, "activation chunks must spread evenly");
-    static_assert((WU * 256) % CH == 0 && BROWS >= BN, "weight chunks must fill whole rows");
+    static_assert((WU * THREADS) % CH == 0 && BROWS >= BN, "weight chunks must fill whole rows");
 };
 
-template <int FMT, int WM, int WN, int BK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void tiled_x3_kernel(TiledArgs a) {
-    using C = X3Cfg<WM, WN, BK>;
-    constexpr int BM = C::BM, BN = C::BN, LDA = C::LDA, CH = C::CH, APL = C::APL;
+template <int FMT, int WAVES, int WM, int WN>
+__global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
+    using C = X3Cfg<WAVES, WM, WN>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LDB = C::LDB, CH = C::CH;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds16[];
 
     int s0, o0;
@@ -376,41 +398,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
     const int g = lane >> 4, li = lane & 15;
     const int nk = a.kp / BK;
 
+    // A fragments of one step: [m][plane][k half], lane (li, g) holds row
+    // 16m + li, positions 32 * half + 8g .. +8 of the step: one 1 KiB block
+    // of the fragment-major planes each
+    typedef u32x4 AFrag[WM][3][2];
+    const int kcs = a.kp / 32;
+    const uint16_t *ap = a.xp + ((long)(s0 / 16 + WM * wave) * kcs) * 512 + lane * 8;
+    auto load_a = [&](int kt, AFrag &af) {
+#pragma unroll
+        for (int m = 0; m < WM; ++m)
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    af[m][pl][h] = *reinterpret_cast<const u32x4 *>(ap + pl * a.plane +
+                                                                     ((long)m * kcs + 2 * kt + h) * 512);
+    };
+
     // Weight rows past O are read from row O - 1: they only feed output
     // columns that are never stored.
-    u32x4 ag[C::AU];
     RawW<FMT> wg[C::WU];
-    auto fetch = [&](int kt) {
+    auto load_w = [&](int kt) {
         const long k0 = (long)kt * BK;
 #pragma unroll
-        for (int j = 0; j < C::AU; ++j) {
-            const int u = tid + 256 * j;
-            const int pl = u / (BM * CH), r = (u / CH) % BM, c = u % CH;
-            ag[j] = *reinterpret_cast<const u32x4 *>(a.xp + pl * a.plane + (long)(s0 + r) * a.kp + k0 + 8 * c);
-        }
-#pragma unroll
         for (int j = 0; j < C::WU; ++j) {
-            const int u = tid + 256 * j;
+            const int u = tid + C::THREADS * j;
             const int row = min(o0 + u / CH, a.O - 1);
             wg[j].load(a.w + (long)row * a.stride, a.stride, k0 + 8 * (u % CH));
         }
     };
-    auto stash = [&](int buf) {
+    auto stash_w = [&](int buf) {
         uint16_t *st = lds16 + buf * C::STAGE;
 #pragma unroll
-        for (int j = 0; j < C::AU; ++j) {
-            const int u = tid + 256 * j;
-            const int pl = u / (BM * CH), r = (u / CH) % BM, c = u % CH;
-            *reinterpret_cast<u32x4 *>(st + pl * APL + r * LDA + 8 * c) = ag[j];
-        }
-#pragma unroll
         for (int j = 0; j < C::WU; ++j) {
-            const int u = tid + 256 * j;
-            *reinterpret_cast<u32x4 *>(st + 3 * APL + (u / CH) * LDA + 8 * (u % CH)) = codes_bf16x8<FMT>(wg[j]);
+            const int u = tid + C::THREADS * j;
+            *reinterpret_cast<u32x4 *>(st + (u / CH) * LDB + 8 * (u % CH)) = codes_bf16x8<FMT>(wg[j]);
         }
     };
 
@@ -420,78 +445,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // fragments of one 32-position sub-step: A (three planes) and B
-    constexpr int KK = BK / 32;
-    auto frags = [&](int buf, int kk, bf16x8 (&av)[WM][3], bf16x8 (&bv)[WN]) {
-        const uint16_t *As = lds16 + buf * C::STAGE;
-        const uint16_t *Bs = As + 3 * APL;
+    // One K step: A of step kt in `cur`; B of step kt in LDS buffer kt & 1;
+    // the weights of step kt + 1 (already in registers) go to the other
+    // buffer, released by the previous barrier; loads for later steps are
+    // issued first (clamped: the last steps reload data nobody reads).
+    auto iter = [&](int kt, const AFrag &cur, AFrag &nxt) {
+        const int buf = kt & 1;
+        load_a(min(kt + 1, nk - 1), nxt);
+        __builtin_amdgcn_sched_barrier(0);  // issue the activation loads first
+        const uint16_t *Bs = lds16 + buf * C::STAGE;
 #pragma unroll
-        for (int n = 0; n < WN; ++n)
-            bv[n] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * 16 * WN + n * 16 + li) * LDA + 32 * kk + 8 * g);
+        for (int h = 0; h < 2; ++h) {
+            bf16x8 bv[WN];
+#pragma unroll
+            for (int n = 0; n < WN; ++n)
+                bv[n] = *reinterpret_cast<const bf16x8 *>(Bs + (16 * n + li) * LDB + 32 * h + 8 * g);
+            if (h == 1) {
+                stash_w(buf ^ 1);
+                load_w(min(kt + 2, nk - 1));
+            }
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                for (int m = 0; m < WM; ++m) {
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, cur[m][pl][h]);
+#pragma unroll
+                    for (int n = 0; n < WN; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[n], acc[m][n], 0, 0, 0);
+                }
+        }
+        __syncthreads();
+    };
+
+    AFrag a0, a1;
+    load_w(0);
+    stash_w(0);
+    load_a(0, a0);
+    load_w(min(1, nk - 1));
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        iter(kt, a0, a1);
+        iter(kt + 1, a1, a0);
+    }
+    if (kt < nk) iter(kt, a0, a1);
+
+    // epilogue: lane holds rows 4g + r, column li of each 16x16 fragment
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+        const int o = o0 + 16 * n + li;
+        if (o >= a.O) continue;
+        const float sc = a.scales[o];
 #pragma unroll
         for (int m = 0; m < WM; ++m)
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl)
-                av[m][pl] = *reinterpret_cast<const bf16x8 *>(As + pl * APL + (wm * 16 * WM + m * 16 + li) * LDA +
-                                                              32 * kk + 8 * g);
-    };
-    auto mma = [&](const bf16x8 (&av)[WM][3], const bf16x8 (&bv)[WN]) {
-#pragma unroll
-        for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-            for (int m = 0; m < WM; ++m)
-#pragma unroll
-                for (int n = 0; n < WN; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m][pl], bv[n], acc[m][n], 0, 0, 0);
-    };
-
-    // Software pipeline, per K step kt (LDS buffer kt & 1 holds step kt):
-    //   region A: all fragment reads of the step; MFMAs of the first
-    //             sub-steps interleaved with the later reads
-    //   region B: MFMAs of the last sub-step interleaved with storing step
-    //             kt + 1 (fetched one step earlier) into the other buffer,
-    //             which the previous barrier released, and with the global
-    //             loads of step kt + 2
-    // In-order issue overlaps VALU, LDS and memory instructions with the
-    // matrix core only when they sit between MFMAs in program order; the
-    // sched_group_barrier sequences below ask the scheduler for that.
-    constexpr int NMMA = 3 * WM * WN;       // MFMAs per sub-step
-    constexpr int NREAD = 3 * WM + WN;      // fragment reads per sub-step
-    constexpr int NWRITE = C::AU + C::WU;   // LDS stores per step
-    constexpr int NLOAD = C::AU + C::WU;    // global loads per step
-    // the last two steps fetch (clamped) data that is stored but never read
-    fetch(0);
-    stash(0);
-    fetch(min(1, nk - 1));
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        bf16x8 av[KK][WM][3], bv[KK][WN];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) frags(buf, kk, av[kk], bv[kk]);
-#pragma unroll
-        for (int kk = 0; kk + 1 < KK; ++kk) mma(av[kk], bv[kk]);
-        __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-#pragma unroll
-        for (int i = 0; i < (KK - 1) * NMMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i < (KK - 1) * NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        stash(buf ^ 1);
-        fetch(min(kt + 2, nk - 1));
-        mma(av[KK - 1], bv[KK - 1]);
-#pragma unroll
-        for (int i = 0; i < NMMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-            if (i < NWRITE) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            if (i < NLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+            for (int r = 0; r < 4; ++r) {
+                const int s = s0 + 16 * WM * wave + 16 * m + 4 * g + r;
+                if (s < a.S) a.y[(long)s * a.O + o] = sc * acc[m][n][r];
+            }
     }
-    store_tile<WM, WN>(a, acc, s0, o0, wm, wn, g, li);
 }
 
 // ===========================================================================
@@ -514,19 +526,19 @@ hipError_t launch_f32(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int FMT, int WM, int WN, int BK>
+template <int FMT, int WAVES, int WM, int WN>
 hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
-    using C = X3Cfg<WM, WN, BK>;
+    using C = X3Cfg<WAVES, WM, WN>;
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile does not fit in LDS");
-    static const hipError_t lim = raise_lds_limit(&tiled_x3_kernel<FMT, WM, WN, BK>, C::LDS_BYTES);
+    static const hipError_t lim = raise_lds_limit(&tiled_x3_kernel<FMT, WAVES, WM, WN>, C::LDS_BYTES);
     if (lim != hipSuccess) return lim;
     const int vec_ok = ((a.I & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
-    const dim3 sgrid((unsigned)((p.kp / 4 + 255) / 256), (unsigned)std::min(p.sp, 65535));
-    hipLaunchKernelGGL((split_x_kernel<FMT>), sgrid, dim3(256), 0, st, a.x, a.S, a.I, a.nfull, vec_ok, p.sp, p.kp,
-                       (long)p.sp * p.kp, const_cast<uint16_t *>(a.xp));
+    const long slots = (long)p.sp * p.kp / 8;  // one thread per 16-byte fragment slot
+    hipLaunchKernelGGL((split_x_kernel<FMT>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st, a.x, a.S,
+                       a.I, a.nfull, vec_ok, p.sp, p.kp, (long)p.sp * p.kp, const_cast<uint16_t *>(a.xp));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WM, WN, BK>), dim3(p.grid), dim3(256), C::LDS_BYTES, st, a);
+    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES, st, a);
     return hipGetLastError();
 }
 
@@ -535,19 +547,15 @@ hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
 struct Shape {
     int bm, bn, bk;
 };
-constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 32}, {64, 64, 64}, {64, 64, 32}};
+constexpr Shape kX3Shapes[] = {{128, 96, 64}, {64, 64, 64}};
 constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
 
 template <int FMT>
 hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if constexpr (FMT != WQ_F32) {
         if (p.mode == kTiledBF16X3) {
-            if (p.bm == 128) {
-                if (p.bk == 64) return launch_x3<FMT, 4, 3, 64>(p, a, st);
-                return launch_x3<FMT, 4, 3, 32>(p, a, st);
-            }
-            if (p.bk == 64) return launch_x3<FMT, 2, 2, 64>(p, a, st);
-            return launch_x3<FMT, 2, 2, 32>(p, a, st);
+            if (p.bm == 128) return launch_x3<FMT, 8, 1, 6>(p, a, st);
+            return launch_x3<FMT, 4, 1, 4>(p, a, st);
         }
     }
     if (p.bm == 128) return launch_f32<FMT, 4, 3>(p, a, st);
@@ -567,7 +575,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape) {
     const bool use_big = S >= 128 && big >= 128;
     Shape sh;
     if (p.mode == kTiledBF16X3) {
-        sh = use_big ? kX3Shapes[0] : kX3Shapes[3];
+        sh = use_big ? kX3Shapes[0] : kX3Shapes[1];
         for (const Shape &c : kX3Shapes)
             if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk) sh = c;
     } else {
@@ -581,6 +589,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape) {
     p.tiles_s = (S + p.bm - 1) / p.bm;
     p.tiles_o = (O + p.bn - 1) / p.bn;
     p.grid = p.tiles_s * p.tiles_o;
+    p.block = (p.mode == kTiledBF16X3 && p.bm == 128) ? 512 : 256;
     if (p.mode == kTiledBF16X3) {
         const long stride = round_up(row_bytes(fmt, I), kRowAlign);
         const long npos = stride * elems_per_byte(fmt);
