@@ -77,7 +77,8 @@ typedef struct wq_group wq_group;   /* opaque set of tensors run in one launch *
  * environment knobs are read again (WQ_FORCE_PATH=gemv|tiled|auto,
  * WQ_GEMV_MAX_S, WQ_MEM_LIMIT_BYTES, WQ_FAULT=upload|launch,
  * WQ_TILED_MODE=bf16x3|fp32, WQ_TILED_SHAPE=BMxBNxBK (a compiled tile shape:
- * 128x96x64 or 64x64x64 in bf16x3 mode, 128x96x32 or 64x64x32 in fp32 mode),
+ * 128x96x64, 128x96x128 or 64x64x64 in bf16x3 mode, 128x96x32 or 64x64x32 in
+ * fp32 mode),
  * WQ_VERBOSE=1 prints one line per device on stderr).
  */
 int wq_init(const int *devices, int ndev);
@@ -131,7 +132,7 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
  * work is queued; y_dev is valid after the stream reaches it.
  * S <= the GEMV limit: one kernel launch, no workspace. Larger S with a
  * quantized format (tiled path, bf16x3 mode): two launches that use the
- * device's workspace (3 * round_up(S, 128) * round_up(fields per row, 64)
+ * device's workspace (3 * round_up(S, 128) * round_up(fields per row, 128)
  * bf16 values; wq_describe_plan prints the size). The workspace grows on
  * demand: growth waits for the device to go idle and allocates; a call being
  * captured into a HIP graph never grows it and returns WQ_E_UNSUPPORTED

@@ -117,15 +117,15 @@ def test_tiled_plan(fmt, O, I, S):
     assert int(p["tiles_s"]) * int(p["bm"]) >= S and int(p["tiles_o"]) * int(p["bn"]) >= O
     assert int(p["grid"]) == int(p["tiles_s"]) * int(p["tiles_o"])
     # plane rows hold every tile row the kernel reads: bm divides the 128-row padding
-    assert 128 % int(p["bm"]) == 0 and 64 % int(p["bk"]) == 0
+    assert 128 % int(p["bm"]) == 0 and 128 % int(p["bk"]) == 0
     if fmt == wq.WQ_F32:
         assert p["mode"] == "fp32" and p["workspace"] == "0"
     else:
-        # three bf16 planes of round_up(S, 128) rows by round_up(fields per row, 64)
+        # three bf16 planes of round_up(S, 128) rows by round_up(fields per row, 128)
         stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
         fields = stride * {wq.WQ_I8: 1, wq.WQ_I4: 2, wq.WQ_I2: 4}[fmt]
         assert p["mode"] == "bf16x3"
-        assert int(p["workspace"]) == 3 * (-(-S // 128) * 128) * (-(-fields // 64) * 64) * 2
+        assert int(p["workspace"]) == 3 * (-(-S // 128) * 128) * (-(-fields // 128) * 128) * 2
 
 
 def test_prefill_plan_uses_large_tiles():

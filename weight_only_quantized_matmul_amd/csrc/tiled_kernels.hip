@@ -372,12 +372,13 @@ __device__ __forceinline__ u32x4 codes_bf16x8(const RawW<FMT> &w) {
 // one step ahead), and only the dequantized weight tile, shared by all the
 // waves, goes through LDS. Eight waves per block give two waves per SIMD,
 // which hide each other's load latency.
-template <int WAVES, int WM, int WN>
+template <int WAVES, int WM, int WN, int BK_>
 struct X3Cfg {
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int BM = 16 * WM * WAVES, BN = 16 * WN, BK = 64;
+    static constexpr int BM = 16 * WM * WAVES, BN = 16 * WN, BK = BK_;
+    static constexpr int KH = BK / 32;               // 32-position MFMA steps per K step
     // 16-byte operand reads (lane l: row l % 16, chunk l / 16) hit distinct
-    // banks when the row stride is an odd multiple of 32 bytes: 160 here
+    // banks when the row stride is an odd multiple of 32 bytes (160 or 288 here)
     static constexpr int LDB = BK + 16;              // bf16 per LDS row
     static constexpr int CH = BK / 8;                // 16-byte chunks per row per step
     static constexpr int WU = (BN * CH + THREADS - 1) / THREADS; // weight chunks per thread
@@ -385,12 +386,22 @@ struct X3Cfg {
     static constexpr int STAGE = BROWS * LDB;        // bf16 per stage
     static constexpr int LDS_BYTES = 2 * STAGE * 2;
     static_assert((WU * THREADS) % CH == 0 && BROWS >= BN, "weight chunks must fill whole rows");
+    static_assert(kTiledKAlign % BK == 0 && ((LDB * 2 / 32) & 1) == 1, "K step and LDS row stride");
 };
 
-template <int FMT, int WAVES, int WM, int WN>
+constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
+
+// bf16x3 pipeline depths (measured on the 512 x 6144 x 6144 int8 prefill:
+// deeper activation prefetch and 2..8 weight sets all ran within 3%)
+constexpr int kX3ActPrefetch = 1;  // activation fragments loaded this many K steps ahead
+constexpr int kX3WeightSets = 4;   // weight-code register sets (loaded kX3WeightSets - 1 steps ahead)
+
+// PD: activation fragments are loaded PD steps ahead (PD + 1 register sets);
+// NW: weight codes are loaded NW - 1 steps before they are staged (NW sets)
+template <int FMT, int WAVES, int WM, int WN, int BK_, int PD, int NW>
 __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
-    using C = X3Cfg<WAVES, WM, WN>;
-    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LDB = C::LDB, CH = C::CH;
+    using C = X3Cfg<WAVES, WM, WN, BK_>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LDB = C::LDB, CH = C::CH, KH = C::KH;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds16[];
 
     int s0, o0;
@@ -401,10 +412,10 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     const int g = lane >> 4, li = lane & 15;
     const int nk = a.kp / BK;
 
-    // A fragments of one step: [m][plane][k half], lane (li, g) holds row
-    // 16m + li, positions 32 * half + 8g .. +8 of the step: one 1 KiB block
-    // of the fragment-major planes each
-    typedef u32x4 AFrag[WM][3][2];
+    // A fragments of one step: [m][plane][32-position part], lane (li, g)
+    // holds row 16m + li, positions 32 * part + 8g .. +8 of the step: one
+    // 1 KiB block of the fragment-major planes each
+    typedef u32x4 AFrag[WM][3][KH];
     const int kcs = a.kp / 32;
     const uint16_t *ap = a.xp + ((long)(s0 / 16 + WM * wave) * kcs) * 512 + lane * 8;
     auto load_a = [&](int kt, AFrag &af) {
@@ -413,29 +424,33 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < KH; ++h)
                     af[m][pl][h] = *reinterpret_cast<const u32x4 *>(ap + pl * a.plane +
-                                                                     ((long)m * kcs + 2 * kt + h) * 512);
+                                                                     ((long)m * kcs + KH * kt + h) * 512);
     };
 
+    // Weight codes travel through a ring of NW register sets: step j's raw
+    // codes sit in set j % NW, loaded NW - 1 steps before they are stored to
+    // LDS (they mostly come from HBM, and loads retire in issue order, so a
+    // short distance would also hold up the activation loads behind them).
     // Weight rows past O are read from row O - 1: they only feed output
     // columns that are never stored.
-    RawW<FMT> wg[C::WU];
-    auto load_w = [&](int kt) {
+    typedef RawW<FMT> WSet[C::WU];
+    auto load_w = [&](int kt, WSet &w) {
         const long k0 = (long)kt * BK;
 #pragma unroll
         for (int j = 0; j < C::WU; ++j) {
             const int u = tid + C::THREADS * j;
             const int row = min(o0 + u / CH, a.O - 1);
-            wg[j].load(a.w + (long)row * a.stride, a.stride, k0 + 8 * (u % CH));
+            w[j].load(a.w + (long)row * a.stride, a.stride, k0 + 8 * (u % CH));
         }
     };
-    auto stash_w = [&](int buf) {
+    auto stash_w = [&](int buf, const WSet &w) {
         uint16_t *st = lds16 + buf * C::STAGE;
 #pragma unroll
         for (int j = 0; j < C::WU; ++j) {
             const int u = tid + C::THREADS * j;
-            *reinterpret_cast<u32x4 *>(st + (u / CH) * LDB + 8 * (u % CH)) = codes_bf16x8<FMT>(wg[j]);
+            *reinterpret_cast<u32x4 *>(st + (u / CH) * LDB + 8 * (u % CH)) = codes_bf16x8<FMT>(w[j]);
         }
     };
 
@@ -445,24 +460,24 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // One K step: A of step kt in `cur`; B of step kt in LDS buffer kt & 1;
-    // the weights of step kt + 1 (already in registers) go to the other
-    // buffer, released by the previous barrier; loads for later steps are
-    // issued first (clamped: the last steps reload data nobody reads).
-    auto iter = [&](int kt, const AFrag &cur, AFrag &nxt) {
+    // One K step kt: A of step kt in `cur`, B of step kt in LDS buffer
+    // kt & 1. The weights of step kt + 1 (`wnext`) go to the other buffer,
+    // released by the previous barrier; activations of step kt + PD and
+    // weights of step kt + NW are loaded (clamped: the last steps reload
+    // data nobody reads).
+    auto iter = [&](int kt, const AFrag &cur, AFrag &nxt, const WSet &wnext, WSet &wload) {
         const int buf = kt & 1;
-        load_a(min(kt + 1, nk - 1), nxt);
-        __builtin_amdgcn_sched_barrier(0);  // issue the activation loads first
+        load_a(min(kt + PD, nk - 1), nxt);
         const uint16_t *Bs = lds16 + buf * C::STAGE;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < KH; ++h) {
             bf16x8 bv[WN];
 #pragma unroll
             for (int n = 0; n < WN; ++n)
                 bv[n] = *reinterpret_cast<const bf16x8 *>(Bs + (16 * n + li) * LDB + 32 * h + 8 * g);
-            if (h == 1) {
-                stash_w(buf ^ 1);
-                load_w(min(kt + 2, nk - 1));
+            if (h == KH / 2) {
+                stash_w(buf ^ 1, wnext);
+                load_w(min(kt + NW, nk - 1), wload);
             }
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl)
@@ -477,18 +492,26 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
         __syncthreads();
     };
 
-    AFrag a0, a1;
-    load_w(0);
-    stash_w(0);
-    load_a(0, a0);
-    load_w(min(1, nk - 1));
+    // Step j uses activation set j % (PD + 1) and weight set j % NW; the
+    // loop body covers U steps so that every index is a constant.
+    constexpr int U = (PD + 1) * NW / gcd_c(PD + 1, NW);
+    AFrag af[PD + 1];
+    WSet wg[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) load_w(min(i, nk - 1), wg[i]);
+    stash_w(0, wg[0]);
+#pragma unroll
+    for (int i = 0; i < PD; ++i) load_a(min(i, nk - 1), af[i]);
     __syncthreads();
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        iter(kt, a0, a1);
-        iter(kt + 1, a1, a0);
+    for (; kt + U <= nk; kt += U) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+            iter(kt + i, af[i % (PD + 1)], af[(i + PD) % (PD + 1)], wg[(i + 1) % NW], wg[i % NW]);
     }
-    if (kt < nk) iter(kt, a0, a1);
+#pragma unroll
+    for (int i = 0; i + 1 < U; ++i)
+        if (kt + i < nk) iter(kt + i, af[i % (PD + 1)], af[(i + PD) % (PD + 1)], wg[(i + 1) % NW], wg[i % NW]);
 
     // epilogue: lane holds rows 4g + r, column li of each 16x16 fragment
 #pragma unroll
@@ -526,11 +549,12 @@ hipError_t launch_f32(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int FMT, int WAVES, int WM, int WN>
+template <int FMT, int WAVES, int WM, int WN, int BK, int PD>
 hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
-    using C = X3Cfg<WAVES, WM, WN>;
+    using C = X3Cfg<WAVES, WM, WN, BK>;
+    constexpr int NW = kX3WeightSets;
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile does not fit in LDS");
-    static const hipError_t lim = raise_lds_limit(&tiled_x3_kernel<FMT, WAVES, WM, WN>, C::LDS_BYTES);
+    static const hipError_t lim = raise_lds_limit(&tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW>, C::LDS_BYTES);
     if (lim != hipSuccess) return lim;
     const int vec_ok = ((a.I & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
     const long slots = (long)p.sp * p.kp / 8;  // one thread per 16-byte fragment slot
@@ -538,7 +562,8 @@ hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
                        a.I, a.nfull, vec_ok, p.sp, p.kp, (long)p.sp * p.kp, const_cast<uint16_t *>(a.xp));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES, st, a);
+    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES,
+                       st, a);
     return hipGetLastError();
 }
 
@@ -547,15 +572,18 @@ hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
 struct Shape {
     int bm, bn, bk;
 };
-constexpr Shape kX3Shapes[] = {{128, 96, 64}, {64, 64, 64}};
+constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 128}, {64, 64, 64}};
 constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
 
 template <int FMT>
 hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if constexpr (FMT != WQ_F32) {
         if (p.mode == kTiledBF16X3) {
-            if (p.bm == 128) return launch_x3<FMT, 8, 1, 6>(p, a, st);
-            return launch_x3<FMT, 4, 1, 4>(p, a, st);
+            if (p.bm == 128) {
+                if (p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch>(p, a, st);
+                return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch>(p, a, st);
+            }
+            return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch>(p, a, st);
         }
     }
     if (p.bm == 128) return launch_f32<FMT, 4, 3>(p, a, st);
@@ -575,7 +603,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape) {
     const bool use_big = S >= 128 && big >= 128;
     Shape sh;
     if (p.mode == kTiledBF16X3) {
-        sh = use_big ? kX3Shapes[0] : kX3Shapes[1];
+        sh = use_big ? kX3Shapes[0] : kX3Shapes[2];
         for (const Shape &c : kX3Shapes)
             if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk) sh = c;
     } else {

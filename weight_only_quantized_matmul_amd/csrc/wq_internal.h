@@ -213,7 +213,7 @@ struct TiledArgs {
 
 constexpr int kTiledF32 = 0;     // fp32 operands, v_mfma_f32_16x16x4_f32
 constexpr int kTiledBF16X3 = 1;  // exact 3-way bf16 split of x, v_mfma_f32_16x16x32_bf16
-constexpr int kTiledKAlign = 64; // plane rows padded (with zeros) to this many positions
+constexpr int kTiledKAlign = 128; // plane rows padded (with zeros) to this many positions
 constexpr int kTiledSAlign = 128; // planes padded (with zero rows) to this many rows
 
 struct TiledPlan {
