@@ -48,7 +48,7 @@ extern "C" {
 #endif
 
 #define WQ_MAX_DEVICES 16   /* size of the static device table */
-#define WQ_GEMV_MAX_S 8     /* default largest S served by the register GEMV */
+#define WQ_GEMV_MAX_S 8     /* largest S the register GEMV serves (by default 4 for int4, which is faster on the tiled path above that) */
 
 enum wq_fmt { WQ_F32 = 0, WQ_I8 = 1, WQ_I4 = 2, WQ_I2 = 3 };
 

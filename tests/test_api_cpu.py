@@ -192,3 +192,10 @@ def test_init_without_gpu_reports_nodev():
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is visible; the no-device path is exercised on GPU-less hosts")
     assert wq.lib.wq_init(None, 0) == wq.WQ_E_NODEV
+
+
+@pytest.mark.parametrize("fmt,S,kind", [(wq.WQ_I4, 4, "gemv"), (wq.WQ_I4, 5, "tiled"), (wq.WQ_I4, 8, "tiled"),
+                                        (wq.WQ_I8, 8, "gemv"), (wq.WQ_I2, 8, "gemv"), (wq.WQ_F32, 8, "gemv")])
+def test_default_gemv_limit_per_format(fmt, S, kind):
+    """int4 leaves the register GEMV above S = 4; the other formats stay on it up to S = 8."""
+    assert _plan(fmt, 4096, 2048, S)[0] == kind

@@ -441,9 +441,9 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
     X(WQ_F32, 4, 16, 4, 2) X(WQ_F32, 8, 16, 2, 2)      \
     X(WQ_I8, 1, 16, 4, 2) X(WQ_I8, 2, 16, 2, 2)        \
     X(WQ_I8, 4, 16, 1, 4) X(WQ_I8, 8, 8, 1, 4)         \
-    X(WQ_I4, 1, 16, 4, 2) X(WQ_I4, 2, 16, 2, 2)        \
+    X(WQ_I4, 1, 16, 4, 2) X(WQ_I4, 2, 16, 1, 2)        \
     X(WQ_I4, 4, 16, 1, 4) X(WQ_I4, 8, 8, 1, 4)         \
-    X(WQ_I2, 1, 16, 2, 2) X(WQ_I2, 2, 16, 1, 4)        \
+    X(WQ_I2, 1, 16, 1, 2) X(WQ_I2, 2, 8, 1, 4)         \
     X(WQ_I2, 4, 8, 1, 4) X(WQ_I2, 8, 4, 1, 4)
 
 __global__ void relayout_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int fmt, int O,
