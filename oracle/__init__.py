@@ -63,6 +63,12 @@ def _load():
             ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_void_p, ctypes.c_long,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int]
+        if hasattr(lib, "oracle_matmul_gs"):
+            lib.oracle_matmul_gs.restype = ctypes.c_int
+            lib.oracle_matmul_gs.argtypes = [
+                ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_void_p, ctypes.c_long,
+                ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -132,3 +138,48 @@ def matmul_rows(fmt: int, w: np.ndarray, scales, x: np.ndarray, rows, I: int | N
     sub_w = np.ascontiguousarray(np.asarray(w)[rows])
     sub_s = None if scales is None else np.ascontiguousarray(np.asarray(scales)[rows])
     return matmul(fmt, sub_w, sub_s, x, I=I, threads=threads)
+
+
+def n_groups(I: int, gs: int) -> int:
+    return (int(I) + int(gs) - 1) // int(gs)
+
+
+def matmul_gs(fmt: int, w: np.ndarray, scales: np.ndarray, gs: int, x: np.ndarray, I: int | None = None,
+              threads: int | None = None, want_bound: bool = True):
+    """Oracle with group-wise scales: y (float32 [S,O]) and bound magnitude A.
+
+    scales: float32 [O, ceil(I/gs)], one scale per (row, group of gs columns).
+    """
+    lib = _load()
+    if int(gs) < 1:
+        raise ValueError("gs must be >= 1")
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be [S, I]")
+    S = x.shape[0]
+    if I is None:
+        I = x.shape[1]
+    if x.shape[1] != I:
+        raise ValueError("x has %d columns, I=%d" % (x.shape[1], I))
+    O, stride = w.shape
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    if scales.shape != (O, n_groups(I, gs)):
+        raise ValueError("scales must be [O, ceil(I/gs)]")
+    y = np.empty((S, O), dtype=np.float32)
+    a = np.empty((S, O), dtype=np.float64) if want_bound else None
+    rc = lib.oracle_matmul_gs(
+        int(fmt), O, int(I), w.ctypes.data, stride, scales.ctypes.data, int(gs),
+        x.ctypes.data, S, y.ctypes.data, a.ctypes.data if a is not None else None,
+        int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_matmul_gs rejected its arguments (rc=%d)" % rc)
+    return y, a
+
+
+def matmul_gs_rows(fmt: int, w: np.ndarray, scales: np.ndarray, gs: int, x: np.ndarray, rows,
+                   I: int | None = None, threads: int | None = None):
+    """matmul_gs restricted to output rows ``rows``: [S, len(rows)]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return matmul_gs(fmt, np.ascontiguousarray(np.asarray(w)[rows]),
+                     np.ascontiguousarray(np.asarray(scales)[rows]), gs, x, I=I, threads=threads)

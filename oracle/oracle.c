@@ -132,3 +132,58 @@ int oracle_matmul(int fmt, long O, long I, const unsigned char *w, long row_stri
     }
     return 0;
 }
+
+/*
+ * Group-wise scales: one scale per (row o, group of gs consecutive columns).
+ * The Vulkan tensor description ("三后端", section 三) carries a group-size
+ * field next to the scales; the CUDA tensor there has per-row scales only.
+ * Reading taken here: columns [g*gs, (g+1)*gs) of row o use
+ * scales[o*ng + g], ng = ceil(I/gs) (the last group may be shorter), and
+ *
+ *     y[s,o] = fl32( sum_g scales[o,g] * sum_{i in group g} q[o,i] * x[s,i] )
+ *
+ * Each group's sum runs in ascending column order in double, is multiplied
+ * by its scale in double and added to the row total in ascending group
+ * order; one rounding to float at the end. absb receives
+ * sum_i |scales[o, i/gs] * q[o,i] * x[s,i]|.
+ *
+ * scales: O x ng floats, row-major (required). gs >= 1.
+ * Returns 0, or -1 on an invalid argument.
+ */
+int oracle_matmul_gs(int fmt, long O, long I, const unsigned char *w, long row_stride,
+                     const float *scales, long gs, const float *x, long S, float *y, double *absb,
+                     int nthreads)
+{
+    long rb = oracle_row_bytes(fmt, I);
+    if (rb < 0 || O < 0 || S < 0 || row_stride < rb || gs < 1 || scales == NULL)
+        return -1;
+    long ng = (I + gs - 1) / gs;
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (long o = 0; o < O; ++o) {
+        const unsigned char *wrow = w + o * row_stride;
+        const float *srow = scales + o * ng;
+        for (long s = 0; s < S; ++s) {
+            const float *xrow = x + s * I;
+            double total = 0.0, magnitude = 0.0;
+            for (long g = 0; g < ng; ++g) {
+                long first = g * gs, end = first + gs < I ? first + gs : I;
+                double group_sum = 0.0, group_mag = 0.0;
+                for (long c = first; c < end; ++c) {
+                    double prod = oracle_weight(fmt, wrow, c) * (double)xrow[c];
+                    group_sum += prod;
+                    group_mag += fabs(prod);
+                }
+                double gscale = (double)srow[g];
+                total += gscale * group_sum;
+                magnitude += fabs(gscale) * group_mag;
+            }
+            y[s * O + o] = (float)total;
+            if (absb)
+                absb[s * O + o] = magnitude;
+        }
+    }
+    return 0;
+}

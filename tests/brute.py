@@ -75,3 +75,22 @@ def matmul_exact(fmt: int, w: np.ndarray, scales, x: np.ndarray, I: int):
 def matmul_rounded(fmt: int, w, scales, x, I: int) -> np.ndarray:
     ex = matmul_exact(fmt, w, scales, x, I)
     return np.array([[round_to_f32(v) for v in row] for row in ex], dtype=np.float32)
+
+
+def matmul_gs_exact(fmt: int, w: np.ndarray, gscales: np.ndarray, gs: int, x: np.ndarray, I: int):
+    """Exact y[s,o] with one scale per (row, group of gs columns): gscales [O, ceil(I/gs)]."""
+    O = w.shape[0]
+    S = x.shape[0]
+    xs = [[Fraction(float(v)) for v in x[s]] for s in range(S)]
+    out = [[None] * O for _ in range(S)]
+    for o in range(O):
+        q = codes(fmt, w[o].tobytes(), I)
+        sc = [Fraction(float(v)) for v in gscales[o]]
+        for s in range(S):
+            out[s][o] = sum((sc[i // gs] * q[i] * xs[s][i] for i in range(I)), Fraction(0))
+    return out
+
+
+def matmul_gs_rounded(fmt: int, w, gscales, gs: int, x, I: int) -> np.ndarray:
+    ex = matmul_gs_exact(fmt, w, gscales, gs, x, I)
+    return np.array([[round_to_f32(v) for v in row] for row in ex], dtype=np.float32)

@@ -55,3 +55,36 @@ def worked_examples():
             else:
                 raise ValueError("bad fixture line: %r" % line)
     return cases
+
+
+def group_scale_examples():
+    """List of dicts like worked_examples plus gs and gscales (float32 [O, ng])."""
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "group_scale_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(" ")
+            if key == "case":
+                cur = {"name": rest, "w": [], "x": [], "y": [], "gscales": []}
+            elif key == "end":
+                cur["w"] = np.array([list(bytes.fromhex(h)) for h in cur["w"]], dtype=np.uint8)
+                cur["x"] = np.array(cur["x"], dtype=np.float32)
+                cur["y"] = np.array(cur["y"], dtype=np.float32)
+                cur["gscales"] = np.array(cur["gscales"], dtype=np.float32)
+                cases.append(cur)
+                cur = None
+            elif key == "fmt":
+                cur["fmt"] = FMT[rest]
+            elif key in ("O", "I", "S", "gs"):
+                cur[key] = int(rest)
+            elif key == "w":
+                cur["w"].append(rest)
+            elif key == "gscales":
+                cur["gscales"].append([float(v) for v in rest.split()])
+            elif key in ("x", "y"):
+                cur[key].append([float(v) for v in rest.split()])
+            else:
+                raise ValueError("bad fixture line: %r" % line)
+    return cases

@@ -34,6 +34,12 @@ MUTANTS = {
     "f32_byte_offset": ("memcpy(&f, row + 4 * i, sizeof f);", "memcpy(&f, row + 2 * i, sizeof f);"),
     "sign_flipped": ("acc += t;", "acc -= t;"),
     "sum_in_float": ("double acc = 0.0, mag = 0.0;", "float acc = 0.0f; double mag = 0.0;"),
+    # group-wise scales
+    "gs_group_shifted": ("long first = g * gs, end", "long first = g * gs + 1, end"),
+    "gs_scales_transposed": ("const float *srow = scales + o * ng;", "const float *srow = scales + o;"),
+    "gs_scale_dropped": ("total += gscale * group_sum;", "total += group_sum;"),
+    "gs_last_group_dropped": ("for (long g = 0; g < ng; ++g) {", "for (long g = 0; g + 1 < ng; ++g) {"),
+    "gs_group_scale_of_next": ("double gscale = (double)srow[g];", "double gscale = (double)srow[(g + 1) % ng];"),
 }
 
 
@@ -49,7 +55,8 @@ def _run_mutant(name, old, new, tmp):
                     cpath, "-o", lpath, "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB_UNDER_TEST=lpath, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_gs_pins.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
 
