@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dense_gemv",
                     choices=["dense_gemv", "moe_decode", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
+                             "dense_gemv_gs128", "prefill_gs128",
                              "prefill"])
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -95,6 +96,16 @@ def problems_for(name):
         return [synth.int2_gemv(S=S)], "int2_gemv: int2 W[16384,8192] (codes U{0..3}), scales U[0.01,0.1], S=%d" % S
     if name == "prefill":
         return [synth.prefill(S=512)], "prefill: int8 W[6144,6144] (rint N(0,40) clipped), scales U[0.001,0.01], S=512"
+    if name == "dense_gemv_gs128":
+        p = synth.dense_gemv(S=1)
+        p.gs, p.gscales = 128, synth.group_scales(p, 128, 0.002, 0.05)
+        return [p], ("dense_gemv_gs128: int4 W[12288,6144] (codes U{0..15}), one scale per row and group of 128 "
+                     "columns U[0.002,0.05], x N(0,1), S=1")
+    if name == "prefill_gs128":
+        p = synth.prefill(S=512)
+        p.gs, p.gscales = 128, synth.group_scales(p, 128, 0.001, 0.01)
+        return [p], ("prefill_gs128: int8 W[6144,6144] (rint N(0,40) clipped), one scale per row and group of 128 "
+                     "columns U[0.001,0.01], S=512")
     raise ValueError(name)
 
 
@@ -127,15 +138,17 @@ def main():
     K, W = args.steps, args.warmup
     grouped = args.workload == "moe_decode"
     weight_bytes = sum(p.weight_bytes for p in probs)
-    alg_bytes = sum(p.weight_bytes + 4 * p.O + 4 * p.S * p.I + 4 * p.S * p.O for p in probs)
+    alg_bytes = sum(p.weight_bytes + 4 * p.O * (p.gscales.shape[1] if getattr(p, "gs", 0) else 1)
+                    + 4 * p.S * p.I + 4 * p.S * p.O for p in probs)
     alg_flops = sum(2.0 * p.S * p.O * p.I for p in probs)
-    compute_bound = args.workload == "prefill"
+    compute_bound = args.workload.startswith("prefill")
     n_rot = 1 if compute_bound else max(1, math.ceil(ROTATION_BYTES / weight_bytes))
 
     # resident weights: n_rot copies of the tensor set
     copies = []
     for _ in range(n_rot):
-        copies.append([wq.wq_tensor_upload(None, 0, p.fmt, p.O, p.I, p.w, p.scales) for p in probs])
+        copies.append([wq.wq_tensor_upload_gs(None, 0, p.fmt, p.O, p.I, p.gs, p.w, p.gscales) if getattr(p, "gs", 0)
+                       else wq.wq_tensor_upload(None, 0, p.fmt, p.O, p.I, p.w, p.scales) for p in probs])
     groups = [wq.wq_grouped_create(c) for c in copies] if grouped else None
     xs = [torch.from_numpy(p.x).to(dev) for p in probs]
     ys = [torch.empty((p.S, p.O), dtype=torch.float32, device=dev) for p in probs]
@@ -258,7 +271,10 @@ def cpu_baseline(probs, compute_bound, seconds):
     t0 = time.perf_counter()
     while True:
         for p, x in sample:
-            oracle.matmul(p.fmt, p.w, p.scales, x, threads=threads, want_bound=False)
+            if getattr(p, "gs", 0):
+                oracle.matmul_gs(p.fmt, p.w, p.gscales, p.gs, x, threads=threads, want_bound=False)
+            else:
+                oracle.matmul(p.fmt, p.w, p.scales, x, threads=threads, want_bound=False)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:

@@ -112,6 +112,24 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
                      const float *scales);
 
 /*
+ * Upload with group-wise scales: one fp32 scale per (output row o, group of
+ * gs consecutive columns) — the group-size field of the Vulkan tensor
+ * description (colibri "第 8 章 · 02 CUDA/Metal/Vulkan 三后端", section 三):
+ *     y[s,o] = sum_g scales[o*ng + g] * sum_{i in [g*gs, (g+1)*gs)} q[o,i] x[s,i],
+ * ng = ceil(I/gs) (the last group may be shorter).
+ *   scales: host pointer to O * ng floats, row-major (required).
+ *   gs:     group size, a positive multiple of 64 (WQ_E_UNSUPPORTED otherwise;
+ *           each 16-byte weight slot and each 64-column tiled step then lies
+ *           inside one group).
+ * Formats int8/int4/int2 only (WQ_E_INVAL for WQ_F32 or gs <= 0). Otherwise
+ * as wq_tensor_upload; a re-upload also checks gs (WQ_E_MISMATCH). The
+ * tensor then works with every matmul call; groups containing such tensors
+ * run one launch per tensor.
+ */
+int wq_tensor_upload_gs(wq_tensor **t, int device, int fmt, int O, int I, int gs, const void *w,
+                        const float *scales);
+
+/*
  * Lazy upload plus a synchronous matmul on host buffers (colibri-analysis
  * "CUDA 后端", section 1, coli_cuda_matmul: upload on first use, copy x in,
  * run, copy y back, all blocking).

@@ -77,6 +77,12 @@ def scales(g: np.random.Generator, O: int, lo: float, hi: float) -> np.ndarray:
     return g.uniform(lo, hi, O).astype(np.float32)
 
 
+def group_scales(p, gs: int, lo: float, hi: float) -> np.ndarray:
+    """One scale per (output row, group of gs columns) for problem p: float32 [O, ceil(I/gs)]."""
+    g = rng(20261290 + gs + p.O)
+    return g.uniform(lo, hi, size=(p.O, -(-p.I // gs))).astype(np.float32)
+
+
 def activations(g: np.random.Generator, S: int, I: int) -> np.ndarray:
     return g.standard_normal((S, I), dtype=np.float32)
 

@@ -199,3 +199,21 @@ def test_init_without_gpu_reports_nodev():
 def test_default_gemv_limit_per_format(fmt, S, kind):
     """int4 leaves the register GEMV above S = 4; the other formats stay on it up to S = 8."""
     assert _plan(fmt, 4096, 2048, S)[0] == kind
+
+
+def test_upload_gs_validation_without_device():
+    """Group-scale upload: arguments are checked before any device is touched."""
+    w = np.zeros((4, 64), np.uint8)   # int8 [4, 64]
+    sc = np.ones((4, 1), np.float32)
+
+    def up(fmt, gs, scales=sc, I=64):
+        h = ctypes.c_void_p(None)
+        return wq.lib.wq_tensor_upload_gs(ctypes.byref(h), 0, fmt, 4, I, gs, w.ctypes.data,
+                                          scales.ctypes.data if scales is not None else None)
+    assert up(wq.WQ_I8, 0) == wq.WQ_E_INVAL            # gs must be positive
+    assert up(wq.WQ_I8, -64) == wq.WQ_E_INVAL
+    assert up(wq.WQ_F32, 64) == wq.WQ_E_INVAL          # group scales are for quantized weights
+    assert up(wq.WQ_I8, 32) == wq.WQ_E_UNSUPPORTED     # not a multiple of 64
+    assert up(wq.WQ_I8, 100) == wq.WQ_E_UNSUPPORTED
+    assert up(wq.WQ_I8, 64, scales=None) == wq.WQ_E_INVAL
+    assert up(wq.WQ_I8, 64) in (wq.WQ_E_NOTINIT, wq.WQ_OK)  # valid: needs an opened device

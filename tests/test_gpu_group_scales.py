@@ -1,0 +1,157 @@
+"""GPU parity for tensors with group-wise scales (one scale per output row and
+group of gs columns) against the oracle's matmul_gs, through the C ABI."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU hosts
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gpu_util as gu  # noqa: E402
+import weight_only_quantized_matmul_amd as wq  # noqa: E402
+
+I8, I4, I2 = 1, 2, 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_GEMV_MAX_S=None, WQ_TILED_MODE=None, WQ_TILED_SHAPE=None)
+    yield
+
+
+def gscales(seed, O, I, gs, lo=0.002, hi=0.05):
+    return synth.rng(seed).uniform(lo, hi, size=(O, oracle.n_groups(I, gs))).astype(np.float32)
+
+
+def upload_gs(fmt, O, I, gs, w, sc):
+    return wq.wq_tensor_upload_gs(None, gu.DEV, fmt, O, I, gs, w, sc)
+
+
+def check(fmt, O, I, S, gs, seed, rows=None, what="gs"):
+    p = synth.ragged(fmt, O, I, S, seed=seed)
+    sc = gscales(seed + 1, O, I, gs)
+    t = upload_gs(fmt, O, I, gs, p.w, sc)
+    try:
+        gu.banner("%s fmt=%d O=%d I=%d S=%d gs=%d plan=%s" % (what, fmt, O, I, S, gs,
+                                                             wq.wq_describe_plan(fmt, O, I, S)))
+        y = gu.run_dev(t, p.x)
+    finally:
+        wq.wq_tensor_free(t)
+    if rows is None:
+        y_ref, A = oracle.matmul_gs(fmt, p.w, sc, gs, p.x)
+        gu.assert_within_bound(y, y_ref, A, what)
+    else:
+        y_ref, A = oracle.matmul_gs_rows(fmt, p.w, sc, gs, p.x, rows)
+        gu.assert_within_bound(y[:, rows], y_ref, A, what)
+    return y
+
+
+@pytest.mark.parametrize("fmt", [I8, I4, I2])
+@pytest.mark.parametrize("gs", [64, 128, 256])
+@pytest.mark.parametrize("S", [1, 2, 3, 8, 20, 130])
+def test_group_scales_parity(fmt, gs, S):
+    check(fmt, 300, 1000, S, gs, seed=8000 + 100 * fmt + gs + S)
+
+
+@pytest.mark.parametrize("fmt,O,I,S,gs", [(I4, 129, 64, 1, 64), (I2, 70, 4100, 2, 1024), (I8, 33, 5000, 9, 64),
+                                         (I4, 1000, 3000, 4, 4096), (I2, 17, 130, 40, 128)])
+def test_group_scales_ragged(fmt, O, I, S, gs):
+    check(fmt, O, I, S, gs, seed=8500 + O + I + S, what="gs-ragged")
+
+
+def test_group_scales_dense_decode_shape():
+    rows = np.arange(0, 12288, 97)
+    check(I4, 12288, 6144, 1, 128, seed=8600, rows=rows, what="gs-dense")
+
+
+def test_group_scales_prefill_shape():
+    rows = np.arange(0, 6144, 191)
+    check(I8, 6144, 6144, 512, 128, seed=8601, rows=rows, what="gs-prefill")
+
+
+@pytest.mark.parametrize("fmt,I", [(I8, 256), (I4, 512), (I2, 1024)])
+@pytest.mark.parametrize("S", [1, 8, 24])
+def test_group_scales_one_hot_bit_exact(fmt, I, S):
+    gs = 64
+    row = np.arange(256, dtype=np.uint8)[None, :]
+    O = 4
+    w = np.repeat(row, O, axis=0)
+    sc = gscales(8700 + fmt, O, I, gs, 0.01, 3.0)
+    t = upload_gs(fmt, O, I, gs, w, sc)
+    g = synth.rng(8710 + fmt + S)
+    try:
+        for c0 in range(0, I, S * 8):
+            cols = np.arange(c0, min(I, c0 + S * 8), 8)[:S]
+            cols = (cols + g.integers(0, 8, size=cols.size)).clip(max=I - 1)
+            x = np.zeros((cols.size, I), np.float32)
+            x[np.arange(cols.size), cols] = 1.0
+            gu.banner("gs one-hot fmt=%d S=%d c0=%d" % (fmt, x.shape[0], c0))
+            y = gu.run_dev(t, x)
+            y_ref, _ = oracle.matmul_gs(fmt, w, sc, gs, x)
+            np.testing.assert_array_equal(y, y_ref)
+    finally:
+        wq.wq_tensor_free(t)
+
+
+@pytest.mark.parametrize("fmt,zero", [(I8, 0x00), (I4, 0x88), (I2, 0xAA)])
+@pytest.mark.parametrize("S", [1, 8, 40])
+def test_group_scales_zero_rows_exact(fmt, zero, S):
+    O, I, gs = 67, 900, 128
+    p = synth.ragged(fmt, O, I, S, seed=8800 + fmt + S)
+    sc = gscales(8801 + fmt, O, I, gs)
+    p.w[5] = zero          # all codes decode to 0
+    sc[7] = 0.0            # every group scale of a row is 0
+    sc[20, 1] = 0.0        # one group of a row is 0: only that group drops out
+    t = upload_gs(fmt, O, I, gs, p.w, sc)
+    try:
+        gu.banner("gs zeros fmt=%d S=%d" % (fmt, S))
+        y = gu.run_dev(t, p.x)
+    finally:
+        wq.wq_tensor_free(t)
+    assert np.all(y[:, 5] == 0.0) and np.all(y[:, 7] == 0.0)
+    y_ref, A = oracle.matmul_gs(fmt, p.w, sc, gs, p.x)
+    gu.assert_within_bound(y, y_ref, A, "gs zeros")
+
+
+def test_group_scales_in_a_group_call():
+    """Grouped calls holding group-scaled tensors run per tensor, still stream-ordered."""
+    probs = [synth.ragged(I4, 512, 2048, 1, seed=8900 + k) for k in range(3)]
+    scs = [gscales(8950 + k, 512, 2048, 128) for k in range(3)]
+    ts = [upload_gs(I4, 512, 2048, 128, p.w, sc) for p, sc in zip(probs, scs)]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x).cuda() for p in probs]
+        ys = [torch.empty((1, 512), device="cuda") for _ in probs]
+        gu.banner("gs grouped call")
+        wq.wq_grouped_matmul_dev(g, xs, ys)
+        torch.cuda.synchronize()
+        for p, sc, y in zip(probs, scs, ys):
+            y_ref, A = oracle.matmul_gs(I4, p.w, sc, 128, p.x)
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, "gs grouped")
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
+def test_group_scale_reupload_checks_gs():
+    p = synth.ragged(I8, 16, 256, 1, seed=9000)
+    sc = gscales(9001, 16, 256, 64)
+    t = upload_gs(I8, 16, 256, 64, p.w, sc)
+    try:
+        assert wq.wq_tensor_upload_gs(t, gu.DEV, I8, 16, 256, 64, None, None) is t
+        with pytest.raises(wq.WqError) as ei:
+            wq.wq_tensor_upload_gs(t, gu.DEV, I8, 16, 256, 128, None, None)
+        assert ei.value.code == wq.WQ_E_MISMATCH
+        with pytest.raises(wq.WqError) as ei:
+            wq.wq_tensor_upload(t, gu.DEV, I8, 16, 256, None, None)
+        assert ei.value.code == wq.WQ_E_MISMATCH
+    finally:
+        wq.wq_tensor_free(t)

@@ -58,6 +58,7 @@ def _bind(lib):
         "wq_mem_info": (ci, [ci, _c_size_p, _c_size_p]),
         "wq_row_bytes": (cl, [ci, cl]),
         "wq_tensor_upload": (ci, [ctypes.POINTER(vp), ci, ci, ci, ci, vp, vp]),
+        "wq_tensor_upload_gs": (ci, [ctypes.POINTER(vp), ci, ci, ci, ci, ci, vp, vp]),
         "wq_matmul": (ci, [ctypes.POINTER(vp), ci, ci, ci, ci, vp, vp, vp, ci, vp]),
         "wq_matmul_t": (ci, [vp, vp, ci, vp]),
         "wq_matmul_dev": (ci, [vp, vp, ci, vp, vp]),
@@ -183,6 +184,21 @@ def wq_tensor_upload(t, device: int, fmt: int, O: int, I: int, w, scales) -> Ten
         wp, sp = None, None
     _check(lib.wq_tensor_upload(ctypes.byref(h), int(device), int(fmt), int(O), int(I), wp, sp),
            "wq_tensor_upload")
+    return t if t is not None else Tensor(h, int(device), int(fmt), int(O), int(I))
+
+
+def wq_tensor_upload_gs(t, device: int, fmt: int, O: int, I: int, gs: int, w, scales) -> Tensor:
+    """Upload with group-wise scales (scales float32 [O, ceil(I/gs)]) or validate; returns the handle."""
+    h = ctypes.c_void_p(t.ptr.value if t is not None else None)
+    if t is None:
+        w, _ = _weights(fmt, O, I, w, None)
+        ng = (int(I) + int(gs) - 1) // int(gs) if int(gs) > 0 else 1
+        scales = _host_f32(scales, (O, ng), "scales")
+        wp, sp = w.ctypes.data, scales.ctypes.data
+    else:
+        wp, sp = None, None
+    _check(lib.wq_tensor_upload_gs(ctypes.byref(h), int(device), int(fmt), int(O), int(I), int(gs), wp, sp),
+           "wq_tensor_upload_gs")
     return t if t is not None else Tensor(h, int(device), int(fmt), int(O), int(I))
 
 

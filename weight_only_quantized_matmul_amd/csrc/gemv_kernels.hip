@@ -142,11 +142,14 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
 // One team processes rows [row_begin, row_begin + rpt) (rows >= O are not
 // stored). red: LDS scratch of 2 * kMaxTeam * D * SMAX floats, used when
 // team > 1 (then the block is exactly one team).
-template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool XL = false>
+// GS: group-wise scales (rows in natural order; scales[row * ng + i / gs]);
+// each lane slot lies in one group, so a slot's partial sum is scaled once.
+template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool XL = false, bool GS = false>
 __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long stride, int nfull,
                                           const float *__restrict__ scales, const float *__restrict__ x,
                                           float *__restrict__ y, int O, int I, int S, int team, int tl,
-                                          int wave_in_team, int row_begin, int rpt, float *red) {
+                                          int wave_in_team, int row_begin, int rpt, float *red, int gs = 0,
+                                          int ng = 1) {
     // KMAX is the exact number of load slots per lane: every slot is loaded
     // unconditionally (a slot past the row re-reads the row start, see
     // below), which keeps the compiler's memory wait counts exact.
@@ -245,17 +248,31 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
     // activations (cache hits) complete first and are prepared while the
     // first rows stream in.
     uint32_t ring[D][KMAX][WPC];
-    auto load_row = [&](uint32_t (&b)[KMAX][WPC], int row) {
-        const uint8_t *p = w + (long)min(row, row_last) * stride;  // wave-uniform
+    float gring[D][KMAX];  // GS: the group scale of each slot, per row in flight
+    int grp[KMAX];         // GS: group of each slot (clamped: dead slots have zero activations)
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) grp[k] = GS ? min(xb[k] / max(gs, 1), ng - 1) : 0;
+    auto load_row = [&](uint32_t (&b)[KMAX][WPC], float (&gv)[KMAX], int row) {
+        const long r = min(row, row_last);
+        const uint8_t *p = w + r * stride;  // wave-uniform
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) load_w<LW>(p + cb[k], b[k]);
+        if constexpr (GS) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) gv[k] = scales[r * ng + grp[k]];
+        }
     };
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_row(ring[d], row_begin + d);
+    for (int d = 0; d < D; ++d) load_row(ring[d], gring[d], row_begin + d);
 
     float sx[SMAX];
 #pragma unroll
     for (int s = 0; s < SMAX; ++s) sx[s] = 0.0f;
+    float sxk[KMAX][SMAX];  // GS: activation sums per slot
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) sxk[k][s] = 0.0f;
     if (wave_in) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
@@ -265,7 +282,10 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 for (int e = 0; e < EPC; ++e) {
                     const float v = xr[k][e][s];
                     xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
-                    if constexpr (OFF != 0) sx[s] += v;
+                    if constexpr (OFF != 0) {
+                        if constexpr (GS) sxk[k][s] += v;
+                        else sx[s] += v;
+                    }
                 }
     } else {
 #pragma unroll
@@ -278,13 +298,16 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     const bool in = live[k] && ei < I;
                     const float v = in ? xr[k][e][s] : 0.0f;
                     xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
-                    if constexpr (OFF != 0) sx[s] += v;
+                    if constexpr (OFF != 0) {
+                        if constexpr (GS) sxk[k][s] += v;
+                        else sx[s] += v;
+                    }
                 }
     }
 #undef WQ_XE
 
     // Partial sums of one row (wave total in lane 63).
-    auto row_partials = [&](uint32_t (&b)[KMAX][WPC], float (&part)[SMAX]) {
+    auto row_partials = [&](uint32_t (&b)[KMAX][WPC], const float (&gv)[KMAX], float (&part)[SMAX]) {
         if constexpr (FMT == WQ_F32) {
 #pragma unroll
             for (int k = 0; k < KMAX; ++k)
@@ -299,13 +322,29 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (k < K) {
+                if constexpr (GS) {
+                    // the slot's sum (offset removed with its own activation
+                    // sum, so all-zero codes give exactly 0) times its group scale
+                    float t[SMAX];
 #pragma unroll
-                for (int j = 0; j < WPC; ++j) word_fma<FMT, SMAX>(b[k][j], &xr[k][j * EPW], acc);
+                    for (int s = 0; s < SMAX; ++s) t[s] = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < WPC; ++j) word_fma<FMT, SMAX>(b[k][j], &xr[k][j * EPW], t);
+#pragma unroll
+                    for (int s = 0; s < SMAX; ++s) {
+                        float u = t[s];
+                        if constexpr (OFF != 0) u -= (float)OFF * sxk[k][s];
+                        acc[s] = fmaf(gv[k], u, acc[s]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < WPC; ++j) word_fma<FMT, SMAX>(b[k][j], &xr[k][j * EPW], acc);
+                }
             }
 #pragma unroll
         for (int s = 0; s < SMAX; ++s) {
             float t = acc[s];
-            if constexpr (OFF != 0) t -= (float)OFF * sx[s];
+            if constexpr (OFF != 0 && !GS) t -= (float)OFF * sx[s];
             part[s] = wave_sum_lane63(t);
         }
     };
@@ -318,7 +357,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             for (int d = 0; d < D; ++d) {
                 if (d < nvalid) {
                     const int row = row0 + d;
-                    const float sc = scales[min(row, O - 1)];  // wave-uniform: scalar load
+                    const float sc = GS ? 1.0f : scales[min(row, O - 1)];  // wave-uniform: scalar load
                     if (lane == 63 && row <= row_last) {
 #pragma unroll
                         for (int s = 0; s < SMAX; ++s)
@@ -336,7 +375,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             }
             float sc[D];  // wave-uniform rows: scalar loads
 #pragma unroll
-            for (int d = 0; d < D; ++d) sc[d] = scales[min(row0 + d, O - 1)];
+            for (int d = 0; d < D; ++d) sc[d] = GS ? 1.0f : scales[min(row0 + d, O - 1)];
             __syncthreads();
             if (wave_in_team == 0 && lane < D * SMAX) {
                 const int d = lane / SMAX, s = lane % SMAX;
@@ -358,8 +397,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
         float part[D][SMAX];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            row_partials(ring[d], part[d]);
-            load_row(ring[d], row_begin + i + d + D);
+            row_partials(ring[d], gring[d], part[d]);
+            load_row(ring[d], gring[d], row_begin + i + d + D);
         }
         finish(row_begin + i, part, D);
     }
@@ -368,7 +407,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if (i + d < rpt) {
-                row_partials(ring[d], part[d]);
+                row_partials(ring[d], gring[d], part[d]);
             } else {
 #pragma unroll
                 for (int s = 0; s < SMAX; ++s) part[d][s] = 0.0f;
@@ -381,7 +420,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 // XL: the block first copies the S x I activations into LDS (one coalesced
 // pass per block instead of one per wave) and the waves stage their
 // registers from there; used when x fits (host check) and XV holds.
-template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool XL>
+template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool XL, bool GS = false>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     __shared__ float red[2 * kMaxTeam * D * SMAX];
     extern __shared__ __attribute__((aligned(16))) float xl[];
@@ -401,9 +440,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         xsrc = xl;
     }
     if (row_begin >= a.O) return;  // uniform over the team (and the block when team > 1)
-    team_rows<FMT, SMAX, LW, KS, D, XV, XL>(a.w, a.stride, a.nfull, a.scales, xsrc, a.y, a.O, a.I, a.S, a.team,
-                                            wave_in_team * 64 + lane, wave_in_team, row_begin, a.rows_per_team,
-                                            red);
+    team_rows<FMT, SMAX, LW, KS, D, XV, XL, GS>(a.w, a.stride, a.nfull, a.scales, xsrc, a.y, a.O, a.I, a.S,
+                                                a.team, wave_in_team * 64 + lane, wave_in_team, row_begin,
+                                                a.rows_per_team, red, a.gs, a.ng);
 }
 
 template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV>
@@ -511,6 +550,17 @@ hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStrea
 #define WQ_K(KS)                                                                                          \
     if constexpr (KS <= KM) {                                                                             \
         if (p.k == KS) {                                                                                  \
+            if constexpr (F != WQ_F32) {                                                                  \
+                if (a.gs > 0) {                                                                           \
+                    if (xl)                                                                               \
+                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, true, true, true>), dim3(p.grid), \
+                                           dim3(p.block), xbytes, st, a);                                 \
+                    else                                                                                  \
+                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, false, false, true>), dim3(p.grid), \
+                                           dim3(p.block), 0, st, a);                                      \
+                    return hipGetLastError();                                                             \
+                }                                                                                         \
+            }                                                                                             \
             if (xl)                                                                                       \
                 hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, true, true>), dim3(p.grid), dim3(p.block), \
                                    xbytes, st, a);                                                        \

@@ -189,6 +189,8 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
         a.y = y;
         a.stride = t->stride;
         a.nfull = t->nfull;
+        a.gs = t->gs;
+        a.ng = t->ng;
         a.O = t->O;
         a.I = t->I;
         a.S = S;
@@ -198,14 +200,16 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
         a.rows_per_team = gp.rows_per_team;
         return hip_status(wq::launch_gemv(gp, a, st));
     }
-    const wq::TiledPlan tp = wq::plan_tiled(t->fmt, t->O, t->I, S, g_cfg.tiled_mode, g_cfg.tiled_shape);
+    const wq::TiledPlan tp = wq::plan_tiled(t->fmt, t->O, t->I, S, g_cfg.tiled_mode, g_cfg.tiled_shape, t->gs);
     wq::TiledArgs a;
     a.w = t->d_w;
-    a.scales = t->d_scales;
+    a.scales = t->gs > 0 ? t->d_scales_t : t->d_scales;
     a.x = x;
     a.y = y;
     a.stride = t->stride;
     a.nfull = t->nfull;
+    a.gs = t->gs;
+    a.ng = t->ng;
     a.O = t->O;
     a.I = t->I;
     a.S = S;
@@ -311,13 +315,22 @@ int wq_mem_info(int device, size_t *free_b, size_t *total_b) {
 
 long wq_row_bytes(int fmt, long I) { return wq::row_bytes(fmt, I); }
 
-int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const void *w, const float *scales) {
+} // extern "C"
+
+namespace {
+
+// gs == 0: one scale per row (device rows permuted in 1 KiB blocks);
+// gs > 0: O x ceil(I/gs) scales, rows kept in natural element order.
+int upload_impl(wq_tensor **t, int device, int fmt, int O, int I, int gs, const void *w, const float *scales) {
     if (t == nullptr) return WQ_E_INVAL;
-    if (!valid_fmt(fmt) || O <= 0 || I <= 0 || device < 0 || device >= WQ_MAX_DEVICES) return WQ_E_INVAL;
+    if (!valid_fmt(fmt) || O <= 0 || I <= 0 || device < 0 || device >= WQ_MAX_DEVICES || gs < 0)
+        return WQ_E_INVAL;
+    if (gs > 0 && fmt == WQ_F32) return WQ_E_INVAL;  // scales apply to quantized weights only
+    if (gs > 0 && gs % wq::kGroupAlign != 0) return WQ_E_UNSUPPORTED;
     if (*t != nullptr) {
         const wq_tensor *r = *t;
         if (!tensor_ok(r)) return WQ_E_INVAL;
-        if (r->device != device || r->fmt != fmt || r->O != O || r->I != I) return WQ_E_MISMATCH;
+        if (r->device != device || r->fmt != fmt || r->O != O || r->I != I || r->gs != gs) return WQ_E_MISMATCH;
         return WQ_OK;
     }
     if (w == nullptr) return WQ_E_INVAL;
@@ -330,17 +343,25 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
 
     const long rb = wq::row_bytes(fmt, I);
     const long stride = wq::round_up(rb, wq::kRowAlign);
+    const int ng = gs > 0 ? (int)(((long)I + gs - 1) / gs) : 1;
     const size_t wbytes = (size_t)O * stride;
-    const size_t sbytes = (size_t)O * sizeof(float);
-    void *dw = nullptr, *ds = nullptr;
+    const size_t sbytes = (size_t)O * ng * sizeof(float);
+    void *dw = nullptr, *ds = nullptr, *dst_t = nullptr;
     int rc = dev_alloc(d, &dw, wbytes);
     if (rc != WQ_OK) return rc;
     rc = dev_alloc(d, &ds, sbytes);
+    if (rc == WQ_OK && gs > 0) rc = dev_alloc(d, &dst_t, sbytes);
     if (rc != WQ_OK) {
         dev_free(d, dw, wbytes);
+        dev_free(d, ds, sbytes);
         return rc;
     }
-    const int nfull = wq::full_blocks(fmt, rb);
+    auto free_all = [&]() {
+        dev_free(d, dw, wbytes);
+        dev_free(d, ds, sbytes);
+        if (dst_t) dev_free(d, dst_t, sbytes);
+    };
+    const int nfull = gs > 0 ? 0 : wq::full_blocks(fmt, rb);
     hipError_t e = hipSuccess;
     if (nfull == 0) {
         // natural order: copy rows into the padded stride
@@ -356,8 +377,7 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
         void *tmp = nullptr;
         if (hipMalloc(&tmp, (size_t)O * rb) != hipSuccess) {
             (void)hipGetLastError();
-            dev_free(d, dw, wbytes);
-            dev_free(d, ds, sbytes);
+            free_all();
             return WQ_E_OOM;
         }
         e = hipMemcpyAsync(tmp, w, (size_t)O * rb, hipMemcpyHostToDevice, d.stream);
@@ -370,23 +390,28 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
     std::vector<float> ones;
     if (e == hipSuccess) {
         const float *src = scales;
-        if (src == nullptr) {
+        if (src == nullptr) {  // f32 without scales (gs == 0 only)
             ones.assign(O, 1.0f);
             src = ones.data();
         }
         e = hipMemcpyAsync(ds, src, sbytes, hipMemcpyHostToDevice, d.stream);
     }
+    std::vector<float> st;
+    if (e == hipSuccess && gs > 0) {  // group-major copy for the tiled path
+        st.resize((size_t)O * ng);
+        for (long o = 0; o < O; ++o)
+            for (long g = 0; g < ng; ++g) st[(size_t)g * O + o] = scales[(size_t)o * ng + g];
+        e = hipMemcpyAsync(dst_t, st.data(), sbytes, hipMemcpyHostToDevice, d.stream);
+    }
     if (e == hipSuccess) e = hipStreamSynchronize(d.stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
-        dev_free(d, dw, wbytes);
-        dev_free(d, ds, sbytes);
+        free_all();
         return hip_status(e);
     }
     wq_tensor *nt = new (std::nothrow) wq_tensor;
     if (!nt) {
-        dev_free(d, dw, wbytes);
-        dev_free(d, ds, sbytes);
+        free_all();
         return WQ_E_OOM;
     }
     nt->magic = wq::kTensorMagic;
@@ -397,11 +422,28 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
     nt->rb = rb;
     nt->stride = stride;
     nt->nfull = nfull;
+    nt->gs = gs;
+    nt->ng = ng;
     nt->d_w = (uint8_t *)dw;
     nt->d_scales = (float *)ds;
-    nt->bytes = wbytes + sbytes;
+    nt->d_scales_t = (float *)dst_t;
+    nt->bytes = wbytes + sbytes * (gs > 0 ? 2 : 1);
     *t = nt;
     return WQ_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const void *w, const float *scales) {
+    return upload_impl(t, device, fmt, O, I, 0, w, scales);
+}
+
+int wq_tensor_upload_gs(wq_tensor **t, int device, int fmt, int O, int I, int gs, const void *w,
+                        const float *scales) {
+    if (gs <= 0) return WQ_E_INVAL;
+    return upload_impl(t, device, fmt, O, I, gs, w, scales);
 }
 
 int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y) {
@@ -486,6 +528,7 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
         gd.I = ts[i]->I;
         gd.pad = 0;
         g->h_desc.push_back(gd);
+        if (ts[i]->gs > 0) g->has_gs = true;
     }
     auto fail = [&](int rc) {
         for (auto &b : g->buckets)
@@ -578,7 +621,7 @@ int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, 
     hipStream_t st = (hipStream_t)hip_stream;
     const int bucket = wq::gemv_smax_bucket(smax);
     const int bi = bucket == 1 ? 0 : bucket == 2 ? 1 : bucket == 4 ? 2 : bucket == 8 ? 3 : -1;
-    const bool one_launch = g_cfg.force_path != 2 && smax <= gemv_limit(g->fmt) && bi >= 0 &&
+    const bool one_launch = !g->has_gs && g_cfg.force_path != 2 && smax <= gemv_limit(g->fmt) && bi >= 0 &&
                             g->buckets[bi].plan.ok;
     if (!one_launch) {
         for (int i = 0; i < g->G; ++i) {
@@ -638,7 +681,8 @@ int wq_tensor_free(wq_tensor *t) {
     std::lock_guard<std::recursive_mutex> lk(d.mu);
     DeviceGuard guard(t->device);
     dev_free(d, t->d_w, (size_t)t->O * t->stride);
-    dev_free(d, t->d_scales, (size_t)t->O * sizeof(float));
+    dev_free(d, t->d_scales, (size_t)t->O * t->ng * sizeof(float));
+    if (t->d_scales_t) dev_free(d, t->d_scales_t, (size_t)t->O * t->ng * sizeof(float));
     t->magic = 0;
     delete t;
     return WQ_OK;

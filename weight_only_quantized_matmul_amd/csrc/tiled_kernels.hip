@@ -398,7 +398,11 @@ constexpr int kX3WeightSets = 4;   // weight-code register sets (loaded kX3Weigh
 
 // PD: activation fragments are loaded PD steps ahead (PD + 1 register sets);
 // NW: weight codes are loaded NW - 1 steps before they are staged (NW sets)
-template <int FMT, int WAVES, int WM, int WN, int BK_, int PD, int NW>
+// GS: group-wise scales (rows in natural order, gs a multiple of BK = 64):
+// each K step lies in one group; the steps of a group accumulate into
+// separate fragments, which are added to the accumulators times the group
+// scale of their output column when the group ends.
+template <int FMT, int WAVES, int WM, int WN, int BK_, int PD, int NW, bool GS>
 __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     using C = X3Cfg<WAVES, WM, WN, BK_>;
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LDB = C::LDB, CH = C::CH, KH = C::KH;
@@ -465,9 +469,27 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     // released by the previous barrier; activations of step kt + PD and
     // weights of step kt + NW are loaded (clamped: the last steps reload
     // data nobody reads).
+    f32x4 tacc[WM][WN];  // GS: the current group's sums
     auto iter = [&](int kt, const AFrag &cur, AFrag &nxt, const WSet &wnext, WSet &wload) {
         const int buf = kt & 1;
         load_a(min(kt + PD, nk - 1), nxt);
+        float gsc[WN];
+        bool group_ends = false;
+        if constexpr (GS) {
+            static_assert(BK == kGroupAlign, "a group-scaled K step must lie in one group");
+            const long first = (long)kt * BK;
+            const int grp = min((int)(first / a.gs), a.ng - 1);
+            group_ends = (first + BK) % a.gs == 0 || kt + 1 == nk;  // wave-uniform
+#pragma unroll
+            for (int n = 0; n < WN; ++n) gsc[n] = a.scales[(long)grp * a.O + min(o0 + 16 * n + li, a.O - 1)];
+            if (first % a.gs == 0) {
+#pragma unroll
+                for (int m = 0; m < WM; ++m)
+#pragma unroll
+                    for (int n = 0; n < WN; ++n) tacc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        auto &dst = *(GS ? &tacc : &acc);
         const uint16_t *Bs = lds16 + buf * C::STAGE;
 #pragma unroll
         for (int h = 0; h < KH; ++h) {
@@ -486,8 +508,18 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
                     const bf16x8 av = __builtin_bit_cast(bf16x8, cur[m][pl][h]);
 #pragma unroll
                     for (int n = 0; n < WN; ++n)
-                        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[n], acc[m][n], 0, 0, 0);
+                        dst[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[n], dst[m][n], 0, 0, 0);
                 }
+        }
+        if constexpr (GS) {
+            if (group_ends) {
+#pragma unroll
+                for (int m = 0; m < WM; ++m)
+#pragma unroll
+                    for (int n = 0; n < WN; ++n)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf(gsc[n], tacc[m][n][r], acc[m][n][r]);
+            }
         }
         __syncthreads();
     };
@@ -518,7 +550,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     for (int n = 0; n < WN; ++n) {
         const int o = o0 + 16 * n + li;
         if (o >= a.O) continue;
-        const float sc = a.scales[o];
+        const float sc = GS ? 1.0f : a.scales[o];
 #pragma unroll
         for (int m = 0; m < WM; ++m)
 #pragma unroll
@@ -549,12 +581,13 @@ hipError_t launch_f32(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int FMT, int WAVES, int WM, int WN, int BK, int PD>
+template <int FMT, int WAVES, int WM, int WN, int BK, int PD, bool GS = false>
 hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     using C = X3Cfg<WAVES, WM, WN, BK>;
     constexpr int NW = kX3WeightSets;
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile does not fit in LDS");
-    static const hipError_t lim = raise_lds_limit(&tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW>, C::LDS_BYTES);
+    static const hipError_t lim =
+        raise_lds_limit(&tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW, GS>, C::LDS_BYTES);
     if (lim != hipSuccess) return lim;
     const int vec_ok = ((a.I & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
     const long slots = (long)p.sp * p.kp / 8;  // one thread per 16-byte fragment slot
@@ -562,7 +595,7 @@ hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
                        a.I, a.nfull, vec_ok, p.sp, p.kp, (long)p.sp * p.kp, const_cast<uint16_t *>(a.xp));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES,
+    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW, GS>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES,
                        st, a);
     return hipGetLastError();
 }
@@ -578,6 +611,10 @@ constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
 template <int FMT>
 hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if constexpr (FMT != WQ_F32) {
+        if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: 64-position K steps
+            if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true>(p, a, st);
+            return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true>(p, a, st);
+        }
         if (p.mode == kTiledBF16X3) {
             if (p.bm == 128) {
                 if (p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch>(p, a, st);
@@ -592,10 +629,11 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
 
 } // namespace
 
-TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape) {
+TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) {
     TiledPlan p;
-    // the bf16 split needs exact integer codes (quantized formats); f32 weights stay fp32
-    p.mode = (fmt != WQ_F32 && mode == kTiledBF16X3) ? kTiledBF16X3 : kTiledF32;
+    // the bf16 split needs exact integer codes (quantized formats); f32 weights
+    // stay fp32; group-scaled tensors always take the bf16x3 kernel
+    p.mode = (fmt != WQ_F32 && (mode == kTiledBF16X3 || gs > 0)) ? kTiledBF16X3 : kTiledF32;
     // plane sizes are kept in int: rows near the int limit take the fp32 mode
     if ((long)S > INT_MAX - kTiledSAlign || (long)I > INT_MAX / 2 - 4 * kTiledKAlign) p.mode = kTiledF32;
     // big tiles (128 x 96, 4 x 3 fragments per wave) when there are enough of them
@@ -605,7 +643,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape) {
     if (p.mode == kTiledBF16X3) {
         sh = use_big ? kX3Shapes[0] : kX3Shapes[2];
         for (const Shape &c : kX3Shapes)
-            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk) sh = c;
+            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign)) sh = c;
     } else {
         sh = use_big ? kF32Shapes[0] : kF32Shapes[1];
         for (const Shape &c : kF32Shapes)

@@ -104,9 +104,12 @@ struct wq_tensor {
     int device, fmt, O, I;
     long rb;      // packed host row bytes
     long stride;  // device row stride (rb rounded up to kRowAlign; padding zeroed)
-    int nfull;    // permuted 1 KiB blocks per row
+    int nfull;    // permuted 1 KiB blocks per row (0 for group-scaled tensors: natural order)
+    int gs;       // group size of the scales (0: one scale per row)
+    int ng;       // scales per row (1, or ceil(I / gs))
     uint8_t *d_w;
-    float *d_scales;
+    float *d_scales;   // O x ng floats (row-major: one row's groups together)
+    float *d_scales_t; // gs > 0: the same scales group-major, ng x O (tiled path)
     size_t bytes; // device bytes held (weights + scales)
 };
 
@@ -130,6 +133,13 @@ struct GemvPlan {
     bool ok = false;
 };
 
+// Group-wise scales (gs > 0): rows are in natural element order, gs is a
+// multiple of kGroupAlign, so every lane slot (at most 64 elements) and every
+// 64-position tiled K step lies inside one group. The GEMV reads
+// scales[o * ng + g]; the tiled kernel reads a group-major copy,
+// scales[g * O + o], so one tile's rows share cache lines.
+constexpr int kGroupAlign = 64;
+
 struct GemvArgs {
     const uint8_t *w;
     const float *scales;
@@ -137,6 +147,7 @@ struct GemvArgs {
     float *y;
     long stride;
     int nfull;
+    int gs, ng;       // group-wise scales (gs == 0: one scale per row)
     int O, I, S;
     int k;             // load slots per lane per row
     int team;          // waves per team
@@ -153,7 +164,7 @@ GemvShape gemv_shape(int fmt, int smax);
 int gemv_smax_bucket(int S); // 1,2,4,8 or 0 if S > 8
 
 GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu);
-hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);
+hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);  // a.gs selects the variant
 
 // ---------------------------------------------------------------------------
 // Grouped GEMV: one launch over several tensors of one format.
@@ -203,6 +214,7 @@ struct TiledArgs {
     float *y;
     long stride;
     int nfull;
+    int gs, ng;       // group-wise scales (gs == 0: one scale per row)
     int O, I, S;
     int tiles_s, tiles_o;
     // bf16x3 mode: workspace holding the three activation planes
@@ -225,7 +237,8 @@ struct TiledPlan {
 };
 
 // shape: 0 picks by size; bm * 1000000 + bn * 1000 + bk forces a compiled tile shape
-TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape);
+// gs > 0 (group-wise scales) always takes the bf16x3 mode
+TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs = 0);
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
@@ -241,6 +254,7 @@ struct wq_group {
     std::vector<wq_tensor *> ts;
     std::vector<wq::GroupDesc> h_desc;
     wq::GroupDesc *d_desc;
+    bool has_gs = false;  // a group-scaled tensor is present: one launch per tensor
     // per S bucket (index 0..3 for 1,2,4,8): work table on the device
     struct Bucket {
         bool built = false;
