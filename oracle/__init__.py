@@ -63,6 +63,9 @@ def _load():
             ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_void_p, ctypes.c_long,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int]
+        if hasattr(lib, "oracle_silu_mul"):
+            lib.oracle_silu_mul.restype = None
+            lib.oracle_silu_mul.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
         if hasattr(lib, "oracle_matmul_gs"):
             lib.oracle_matmul_gs.restype = ctypes.c_int
             lib.oracle_matmul_gs.argtypes = [
@@ -183,3 +186,28 @@ def matmul_gs_rows(fmt: int, w: np.ndarray, scales: np.ndarray, gs: int, x: np.n
     rows = np.asarray(rows, dtype=np.int64)
     return matmul_gs(fmt, np.ascontiguousarray(np.asarray(w)[rows]),
                      np.ascontiguousarray(np.asarray(scales)[rows]), gs, x, I=I, threads=threads)
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = fl32(silu(g) * u) elementwise, computed in double (float32 in, float32 out)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    if g.shape != u.shape:
+        raise ValueError("g and u must have the same shape")
+    h = np.empty_like(g)
+    _load().oracle_silu_mul(g.ctypes.data, u.ctypes.data, g.size, h.ctypes.data)
+    return h
+
+
+def swiglu_ffn(fmt: int, gate, up, down, x: np.ndarray):
+    """One expert's feed-forward step, every stage from the oracle.
+
+    gate, up: (w, scales) of [O, I] tensors; down: (w, scales) of an [I2, O]
+    tensor; x: float32 [S, I]. Returns a dict with g, u (and their bound
+    magnitudes Ag, Au), h = silu_mul(g, u), y = down . h (and Ay).
+    """
+    g, ag = matmul(fmt, gate[0], gate[1], x)
+    u, au = matmul(fmt, up[0], up[1], x)
+    h = silu_mul(g, u)
+    y, ay = matmul(fmt, down[0], down[1], h)
+    return {"g": g, "Ag": ag, "u": u, "Au": au, "h": h, "y": y, "Ay": ay}

@@ -187,3 +187,22 @@ int oracle_matmul_gs(int fmt, long O, long I, const unsigned char *w, long row_s
     }
     return 0;
 }
+
+/*
+ * SiLU-gated product of a mixture-of-experts feed-forward step. colibri
+ * "第 8 章 · 02 CUDA/Metal/Vulkan 三后端" (learning goals and section recap)
+ * names a gated up-projection shader, qmatmul_gate_up.comp, but shows neither
+ * its body nor its activation; the reading taken is SiLU gating (SwiGLU):
+ *
+ *     h[j] = fl32( silu(g[j]) * u[j] ),   silu(z) = z / (1 + exp(-z)),
+ *
+ * evaluated in double from the float inputs (g = gate rows . x, u = up rows . x).
+ */
+void oracle_silu_mul(const float *g, const float *u, long n, float *h)
+{
+    for (long j = 0; j < n; ++j) {
+        double z = (double)g[j];
+        double silu = z / (1.0 + exp(-z));
+        h[j] = (float)(silu * (double)u[j]);
+    }
+}

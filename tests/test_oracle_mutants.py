@@ -40,6 +40,9 @@ MUTANTS = {
     "gs_scale_dropped": ("total += gscale * group_sum;", "total += group_sum;"),
     "gs_last_group_dropped": ("for (long g = 0; g < ng; ++g) {", "for (long g = 0; g + 1 < ng; ++g) {"),
     "gs_group_scale_of_next": ("double gscale = (double)srow[g];", "double gscale = (double)srow[(g + 1) % ng];"),
+    # SiLU-gated product
+    "silu_exp_sign": ("double silu = z / (1.0 + exp(-z));", "double silu = z / (1.0 + exp(z));"),
+    "silu_gate_dropped": ("double silu = z / (1.0 + exp(-z));", "double silu = z;"),
 }
 
 
@@ -56,7 +59,8 @@ def _run_mutant(name, old, new, tmp):
     env = dict(os.environ, ORACLE_LIB_UNDER_TEST=lpath, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_gs_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_gs_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_ffn_pins.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     return name, r.returncode, r.stdout[-400:]
 
