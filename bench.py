@@ -16,6 +16,11 @@ average launch duration from HIP events on the launch stream, with the MI355X
 peak; `cpu_baseline` is the CPU oracle timed on this host on a bounded sample
 of the same workload.
 
+The moe_ffn workload runs the whole gated feed-forward of 8 int4 experts per
+step (the fused gate/up launch writing h = silu(g) * u, then the grouped down
+launch); its roofline is that of the gate/up launch, timed in a graph of its
+own.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
 """
 from __future__ import annotations
@@ -45,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dense_gemv",
-                    choices=["dense_gemv", "moe_decode", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
+                    choices=["dense_gemv", "moe_decode", "moe_ffn", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
                              "dense_gemv_gs128", "prefill_gs128",
                              "prefill"])
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
@@ -91,6 +96,9 @@ def problems_for(name):
     if name == "moe_decode":
         return synth.moe_decode(), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
                                     "S=1 per expert, one grouped launch")
+    if name == "moe_ffn":
+        return synth.moe_decode(), ("moe_ffn: 8 experts x int4 {gate,up}[2048,6144] -> h = silu(g)*u -> "
+                                    "down[6144,2048], S=1 per expert, fused gate/up launch + grouped down launch")
     if name.startswith("int2_gemv_s"):
         S = int(name[len("int2_gemv_s"):])
         return [synth.int2_gemv(S=S)], "int2_gemv: int2 W[16384,8192] (codes U{0..3}), scales U[0.01,0.1], S=%d" % S
@@ -137,9 +145,19 @@ def main():
     torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
     grouped = args.workload == "moe_decode"
+    ffn = args.workload == "moe_ffn"
     weight_bytes = sum(p.weight_bytes for p in probs)
-    alg_bytes = sum(p.weight_bytes + 4 * p.O * (p.gscales.shape[1] if getattr(p, "gs", 0) else 1)
-                    + 4 * p.S * p.I + 4 * p.S * p.O for p in probs)
+
+    def io_bytes(p):  # weights, scales, activations in, results out
+        return (p.weight_bytes + 4 * p.O * (p.gscales.shape[1] if getattr(p, "gs", 0) else 1)
+                + 4 * p.S * p.I + 4 * p.S * p.O)
+
+    alg_bytes = sum(io_bytes(p) for p in probs)
+    if ffn:
+        # gate and up read one x and write one h between them; down reads h
+        gu_bytes = sum(p.weight_bytes + 4 * p.O for i, p in enumerate(probs) if i % 3 != 2) + sum(
+            4 * p.S * p.I + 4 * p.S * p.O for i, p in enumerate(probs) if i % 3 == 0)
+        alg_bytes = gu_bytes + sum(io_bytes(p) for i, p in enumerate(probs) if i % 3 == 2)
     alg_flops = sum(2.0 * p.S * p.O * p.I for p in probs)
     compute_bound = args.workload.startswith("prefill")
     n_rot = 1 if compute_bound else max(1, math.ceil(ROTATION_BYTES / weight_bytes))
@@ -152,13 +170,27 @@ def main():
     groups = [wq.wq_grouped_create(c) for c in copies] if grouped else None
     xs = [torch.from_numpy(p.x).to(dev) for p in probs]
     ys = [torch.empty((p.S, p.O), dtype=torch.float32, device=dev) for p in probs]
+    if ffn:
+        E = len(probs) // 3
+        gated = [wq.wq_swiglu_create(c[0::3], c[1::3]) for c in copies]
+        downs = [wq.wq_grouped_create(c[2::3]) for c in copies]
+        groups = gated + downs
+        fx = [xs[3 * e] for e in range(E)]
+        fh = [torch.empty((probs[3 * e].S, probs[3 * e].O), dtype=torch.float32, device=dev) for e in range(E)]
+        fy = [torch.empty((probs[3 * e].S, probs[3 * e + 2].O), dtype=torch.float32, device=dev)
+              for e in range(E)]
 
     def step(i):
         r = i % n_rot
-        if grouped:
+        if ffn:
+            wq.wq_swiglu_ffn_dev(gated[r], downs[r], fx, fh, fy)
+        elif grouped:
             wq.wq_grouped_matmul_dev(groups[r], xs, ys)
         else:
             wq.wq_matmul_dev(copies[r][0], xs[0], ys[0])
+
+    def gate_up_only(i):
+        wq.wq_swiglu_matmul_dev(gated[i % n_rot], fx, fh)
 
     stream = torch.cuda.current_stream()
     for i in range(W):
@@ -193,6 +225,25 @@ def main():
     wall = t1 - t0
     ev_s = ev0.elapsed_time(ev1) / 1e3
     per_launch = ev_s / K  # average launch duration on the launch stream (s)
+    if ffn:
+        # the step is two launches: time the dominant one (gate/up) in a graph of its own
+        g2 = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(g2, stream=side):
+            for i in range(K):
+                gate_up_only(i)
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g2.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_per_launch = per_launch
+        per_launch = e0.elapsed_time(e1) / 1e3 / K
 
     plans = [wq.wq_describe_plan(p.fmt, p.O, p.I, p.S) for p in probs]
     bf16x3 = compute_bound and all("mode=bf16x3" in pl for pl in plans)
@@ -210,13 +261,16 @@ def main():
     else:
         value = weight_bytes * K / wall / 1e9
         unit = "GB/s"
-        roof = {"bound": "hbm", "achieved": alg_bytes / per_launch / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": (gu_bytes if ffn else alg_bytes) / per_launch / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        if ffn:
+            roof["kernel"] = "fused gate/up (paired rows, silu(g)*u epilogue), all experts in one launch"
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_counters(args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(probs, compute_bound, args.cpu_seconds)
+        cpu = cpu_baseline(probs, compute_bound, args.cpu_seconds, ffn=ffn)
 
     out = {
         "metric": METRIC,
@@ -240,6 +294,8 @@ def main():
             "launch": "eager" if graph is None else "one HIP graph of K kernel launches",
             "pct_hbm_peak_weight_stream": None if compute_bound else 100.0 * value / HBM_PEAK_GBS,
             "event_us_per_launch": per_launch * 1e6,
+            **({"event_us_per_step_two_launches": step_per_launch * 1e6,
+                "algorithmic_bytes_gate_up_launch": gu_bytes} if ffn else {}),
             "plan": plans[:3],
         },
         "roofline": roof,
@@ -255,12 +311,28 @@ def main():
             wq.wq_tensor_free(t)
 
 
-def cpu_baseline(probs, compute_bound, seconds):
+def cpu_baseline(probs, compute_bound, seconds, ffn=False):
     """The CPU oracle as it stands, on this host, for about `seconds` of work."""
-    import numpy as np
-
     import oracle
     threads = oracle.default_threads()
+    if ffn:  # the oracle's gate, up, silu_mul, down chain per expert
+        E = len(probs) // 3
+        unit_work = sum(p.weight_bytes for p in probs)
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            for e in range(E):
+                gp, up, dp = probs[3 * e:3 * e + 3]
+                g, _ = oracle.matmul(gp.fmt, gp.w, gp.scales, gp.x, threads=threads, want_bound=False)
+                u, _ = oracle.matmul(up.fmt, up.w, up.scales, gp.x, threads=threads, want_bound=False)
+                h = oracle.silu_mul(g, u)
+                oracle.matmul(dp.fmt, dp.w, dp.scales, h, threads=threads, want_bound=False)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                break
+        return {"value": unit_work * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": "%d pass(es) over the 8-expert gate/up/silu/down chain, S=1, %.1f s" % (reps, el)}
     # bounded sample: whole weight matrices, at most 16 activation rows of each
     sample = []
     for p in probs:

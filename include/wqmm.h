@@ -172,7 +172,8 @@ int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, v
 int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
 
 /*
- * Run every tensor of the group: y_dev[g] = matmul(ts[g], x_dev[g], S[g]).
+ * Run every tensor of a plain group (a gated group gives WQ_E_INVAL):
+ * y_dev[g] = matmul(ts[g], x_dev[g], S[g]).
  * x_dev, S, y_dev: host arrays of G entries (device pointers inside);
  * S[g] == 0 skips tensor g. One kernel launch on hip_stream when every
  * S[g] <= the GEMV limit and every row fits the register GEMV; otherwise one
@@ -182,7 +183,50 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
 int wq_grouped_matmul_dev(wq_group *group, const float *const *x_dev, const int *S,
                           float *const *y_dev, void *hip_stream);
 
+/* Release a group (plain or gated); NULL is a no-op. */
 int wq_grouped_free(wq_group *group);
+
+/*
+ * Gated feed-forward of a mixture-of-experts layer (the fused gate/up matmul
+ * feeding the down projection: the gated up-projection shader
+ * qmatmul_gate_up.comp named in colibri "第 8 章 · 02 CUDA/Metal/Vulkan
+ * 三后端", learning goals and section recap, whose body and activation the
+ * pages do not give; SiLU gating is the reading taken). For expert e:
+ *
+ *     g = gate_e . x_e,  u = up_e . x_e      (each as wq_matmul_dev computes it)
+ *     h_e[s,o] = silu(g[s,o]) * u[s,o],      silu(z) = z / (1 + e^-z)
+ *     y_e = down_e . h_e
+ *
+ * wq_swiglu_create pairs gate[e] with up[e] (host arrays of E tensors, all on
+ * one device in one format; gate[e] and up[e] must have the same O, I and
+ * group size, else WQ_E_INVAL) into a gated group, freed with
+ * wq_grouped_free before its tensors. The group references the tensors.
+ *
+ * wq_swiglu_matmul_dev: h_dev[e] = h_e, an fp32 [S[e], O_e] device buffer,
+ * for x_dev[e] fp32 [S[e], I_e] (host arrays of E device pointers; S[e] == 0
+ * skips expert e). Stream-ordered on hip_stream. With every S[e] within the
+ * GEMV limit, one scale per row and rows that fit one wave, all experts run
+ * in one launch that reads each gate row and up row once and writes h
+ * directly (g and u never reach memory); otherwise each expert runs as its
+ * own paired launch, or (S above the GEMV limit, or group-wise scales) as
+ * gate -> h_dev[e], up -> the device workspace, then an activation kernel.
+ * The last form may grow the workspace (refused with WQ_E_UNSUPPORTED while
+ * the stream is being captured; warm up first).
+ *
+ * Accuracy: g and u meet the matmul contract; h is silu and the product
+ * evaluated in fp32 on those values (a few ulps, no further cancellation).
+ *
+ * wq_swiglu_ffn_dev: the whole layer, both launches stream-ordered on
+ * hip_stream: h_dev as above (the caller's intermediate buffers), then
+ * y_dev[e] = down_e . h_e through the plain group `down` (wq_grouped_create
+ * of the E down tensors, down[e]->I == gate[e]->O, else WQ_E_INVAL);
+ * y_dev[e] is fp32 [S[e], O_down_e].
+ */
+int wq_swiglu_create(wq_tensor *const *gate, wq_tensor *const *up, int E, wq_group **group);
+int wq_swiglu_matmul_dev(wq_group *gated, const float *const *x_dev, const int *S,
+                         float *const *h_dev, void *hip_stream);
+int wq_swiglu_ffn_dev(wq_group *gated, wq_group *down, const float *const *x_dev, const int *S,
+                      float *const *h_dev, float *const *y_dev, void *hip_stream);
 
 /* Release a resident tensor (colibri-analysis "CUDA 后端", section 1,
  * coli_cuda_tensor_free). NULL is a no-op. */

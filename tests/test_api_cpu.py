@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("wq_init", "wq_mem_info", "wq_tensor_upload", "wq_matmul", "wq_matmul_t",
                  "wq_matmul_dev", "wq_grouped_create", "wq_grouped_matmul_dev", "wq_grouped_free",
-                 "wq_tensor_free", "wq_strerror"):
+                 "wq_tensor_free", "wq_strerror", "wq_swiglu_create", "wq_swiglu_matmul_dev",
+                 "wq_swiglu_ffn_dev"):
         assert must in names
 
 
@@ -169,6 +170,9 @@ def test_validation_without_device():
     assert L.wq_grouped_matmul_dev(None, None, None, None, None) == wq.WQ_E_INVAL
     assert L.wq_tensor_free(None) == wq.WQ_OK
     assert L.wq_grouped_free(None) == wq.WQ_OK
+    assert L.wq_swiglu_create(None, None, 1, ctypes.byref(h)) == wq.WQ_E_INVAL
+    assert L.wq_swiglu_matmul_dev(None, None, None, None, None) == wq.WQ_E_INVAL
+    assert L.wq_swiglu_ffn_dev(None, None, None, None, None, None, None) == wq.WQ_E_INVAL
     assert L.wq_mem_info(-1, None, None) == wq.WQ_E_INVAL
     assert L.wq_mem_info(7, None, None) == wq.WQ_E_NOTINIT
 

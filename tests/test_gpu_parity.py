@@ -171,6 +171,39 @@ def test_grouped_mixed_S_and_skips():
             wq.wq_tensor_free(t)
 
 
+@pytest.mark.parametrize("fmt,S", [(I4, 1), (I8, 2), (I2, 1), (F32, 1)])
+def test_grouped_many_problems_mixed_row_lengths(fmt, S):
+    # 70 problems (two launch chunks) whose rows need 1..4 load slots: one
+    # launch per (chunk, slot count); skipped problems in between
+    g0 = synth.rng(77 + fmt + S)
+    Is = [int(v) for v in g0.choice([3, 100, 700, 1500, 2100, 3000, 4000, 6000], size=70)]
+    probs = []
+    for j, I in enumerate(Is):
+        p = synth.ragged(fmt, int(g0.integers(1, 90)), I, S, seed=4000 + j)
+        if j % 9 == 4:
+            p.x = None
+        probs.append(p)
+    ts = [gu.upload(p) for p in probs]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x).cuda() if p.x is not None else None for p in probs]
+        outs = [gu.guarded_output(S, p.O) for p in probs]
+        ys = [o[1] if p.x is not None else None for o, p in zip(outs, probs)]
+        gu.banner("grouped 70 problems fmt=%d S=%d" % (fmt, S))
+        wq.wq_grouped_matmul_dev(g, xs, ys)
+        torch.cuda.synchronize()
+        for p, (b, y) in zip(probs, outs):
+            gu.check_canaries(b, S if p.x is not None else 0, p.O)
+            if p.x is None:
+                continue
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, p.name)
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
 # ---------------------------------------------------------------------------------------
 # ragged shapes, both paths
 

@@ -65,6 +65,10 @@ def _bind(lib):
         "wq_grouped_create": (ci, [ctypes.POINTER(vp), ci, ctypes.POINTER(vp)]),
         "wq_grouped_matmul_dev": (ci, [vp, ctypes.POINTER(vp), _c_int_p, ctypes.POINTER(vp), vp]),
         "wq_grouped_free": (ci, [vp]),
+        "wq_swiglu_create": (ci, [ctypes.POINTER(vp), ctypes.POINTER(vp), ci, ctypes.POINTER(vp)]),
+        "wq_swiglu_matmul_dev": (ci, [vp, ctypes.POINTER(vp), _c_int_p, ctypes.POINTER(vp), vp]),
+        "wq_swiglu_ffn_dev": (ci, [vp, vp, ctypes.POINTER(vp), _c_int_p, ctypes.POINTER(vp),
+                                   ctypes.POINTER(vp), vp]),
         "wq_tensor_free": (ci, [vp]),
         "wq_strerror": (ctypes.c_char_p, [ci]),
         "wq_describe_plan": (ci, [ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t]),
@@ -129,10 +133,11 @@ class Tensor:
 
 
 class Group:
-    """Handle of a tensor group (the C wq_group*)."""
+    """Handle of a tensor group (the C wq_group*); `ups` is set for a gated group."""
 
-    def __init__(self, ptr: ctypes.c_void_p, tensors):
+    def __init__(self, ptr: ctypes.c_void_p, tensors, ups=None):
         self.ptr, self.tensors = ptr, list(tensors)
+        self.ups = None if ups is None else list(ups)
 
 
 # ----------------------------------------------------------------------------
@@ -263,6 +268,59 @@ def wq_grouped_matmul_dev(g: Group, xs, ys, stream=None) -> None:
         Ss[i] = S
     dev = g.tensors[0].device
     _check(lib.wq_grouped_matmul_dev(g.ptr, xp, Ss, yp, _stream_handle(stream, dev)), "wq_grouped_matmul_dev")
+
+
+def _per_problem(tensors, xs, outs, out_cols, what):
+    G = len(tensors)
+    if len(xs) != G or len(outs) != G:
+        raise ValueError("need one x and one %s per problem" % what)
+    xp = (ctypes.c_void_p * G)()
+    op = (ctypes.c_void_p * G)()
+    Ss = (ctypes.c_int * G)()
+    for i, (t, x, o) in enumerate(zip(tensors, xs, outs)):
+        if x is None:
+            Ss[i] = 0
+            continue
+        S = x.shape[0]
+        xp[i] = _dev_f32(x, (S, t.I), t.device, "xs[%d]" % i).value
+        op[i] = _dev_f32(o, (S, out_cols[i]), t.device, "%s[%d]" % (what, i)).value
+        Ss[i] = S
+    return xp, Ss, op
+
+
+def wq_swiglu_create(gates, ups) -> Group:
+    """Gated group: expert e pairs gates[e] with ups[e] (same shape)."""
+    gs, us = list(gates), list(ups)
+    if len(gs) != len(us):
+        raise ValueError("need one up tensor per gate tensor")
+    ga = (ctypes.c_void_p * len(gs))(*[t.ptr.value for t in gs])
+    ua = (ctypes.c_void_p * len(us))(*[t.ptr.value for t in us])
+    h = ctypes.c_void_p(None)
+    _check(lib.wq_swiglu_create(ga, ua, len(gs), ctypes.byref(h)), "wq_swiglu_create")
+    return Group(h, gs, us)
+
+
+def wq_swiglu_matmul_dev(g: Group, xs, hs, stream=None) -> None:
+    """hs[e][S_e, O_e] = silu(gate_e . xs[e]) * (up_e . xs[e]); xs[e] None skips expert e."""
+    xp, Ss, hp = _per_problem(g.tensors, xs, hs, [t.O for t in g.tensors], "hs")
+    dev = g.tensors[0].device
+    _check(lib.wq_swiglu_matmul_dev(g.ptr, xp, Ss, hp, _stream_handle(stream, dev)), "wq_swiglu_matmul_dev")
+
+
+def wq_swiglu_ffn_dev(g: Group, down: Group, xs, hs, ys, stream=None) -> None:
+    """Both halves of the gated feed-forward: hs as wq_swiglu_matmul_dev, then ys[e] = down_e . hs[e]."""
+    xp, Ss, hp = _per_problem(g.tensors, xs, hs, [t.O for t in g.tensors], "hs")
+    if len(ys) != len(down.tensors):
+        raise ValueError("need one y per expert")
+    E = len(g.tensors)
+    yp = (ctypes.c_void_p * E)()
+    for i in range(E):
+        if Ss[i] > 0:
+            t = down.tensors[i]
+            yp[i] = _dev_f32(ys[i], (Ss[i], t.O), t.device, "ys[%d]" % i).value
+    dev = g.tensors[0].device
+    _check(lib.wq_swiglu_ffn_dev(g.ptr, down.ptr, xp, Ss, hp, yp, _stream_handle(stream, dev)),
+           "wq_swiglu_ffn_dev")
 
 
 def wq_grouped_free(g: Group) -> None:

@@ -30,6 +30,13 @@
 //    fixed order, so results are deterministic. Row scales are read with
 //    scalar loads (the row index is wave-uniform), which do not wait on the
 //    weight stream.
+//  * Paired rows (gated feed-forward): the ring walks virtual rows 2o and
+//    2o + 1, gate row o and up row o of two tensors of one shape, so both
+//    dot products of an output meet the same staged activations and end in
+//    the same epilogue, which writes h = silu(g) * u instead of g and u
+//    (SiLU gating: the reading taken for the gated up-projection shader that
+//    colibri "第 8 章 · 02 CUDA/Metal/Vulkan 三后端" names in its learning
+//    goals and section recap without giving its activation).
 #include "wq_internal.h"
 
 namespace wq {
@@ -123,6 +130,10 @@ __device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], fl
     }
 }
 
+// silu(g) * u with silu(z) = z / (1 + e^-z), in fp32 (expf from the device
+// math library; a very negative g gives -0 * u).
+__device__ __forceinline__ float gated(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp_move(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
@@ -144,12 +155,17 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
 // team > 1 (then the block is exactly one team).
 // GS: group-wise scales (rows in natural order; scales[row * ng + i / gs]);
 // each lane slot lies in one group, so a slot's partial sum is scaled once.
-template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool XL = false, bool GS = false>
+// PAIR: O counts virtual rows (twice the output rows); virtual row 2o is row
+// o of (w, scales), 2o + 1 row o of (w2, scales2); y is S x O/2 and receives
+// gated(g, u). D is even, row_begin and rpt are multiples of D.
+template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool XL = false, bool GS = false, bool PAIR = false>
 __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long stride, int nfull,
                                           const float *__restrict__ scales, const float *__restrict__ x,
                                           float *__restrict__ y, int O, int I, int S, int team, int tl,
                                           int wave_in_team, int row_begin, int rpt, float *red, int gs = 0,
-                                          int ng = 1) {
+                                          int ng = 1, const uint8_t *__restrict__ w2 = nullptr,
+                                          const float *__restrict__ scales2 = nullptr) {
+    static_assert(!PAIR || D % 2 == 0, "paired rows need an even ring depth");
     // KMAX is the exact number of load slots per lane: every slot is loaded
     // unconditionally (a slot past the row re-reads the row start, see
     // below), which keeps the compiler's memory wait counts exact.
@@ -254,12 +270,16 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
     for (int k = 0; k < KMAX; ++k) grp[k] = GS ? min(xb[k] / max(gs, 1), ng - 1) : 0;
     auto load_row = [&](uint32_t (&b)[KMAX][WPC], float (&gv)[KMAX], int row) {
         const long r = min(row, row_last);
-        const uint8_t *p = w + r * stride;  // wave-uniform
+        // wave-uniform tensor, row and scale pointer
+        const long rr = PAIR ? (r >> 1) : r;
+        const uint8_t *wb = (PAIR && (r & 1)) ? w2 : w;
+        const float *sb = (PAIR && (r & 1)) ? scales2 : scales;
+        const uint8_t *p = wb + rr * stride;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) load_w<LW>(p + cb[k], b[k]);
         if constexpr (GS) {
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) gv[k] = scales[r * ng + grp[k]];
+            for (int k = 0; k < KMAX; ++k) gv[k] = sb[rr * ng + grp[k]];
         }
     };
 #pragma unroll
@@ -351,7 +371,61 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 
     // Finish D rows starting at row0: part[d][s] holds this wave's totals.
     int pb = 0;
+    const int Oy = PAIR ? O / 2 : O;  // output rows (row stride of y)
     auto finish = [&](int row0, float (&part)[D][SMAX], int nvalid) {
+        if constexpr (PAIR) {
+            if (team == 1) {
+#pragma unroll
+                for (int d = 0; d < D; d += 2) {
+                    if (d < nvalid) {
+                        const int o = (row0 + d) >> 1;
+                        const int oc = min(o, Oy - 1);
+                        const float sg = GS ? 1.0f : scales[oc];  // wave-uniform: scalar loads
+                        const float su = GS ? 1.0f : scales2[oc];
+                        if (lane == 63 && row0 + d <= row_last) {
+#pragma unroll
+                            for (int s = 0; s < SMAX; ++s)
+                                if (s < S) y[(long)s * Oy + o] = gated(sg * part[d][s], su * part[d + 1][s]);
+                        }
+                    }
+                }
+            } else {
+                float *rbuf = red + pb * (kMaxTeam * D * SMAX);
+                if (lane == 63) {
+#pragma unroll
+                    for (int d = 0; d < D; ++d)
+#pragma unroll
+                        for (int s = 0; s < SMAX; ++s) rbuf[(wave_in_team * D + d) * SMAX + s] = part[d][s];
+                }
+                float sg[D / 2], su[D / 2];
+#pragma unroll
+                for (int j = 0; j < D / 2; ++j) {
+                    const int oc = min((row0 >> 1) + j, Oy - 1);
+                    sg[j] = GS ? 1.0f : scales[oc];
+                    su[j] = GS ? 1.0f : scales2[oc];
+                }
+                __syncthreads();
+                if (wave_in_team == 0 && lane < (D / 2) * SMAX) {
+                    const int j = lane / SMAX, s = lane % SMAX;
+                    const int d = 2 * j;
+                    float tg = 0.0f, tu = 0.0f;
+                    for (int w2i = 0; w2i < team; ++w2i) {
+                        tg += rbuf[(w2i * D + d) * SMAX + s];
+                        tu += rbuf[(w2i * D + d + 1) * SMAX + s];
+                    }
+                    float g = sg[0], u = su[0];
+#pragma unroll
+                    for (int jj = 1; jj < D / 2; ++jj) {
+                        g = (j == jj) ? sg[jj] : g;
+                        u = (j == jj) ? su[jj] : u;
+                    }
+                    if (d < nvalid && row0 + d <= row_last && s < S)
+                        y[(long)s * Oy + ((row0 + d) >> 1)] = gated(g * tg, u * tu);
+                }
+                pb ^= 1;
+            }
+            return;
+        }
         if (team == 1) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
@@ -420,7 +494,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 // XL: the block first copies the S x I activations into LDS (one coalesced
 // pass per block instead of one per wave) and the waves stage their
 // registers from there; used when x fits (host check) and XV holds.
-template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool XL, bool GS = false>
+template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool XL, bool GS = false, bool PAIR = false>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     __shared__ float red[2 * kMaxTeam * D * SMAX];
     extern __shared__ __attribute__((aligned(16))) float xl[];
@@ -440,36 +514,32 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
         xsrc = xl;
     }
     if (row_begin >= a.O) return;  // uniform over the team (and the block when team > 1)
-    team_rows<FMT, SMAX, LW, KS, D, XV, XL, GS>(a.w, a.stride, a.nfull, a.scales, xsrc, a.y, a.O, a.I, a.S,
-                                                a.team, wave_in_team * 64 + lane, wave_in_team, row_begin,
-                                                a.rows_per_team, red, a.gs, a.ng);
+    team_rows<FMT, SMAX, LW, KS, D, XV, XL, GS, PAIR>(a.w, a.stride, a.nfull, a.scales, xsrc, a.y, a.O, a.I,
+                                                      a.S, a.team, wave_in_team * 64 + lane, wave_in_team,
+                                                      row_begin, a.rows_per_team, red, a.gs, a.ng, a.w2,
+                                                      a.scales2);
 }
 
-template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV>
+// PAIR: every problem is a (gate, up) pair; its work items count virtual rows.
+// KS: the slot count every item of the launch has (the runtime launches each
+// slot count on its own), so the kernel's registers are those of its rows.
+template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool PAIR, int KS>
 __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int item_id = blockIdx.x * 4 + wave;
     if (item_id >= a.n_items) return;
     const WorkItem it = a.items[item_id];
+    if (__builtin_amdgcn_readfirstlane(it.k) != KS) return;  // a table built for another slot count
     const int p = __builtin_amdgcn_readfirstlane(it.p);
     const int S = a.S[p];
     if (S <= 0) return;
     const GroupDesc d = a.desc[p];
     const int r0 = __builtin_amdgcn_readfirstlane(it.row_begin);
     const int nr = __builtin_amdgcn_readfirstlane(it.row_end - it.row_begin);
-    // exact slot count of this problem's rows (wave-uniform)
-    switch (__builtin_amdgcn_readfirstlane(it.k)) {
-#define WQ_GROUP_K(KS)                                                                                        \
-    case KS:                                                                                                  \
-        if constexpr (KS <= KMAX)                                                                             \
-            team_rows<FMT, SMAX, LW, KS, D, XV>(d.w, d.stride, d.nfull, d.scales, a.x[p], a.y[p], d.O, d.I, S, 1, \
-                                                lane, 0, r0, nr, nullptr);                                    \
-        break;
-        WQ_GROUP_K(1) WQ_GROUP_K(2) WQ_GROUP_K(3) WQ_GROUP_K(4)
-#undef WQ_GROUP_K
-    default: break;
-    }
+    team_rows<FMT, SMAX, LW, KS, ring_depth(KMAX, D, KS), XV, false, false, PAIR>(
+        d.w, d.stride, d.nfull, d.scales, a.x[p], a.y[p], PAIR ? 2 * d.O : d.O, d.I, S, 1, lane, 0, r0, nr, nullptr,
+        0, 1, d.w2, d.scales2);
 }
 
 // ---- compiled shapes -------------------------------------------------------
@@ -494,7 +564,22 @@ __global__ void relayout_kernel(const uint8_t *__restrict__ src, uint8_t *__rest
     }
 }
 
+// h[j] = gated(h[j], u[j]): the activation step of the gated feed-forward
+// when gate and up ran as separate matmuls (h holds g on entry).
+__global__ void gated_inplace_kernel(float *__restrict__ h, const float *__restrict__ u, long n) {
+    for (long j = blockIdx.x * (long)blockDim.x + threadIdx.x; j < n; j += (long)gridDim.x * blockDim.x)
+        h[j] = gated(h[j], u[j]);
+}
+
 } // namespace
+
+hipError_t launch_gated_inplace(float *h, const float *u, long n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int block = 256;
+    const int grid = (int)std::min<long>((n + block - 1) / block, 4096);
+    hipLaunchKernelGGL(gated_inplace_kernel, dim3(grid), dim3(block), 0, st, h, u, n);
+    return hipGetLastError();
+}
 
 int gemv_smax_bucket(int S) {
     if (S <= 1) return 1;
@@ -521,13 +606,13 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu) {
     if (sh.lw == 0) return p;
     p.lw = sh.lw;
     p.kmax = sh.kmax;
-    p.d = sh.d;
     const long stride = round_up(row_bytes(fmt, I), kRowAlign);
     const long per_wave = 64L * sh.lw * sh.kmax;
     const long team = (stride + per_wave - 1) / per_wave;
     if (team > kMaxTeam) return p;  // row too long for the register GEMV
     p.team = (int)team;
     p.k = (int)((stride + 64L * p.lw * p.team - 1) / (64L * p.lw * p.team));
+    p.d = ring_depth(sh.kmax, sh.d, p.k);
     p.teams_per_block = (p.team == 1) ? 4 : 1;
     p.block = 64 * p.team * p.teams_per_block;
     // teams: enough waves to keep HBM busy, rows per team a multiple of the ring depth
@@ -550,24 +635,37 @@ hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStrea
 #define WQ_K(KS)                                                                                          \
     if constexpr (KS <= KM) {                                                                             \
         if (p.k == KS) {                                                                                  \
+            if (a.w2 != nullptr) {                                                                        \
+                if (a.gs > 0) return hipErrorInvalidValue;                                                \
+                if (xl)                                                                                   \
+                    hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, true, false, true>), dim3(p.grid), \
+                                       dim3(p.block), xbytes, st, a);                                     \
+                else if (xv)                                                                              \
+                    hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, false, false, true>), dim3(p.grid), \
+                                       dim3(p.block), 0, st, a);                                          \
+                else                                                                                      \
+                    hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, false, false, true>),        \
+                                       dim3(p.grid), dim3(p.block), 0, st, a);                            \
+                return hipGetLastError();                                                                 \
+            }                                                                                             \
             if constexpr (F != WQ_F32) {                                                                  \
                 if (a.gs > 0) {                                                                           \
                     if (xl)                                                                               \
-                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, true, true, true>), dim3(p.grid), \
+                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, true, true>), dim3(p.grid), \
                                            dim3(p.block), xbytes, st, a);                                 \
                     else                                                                                  \
-                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, false, false, true>), dim3(p.grid), \
+                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, false, true>), dim3(p.grid), \
                                            dim3(p.block), 0, st, a);                                      \
                     return hipGetLastError();                                                             \
                 }                                                                                         \
             }                                                                                             \
             if (xl)                                                                                       \
-                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, true, true>), dim3(p.grid), dim3(p.block), \
+                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, true>), dim3(p.grid), dim3(p.block), \
                                    xbytes, st, a);                                                        \
             else if (xv)                                                                                  \
-                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, true, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
+                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
             else                                                                                          \
-                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, D, false, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
+                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
             return hipGetLastError();                                                                     \
         }                                                                                                 \
     }
@@ -585,17 +683,36 @@ hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, hipStream_t st) {
-#define WQ_GLAUNCH_CASE(F, SM, LW, KM, D)                                                                 \
-    if (fmt == F && p.smax == SM) {                                                                       \
-        if (xv)                                                                                           \
-            hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, true>), dim3(p.grid), dim3(p.block), 0,  \
-                               st, a);                                                                    \
-        else                                                                                              \
-            hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, false>), dim3(p.grid), dim3(p.block), 0, \
-                               st, a);                                                                    \
-        return hipGetLastError();                                                                         \
+template <int F, int SM, int LW, int KM, int D>
+hipError_t launch_grouped_k(const GroupedPlan &p, const GroupedArgs &a, bool xv, bool pair, int ks,
+                            hipStream_t st) {
+#define WQ_GK(KU)                                                                                         \
+    if constexpr (KU <= KM) {                                                                             \
+        if (ks == KU) {                                                                                   \
+            if (pair && xv)                                                                               \
+                hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, true, true, KU>), dim3(p.grid),      \
+                                   dim3(p.block), 0, st, a);                                              \
+            else if (pair)                                                                                \
+                hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, false, true, KU>), dim3(p.grid),     \
+                                   dim3(p.block), 0, st, a);                                              \
+            else if (xv)                                                                                  \
+                hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, true, false, KU>), dim3(p.grid),     \
+                                   dim3(p.block), 0, st, a);                                              \
+            else                                                                                          \
+                hipLaunchKernelGGL((grouped_kernel<F, SM, LW, KM, D, false, false, KU>), dim3(p.grid),    \
+                                   dim3(p.block), 0, st, a);                                              \
+            return hipGetLastError();                                                                     \
+        }                                                                                                 \
     }
+    WQ_GK(1) WQ_GK(2) WQ_GK(3) WQ_GK(4)
+#undef WQ_GK
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, bool pair, int ks,
+                          hipStream_t st) {
+#define WQ_GLAUNCH_CASE(F, SM, LW, KM, D) \
+    if (fmt == F && p.smax == SM) return launch_grouped_k<F, SM, LW, KM, D>(p, a, xv, pair, ks, st);
     WQ_SHAPES(WQ_GLAUNCH_CASE)
 #undef WQ_GLAUNCH_CASE
     return hipErrorInvalidValue;

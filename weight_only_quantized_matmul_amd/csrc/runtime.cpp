@@ -498,13 +498,27 @@ int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, v
     return run_matmul(t, x_dev, S, y_dev, (hipStream_t)hip_stream);
 }
 
-int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
+} // extern "C"
+
+namespace {
+
+// A group of G problems; ts2 != nullptr makes it a paired group (problem i is
+// gate ts[i] with up ts2[i], same shape), whose work items count virtual rows.
+int create_group(wq_tensor *const *ts, wq_tensor *const *ts2, int G, wq_group **group) {
     if (ts == nullptr || group == nullptr || G <= 0) return WQ_E_INVAL;
     for (int i = 0; i < G; ++i)
-        if (!tensor_ok(ts[i])) return WQ_E_INVAL;
+        if (!tensor_ok(ts[i]) || (ts2 && !tensor_ok(ts2[i]))) return WQ_E_INVAL;
     const int dev = ts[0]->device, fmt = ts[0]->fmt;
     for (int i = 1; i < G; ++i)
         if (ts[i]->device != dev || ts[i]->fmt != fmt) return WQ_E_INVAL;
+    if (ts2) {
+        for (int i = 0; i < G; ++i) {
+            const wq_tensor *a = ts[i], *b = ts2[i];
+            if (b->device != dev || b->fmt != fmt || b->O != a->O || b->I != a->I || b->gs != a->gs ||
+                b->stride != a->stride || b->nfull != a->nfull)
+                return WQ_E_INVAL;
+        }
+    }
     if (!device_open(dev)) return WQ_E_NOTINIT;
     DeviceCtx &d = g_dev[dev];
     std::lock_guard<std::recursive_mutex> lk(d.mu);
@@ -517,18 +531,22 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
     g->fmt = fmt;
     g->G = G;
     g->ts.assign(ts, ts + G);
+    if (ts2) g->ts2.assign(ts2, ts2 + G);
     g->d_desc = nullptr;
+    const int vrows = ts2 ? 2 : 1;  // virtual rows per output row
     for (int i = 0; i < G; ++i) {
         wq::GroupDesc gd;
         gd.w = ts[i]->d_w;
         gd.scales = ts[i]->d_scales;
+        gd.w2 = ts2 ? ts2[i]->d_w : nullptr;
+        gd.scales2 = ts2 ? ts2[i]->d_scales : nullptr;
         gd.stride = ts[i]->stride;
         gd.nfull = ts[i]->nfull;
         gd.O = ts[i]->O;
         gd.I = ts[i]->I;
         gd.pad = 0;
         g->h_desc.push_back(gd);
-        if (ts[i]->gs > 0) g->has_gs = true;
+        if (ts[i]->gs > 0 || (ts2 && ts2[i]->gs > 0)) g->has_gs = true;
     }
     auto fail = [&](int rc) {
         for (auto &b : g->buckets)
@@ -558,30 +576,53 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
         bool fits = true;
         for (const auto &gd : g->h_desc) {
             if (gd.stride > per_wave) fits = false;
-            total += (long)gd.O * gd.stride;
+            total += (long)vrows * gd.O * gd.stride;
         }
         if (!fits) continue;
+        // One launch per (chunk of <= kGroupMaxPerLaunch problems, slot count
+        // k): each launch runs the kernel compiled for exactly its k, whose
+        // register count (and so occupancy) is that of its own rows, and
+        // splits its own bytes over about waves_per_cu waves per CU.
         const long target_items = std::max(1L, (long)d.cus * g_cfg.waves_per_cu);
-        const long bytes_per_item = std::max(1L, (total + target_items - 1) / target_items);
         std::vector<wq::WorkItem> items;
         for (int c0 = 0; c0 < G; c0 += wq::kGroupMaxPerLaunch) {
-            bk.first_item.push_back((int)items.size());
             const int c1 = std::min(G, c0 + wq::kGroupMaxPerLaunch);
-            for (int p = c0; p < c1; ++p) {
-                const auto &gd = g->h_desc[p];
-                long rows = (bytes_per_item + gd.stride - 1) / gd.stride;
-                rows = std::max<long>(sh.d, (rows + sh.d - 1) / sh.d * sh.d);
-                const int k = (int)((gd.stride + 64L * sh.lw - 1) / (64L * sh.lw));
-                for (long r0 = 0; r0 < gd.O; r0 += rows) {
-                    wq::WorkItem it;
-                    it.p = p - c0;
-                    it.row_begin = (int)r0;
-                    it.row_end = (int)std::min<long>(gd.O, r0 + rows);
-                    it.k = k;
-                    items.push_back(it);
+            for (int k = 1; k <= sh.kmax; ++k) {
+                auto slots = [&](const wq::GroupDesc &gd) {
+                    return (int)((gd.stride + 64L * sh.lw - 1) / (64L * sh.lw));
+                };
+                long seg_bytes = 0;
+                uint64_t mask = 0;
+                for (int p = c0; p < c1; ++p)
+                    if (slots(g->h_desc[p]) == k) {
+                        seg_bytes += (long)vrows * g->h_desc[p].O * g->h_desc[p].stride;
+                        mask |= 1ull << (p - c0);
+                    }
+                if (mask == 0) continue;
+                const long bytes_per_item = std::max(1L, (seg_bytes + target_items - 1) / target_items);
+                const int dk = wq::ring_depth(sh.kmax, sh.d, k);  // the kernel's ring depth for k slots
+                const int first = (int)items.size();
+                for (int p = c0; p < c1; ++p) {
+                    const auto &gd = g->h_desc[p];
+                    if (slots(gd) != k) continue;
+                    long rows = (bytes_per_item + gd.stride - 1) / gd.stride;
+                    rows = std::max<long>(dk, (rows + dk - 1) / dk * dk);
+                    const long nrows = (long)vrows * gd.O;
+                    for (long r0 = 0; r0 < nrows; r0 += rows) {
+                        wq::WorkItem it;
+                        it.p = p - c0;
+                        it.row_begin = (int)r0;
+                        it.row_end = (int)std::min<long>(nrows, r0 + rows);
+                        it.k = k;
+                        items.push_back(it);
+                    }
                 }
+                bk.seg_chunk.push_back(c0 / wq::kGroupMaxPerLaunch);
+                bk.first_item.push_back(first);
+                bk.n_items.push_back((int)items.size() - first);
+                bk.ks.push_back(k);
+                bk.mask.push_back(mask);
             }
-            bk.n_items.push_back((int)items.size() - bk.first_item.back());
         }
         bk.plan.n_items = (int)items.size();
         rc = dev_alloc(d, (void **)&bk.d_items, items.size() * sizeof(wq::WorkItem));
@@ -600,17 +641,58 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
     return WQ_OK;
 }
 
-int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, float *const *y_dev,
-                          void *hip_stream) {
-    if (g == nullptr || g->magic != wq::kGroupMagic) return WQ_E_INVAL;
-    if (x_dev == nullptr || S == nullptr || y_dev == nullptr) return WQ_E_INVAL;
+// One expert's gated front half: h[S, O] = silu(gate . x) * (up . x).
+// S within the GEMV limit and one scale per row: one paired-row launch.
+// Otherwise gate -> h and up -> u (in the device workspace, after the tiled
+// planes) as two ordinary matmuls, then the in-place activation kernel.
+int run_swiglu(const wq_tensor *gt, const wq_tensor *ut, const float *x, int S, float *h, hipStream_t st) {
+    DeviceCtx &d = g_dev[gt->device];
+    wq::GemvPlan gp;
+    if (gt->gs == 0 && choose_path(gt->fmt, 2 * gt->O, gt->I, S, d.cus, &gp) == 1) {
+        wq::GemvArgs a;
+        a.w = gt->d_w;
+        a.scales = gt->d_scales;
+        a.w2 = ut->d_w;
+        a.scales2 = ut->d_scales;
+        a.x = x;
+        a.y = h;
+        a.stride = gt->stride;
+        a.nfull = gt->nfull;
+        a.gs = 0;
+        a.ng = 1;
+        a.O = 2 * gt->O;
+        a.I = gt->I;
+        a.S = S;
+        a.k = gp.k;
+        a.team = gp.team;
+        a.teams_per_block = gp.teams_per_block;
+        a.rows_per_team = gp.rows_per_team;
+        return hip_status(wq::launch_gemv(gp, a, st));
+    }
+    size_t planes = 0;
+    if (choose_path(gt->fmt, gt->O, gt->I, S, d.cus, &gp) == 2)
+        planes = wq::plan_tiled(gt->fmt, gt->O, gt->I, S, g_cfg.tiled_mode, g_cfg.tiled_shape, gt->gs).ws_bytes;
+    const size_t off = (size_t)wq::round_up((long)planes, 256);
+    uint16_t *ws = nullptr;
+    int rc = ensure_workspace(d, off + (size_t)S * gt->O * sizeof(float), st, &ws);
+    if (rc != WQ_OK) return rc;
+    float *u = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + off);
+    rc = run_matmul(gt, x, S, h, st);
+    if (rc == WQ_OK) rc = run_matmul(ut, x, S, u, st);
+    if (rc == WQ_OK) rc = hip_status(wq::launch_gated_inplace(h, u, (long)S * gt->O, st));
+    return rc;
+}
+
+// Shared by the plain and the paired group calls (checked by the callers).
+int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const *y_dev, hipStream_t st) {
+    const bool pair = !g->ts2.empty();
     int smax = 0;
     for (int i = 0; i < g->G; ++i) {
         if (S[i] < 0) return WQ_E_INVAL;
         if (S[i] > 0) {
             if (x_dev[i] == nullptr || y_dev[i] == nullptr) return WQ_E_INVAL;
             if (((uintptr_t)x_dev[i] & 3) || ((uintptr_t)y_dev[i] & 3)) return WQ_E_INVAL;
-            if (!tensor_ok(g->ts[i])) return WQ_E_INVAL;
+            if (!tensor_ok(g->ts[i]) || (pair && !tensor_ok(g->ts2[i]))) return WQ_E_INVAL;
         }
         smax = std::max(smax, S[i]);
     }
@@ -618,7 +700,6 @@ int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, 
     if (!device_open(g->device)) return WQ_E_NOTINIT;
     if (g_cfg.fault == 2) return WQ_E_FAULT;
     DeviceGuard guard(g->device);
-    hipStream_t st = (hipStream_t)hip_stream;
     const int bucket = wq::gemv_smax_bucket(smax);
     const int bi = bucket == 1 ? 0 : bucket == 2 ? 1 : bucket == 4 ? 2 : bucket == 8 ? 3 : -1;
     const bool one_launch = !g->has_gs && g_cfg.force_path != 2 && smax <= gemv_limit(g->fmt) && bi >= 0 &&
@@ -626,14 +707,15 @@ int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, 
     if (!one_launch) {
         for (int i = 0; i < g->G; ++i) {
             if (S[i] == 0) continue;
-            int rc = run_matmul(g->ts[i], x_dev[i], S[i], y_dev[i], st);
+            int rc = pair ? run_swiglu(g->ts[i], g->ts2[i], x_dev[i], S[i], y_dev[i], st)
+                          : run_matmul(g->ts[i], x_dev[i], S[i], y_dev[i], st);
             if (rc != WQ_OK) return rc;
         }
         return WQ_OK;
     }
     const auto &bk = g->buckets[bi];
-    for (size_t c = 0; c < bk.first_item.size(); ++c) {
-        const int c0 = (int)c * wq::kGroupMaxPerLaunch;
+    for (size_t c = 0; c < bk.first_item.size(); ++c) {  // one launch per segment
+        const int c0 = bk.seg_chunk[c] * wq::kGroupMaxPerLaunch;
         const int c1 = std::min(g->G, c0 + wq::kGroupMaxPerLaunch);
         bool any = false;
         wq::GroupedArgs a;
@@ -645,7 +727,7 @@ int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, 
             a.x[p - c0] = x_dev[p];
             a.y[p - c0] = y_dev[p];
             a.S[p - c0] = S[p];
-            any = any || S[p] > 0;
+            if ((bk.mask[c] >> (p - c0)) & 1) any = any || S[p] > 0;
         }
         if (!any || a.n_items == 0) continue;
         bool xv = true;
@@ -654,10 +736,52 @@ int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, 
         wq::GroupedPlan gp = bk.plan;
         gp.grid = (a.n_items + 3) / 4;
         gp.block = 256;
-        int rc = hip_status(wq::launch_grouped(g->fmt, gp, a, xv, st));
+        int rc = hip_status(wq::launch_grouped(g->fmt, gp, a, xv, pair, bk.ks[c], st));
         if (rc != WQ_OK) return rc;
     }
     return WQ_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group) {
+    return create_group(ts, nullptr, G, group);
+}
+
+int wq_swiglu_create(wq_tensor *const *gate, wq_tensor *const *up, int E, wq_group **group) {
+    if (up == nullptr) return WQ_E_INVAL;
+    return create_group(gate, up, E, group);
+}
+
+int wq_swiglu_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, float *const *h_dev,
+                         void *hip_stream) {
+    if (g == nullptr || g->magic != wq::kGroupMagic || g->ts2.empty()) return WQ_E_INVAL;
+    if (x_dev == nullptr || S == nullptr || h_dev == nullptr) return WQ_E_INVAL;
+    return run_group(g, x_dev, S, h_dev, (hipStream_t)hip_stream);
+}
+
+int wq_swiglu_ffn_dev(wq_group *gu, wq_group *down, const float *const *x_dev, const int *S,
+                      float *const *h_dev, float *const *y_dev, void *hip_stream) {
+    if (gu == nullptr || gu->magic != wq::kGroupMagic || gu->ts2.empty()) return WQ_E_INVAL;
+    if (down == nullptr || down->magic != wq::kGroupMagic || !down->ts2.empty()) return WQ_E_INVAL;
+    if (x_dev == nullptr || S == nullptr || h_dev == nullptr || y_dev == nullptr) return WQ_E_INVAL;
+    if (down->G != gu->G || down->device != gu->device) return WQ_E_INVAL;
+    for (int e = 0; e < gu->G; ++e)
+        if (!tensor_ok(down->ts[e]) || !tensor_ok(gu->ts[e]) || down->ts[e]->I != gu->ts[e]->O)
+            return WQ_E_INVAL;
+    hipStream_t st = (hipStream_t)hip_stream;
+    int rc = run_group(gu, x_dev, S, h_dev, st);
+    if (rc != WQ_OK) return rc;
+    return run_group(down, h_dev, S, y_dev, st);
+}
+
+int wq_grouped_matmul_dev(wq_group *g, const float *const *x_dev, const int *S, float *const *y_dev,
+                          void *hip_stream) {
+    if (g == nullptr || g->magic != wq::kGroupMagic || !g->ts2.empty()) return WQ_E_INVAL;
+    if (x_dev == nullptr || S == nullptr || y_dev == nullptr) return WQ_E_INVAL;
+    return run_group(g, x_dev, S, y_dev, (hipStream_t)hip_stream);
 }
 
 int wq_grouped_free(wq_group *g) {

@@ -153,6 +153,10 @@ struct GemvArgs {
     int team;          // waves per team
     int teams_per_block;
     int rows_per_team;
+    // paired rows (gated feed-forward): up rows and scales; O then counts
+    // virtual rows (2 x output rows) and y receives silu(g) * u, S x O/2
+    const uint8_t *w2 = nullptr;
+    const float *scales2 = nullptr;
 };
 
 // Kernel shape for (fmt, S bucket): bytes per lane load, compiled slot count
@@ -161,10 +165,21 @@ struct GemvShape {
     int lw, kmax, d;
 };
 GemvShape gemv_shape(int fmt, int smax);
+
+// Rows in flight per wave for a row that needs ks of the kmax load slots a
+// shape compiles: a shorter row's ring reuses the registers of the unused
+// slots for more rows (d * kmax / ks rounded down to 1x, 2x or 4x), so each
+// wave keeps about the same number of bytes in flight.
+__host__ __device__ constexpr int ring_depth(int kmax, int d, int ks) {
+    return d * (kmax >= 4 * ks ? 4 : kmax >= 2 * ks ? 2 : 1);
+}
 int gemv_smax_bucket(int S); // 1,2,4,8 or 0 if S > 8
 
 GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu);
-hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);  // a.gs selects the variant
+hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);  // a.gs, a.w2 select the variant
+
+// h[j] = silu(h[j]) * u[j], j < n (gated feed-forward after separate gate and up matmuls)
+hipError_t launch_gated_inplace(float *h, const float *u, long n, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Grouped GEMV: one launch over several tensors of one format.
@@ -172,15 +187,17 @@ hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);  /
 struct GroupDesc {
     const uint8_t *w;
     const float *scales;
+    const uint8_t *w2;      // paired groups: the up tensor (same shape); else null
+    const float *scales2;
     long stride;
     int nfull;
-    int O, I;
+    int O, I;  // output rows (a paired problem has 2 * O virtual rows)
     int pad;
 };
 
 struct WorkItem {
     int p;         // problem index within the launch
-    int row_begin;
+    int row_begin; // rows (virtual rows for a paired group)
     int row_end;
     int k;         // load slots for this problem's rows
 };
@@ -202,7 +219,10 @@ struct GroupedPlan {
 };
 
 // xv: every activation pointer 16-byte aligned and every I a multiple of 4.
-hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, hipStream_t st);
+// pair: every problem is a (gate, up) pair and y receives silu(g) * u.
+// ks: the slot count (WorkItem::k, 1..p.kmax) shared by every item of the launch.
+hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, bool pair, int ks,
+                          hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // LDS-tiled dequant + MFMA path (any S).
@@ -252,6 +272,7 @@ struct wq_group {
     uint32_t magic;
     int device, fmt, G;
     std::vector<wq_tensor *> ts;
+    std::vector<wq_tensor *> ts2;  // paired (gated feed-forward) group: the up tensors; else empty
     std::vector<wq::GroupDesc> h_desc;
     wq::GroupDesc *d_desc;
     bool has_gs = false;  // a group-scaled tensor is present: one launch per tensor
@@ -259,8 +280,13 @@ struct wq_group {
     struct Bucket {
         bool built = false;
         wq::GroupedPlan plan;
-        std::vector<int> first_item;           // per launch chunk: first item index
-        std::vector<int> n_items;              // per launch chunk
+        // per launch segment (the problems of one chunk that need the same
+        // number of load slots):
+        std::vector<int> seg_chunk;            // chunk index (problems chunk*64 ..)
+        std::vector<int> first_item;           // first item index
+        std::vector<int> n_items;
+        std::vector<int> ks;                   // slot count of every item of the segment
+        std::vector<uint64_t> mask;            // problems of the chunk in the segment
         wq::WorkItem *d_items = nullptr;
     } buckets[4];
 };
