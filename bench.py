@@ -153,6 +153,10 @@ def main():
                 + 4 * p.S * p.I + 4 * p.S * p.O)
 
     alg_bytes = sum(io_bytes(p) for p in probs)
+    if grouped:
+        # one launch per slot-count class: the gate/up rows (3 KiB) and the
+        # down rows (1 KiB); the gate/up launch dominates
+        gu_bytes = sum(io_bytes(p) for i, p in enumerate(probs) if i % 3 != 2)
     if ffn:
         # gate and up read one x and write one h between them; down reads h
         gu_bytes = sum(p.weight_bytes + 4 * p.O for i, p in enumerate(probs) if i % 3 != 2) + sum(
@@ -189,8 +193,17 @@ def main():
         else:
             wq.wq_matmul_dev(copies[r][0], xs[0], ys[0])
 
+    if grouped:
+        gu_groups = [wq.wq_grouped_create([t for j, t in enumerate(c) if j % 3 != 2]) for c in copies]
+        groups = groups + gu_groups
+        gu_x = [x for j, x in enumerate(xs) if j % 3 != 2]
+        gu_y = [y for j, y in enumerate(ys) if j % 3 != 2]
+
     def gate_up_only(i):
-        wq.wq_swiglu_matmul_dev(gated[i % n_rot], fx, fh)
+        if grouped:
+            wq.wq_grouped_matmul_dev(gu_groups[i % n_rot], gu_x, gu_y)
+        else:
+            wq.wq_swiglu_matmul_dev(gated[i % n_rot], fx, fh)
 
     stream = torch.cuda.current_stream()
     for i in range(W):
@@ -225,7 +238,7 @@ def main():
     wall = t1 - t0
     ev_s = ev0.elapsed_time(ev1) / 1e3
     per_launch = ev_s / K  # average launch duration on the launch stream (s)
-    if ffn:
+    if ffn or grouped:
         # the step is two launches: time the dominant one (gate/up) in a graph of its own
         g2 = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -261,10 +274,12 @@ def main():
     else:
         value = weight_bytes * K / wall / 1e9
         unit = "GB/s"
-        roof = {"bound": "hbm", "achieved": (gu_bytes if ffn else alg_bytes) / per_launch / 1e9,
+        roof = {"bound": "hbm", "achieved": (gu_bytes if (ffn or grouped) else alg_bytes) / per_launch / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         if ffn:
             roof["kernel"] = "fused gate/up (paired rows, silu(g)*u epilogue), all experts in one launch"
+        elif grouped:
+            roof["kernel"] = "grouped GEMV launch over the 16 gate/up matmuls (3 KiB rows)"
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_counters(args.workload)
 
@@ -295,7 +310,7 @@ def main():
             "pct_hbm_peak_weight_stream": None if compute_bound else 100.0 * value / HBM_PEAK_GBS,
             "event_us_per_launch": per_launch * 1e6,
             **({"event_us_per_step_two_launches": step_per_launch * 1e6,
-                "algorithmic_bytes_gate_up_launch": gu_bytes} if ffn else {}),
+                "algorithmic_bytes_gate_up_launch": gu_bytes} if (ffn or grouped) else {}),
             "plan": plans[:3],
         },
         "roofline": roof,

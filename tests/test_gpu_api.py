@@ -165,6 +165,44 @@ def test_graph_capture_replays_match_eager():
         wq.wq_tensor_free(t)
 
 
+def test_grouped_call_capture_two_launches():
+    """A grouped call with launches of two slot counts (gate/up rows and down
+    rows), captured in a graph and replayed, matches eager."""
+    probs = synth.moe_decode(n_experts=3, S=1)
+    ts = [gu.upload(p) for p in probs]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x).cuda() for p in probs]
+        ys_eager = [torch.empty((p.S, p.O), device="cuda") for p in probs]
+        ys_graph = [torch.zeros_like(y) for y in ys_eager]
+        gu.banner("grouped capture, two launches")
+        wq.wq_grouped_matmul_dev(g, xs, ys_eager)
+        torch.cuda.synchronize()
+        for p, y in zip(probs, ys_eager):
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, p.name)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            wq.wq_grouped_matmul_dev(g, xs, ys_graph)
+        torch.cuda.synchronize()
+        for i in range(4):
+            for y in ys_graph:
+                y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for y, ye in zip(ys_graph, ys_eager):
+                assert torch.equal(y, ye), "replay %d differs" % i
+            wq.wq_grouped_matmul_dev(g, xs, ys_eager)  # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
 def _capture(t, x, y):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
