@@ -19,7 +19,11 @@ of the same workload.
 The moe_ffn workload runs the whole gated feed-forward of 8 int4 experts per
 step (the fused gate/up launch writing h = silu(g) * u, then the grouped down
 launch); its roofline is that of the gate/up launch, timed in a graph of its
-own.
+own. moe_ffn_pipeline measures the same step and adds `config.pipeline`: the
+per-step time with the activations device-resident (graph replay, eager
+launches, a host synchronisation every step) and with host input/output
+every step (serialised on one stream, or double-buffered on copy streams that
+overlap the compute), the overlapped outputs checked against eager ones.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
 """
@@ -50,7 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dense_gemv",
-                    choices=["dense_gemv", "moe_decode", "moe_ffn", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
+                    choices=["dense_gemv", "moe_decode", "moe_ffn", "moe_ffn_pipeline", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
                              "dense_gemv_gs128", "prefill_gs128",
                              "prefill"])
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
@@ -96,7 +100,7 @@ def problems_for(name):
     if name == "moe_decode":
         return synth.moe_decode(), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
                                     "S=1 per expert, one grouped launch")
-    if name == "moe_ffn":
+    if name in ("moe_ffn", "moe_ffn_pipeline"):
         return synth.moe_decode(), ("moe_ffn: 8 experts x int4 {gate,up}[2048,6144] -> h = silu(g)*u -> "
                                     "down[6144,2048], S=1 per expert, fused gate/up launch + grouped down launch")
     if name.startswith("int2_gemv_s"):
@@ -145,7 +149,7 @@ def main():
     torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
     grouped = args.workload == "moe_decode"
-    ffn = args.workload == "moe_ffn"
+    ffn = args.workload in ("moe_ffn", "moe_ffn_pipeline")
     weight_bytes = sum(p.weight_bytes for p in probs)
 
     def io_bytes(p):  # weights, scales, activations in, results out
@@ -283,6 +287,11 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_counters(args.workload)
 
+    pipe = None
+    if args.workload == "moe_ffn_pipeline":
+        pipe = pipeline_modes(torch, wq, gated, downs, probs, n_rot, min(K, 400))
+        pipe["graph_replay_us_per_step"] = wall / K * 1e6
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(probs, compute_bound, args.cpu_seconds, ffn=ffn)
@@ -312,6 +321,7 @@ def main():
             **({"event_us_per_step_two_launches": step_per_launch * 1e6,
                 "algorithmic_bytes_gate_up_launch": gu_bytes} if (ffn or grouped) else {}),
             "plan": plans[:3],
+            **({"pipeline": pipe} if pipe else {}),
         },
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -324,6 +334,125 @@ def main():
     for c in copies:
         for t in c:
             wq.wq_tensor_free(t)
+
+
+def pipeline_modes(torch, wq, gated, downs, probs, n_rot, K):
+    """Per-step time (us) of the 8-expert feed-forward in different host/device arrangements.
+
+    Eager modes are launched from Python one call at a time; graph modes
+    capture the same K steps (copies, kernels, cross-stream event waits) into
+    one HIP graph and replay it."""
+    dev = torch.device("cuda:0")
+    E = len(probs) // 3
+    S, I, F, Od = probs[0].S, probs[0].I, probs[0].O, probs[2].O
+    gen = torch.Generator().manual_seed(20261202)
+    x_host = torch.empty((K, E, S, I), dtype=torch.float32, pin_memory=True)
+    x_host.copy_(torch.randn((K, E, S, I), generator=gen))
+    y_host = torch.empty((K, E, S, Od), dtype=torch.float32, pin_memory=True)
+    xd = [torch.zeros((E, S, I), device=dev) for _ in range(2)]
+    hd = [torch.empty((E, S, F), device=dev) for _ in range(2)]
+    yd = [torch.empty((E, S, Od), device=dev) for _ in range(2)]
+    cin, cout = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    ev_in = [torch.cuda.Event() for _ in range(2)]
+    ev_done = [torch.cuda.Event() for _ in range(2)]
+    ev_out = [torch.cuda.Event() for _ in range(2)]
+
+    def ffn(t, b, comp):
+        wq.wq_swiglu_ffn_dev(gated[t % n_rot], downs[t % n_rot], list(xd[b]), list(hd[b]), list(yd[b]),
+                             stream=comp)
+
+    def device_resident(comp):
+        for t in range(K):
+            ffn(t, 0, comp)
+
+    def host_io_serialised(comp):
+        for t in range(K):
+            xd[0].copy_(x_host[t], non_blocking=True)
+            ffn(t, 0, comp)
+            y_host[t].copy_(yd[0], non_blocking=True)
+
+    def host_io_overlapped(comp):
+        # step t uses slot t % 2: x of step t + 1 goes up (stream cin) and y
+        # of step t - 1 comes down (stream cout) while step t computes
+        fork = torch.cuda.Event()
+        fork.record(comp)
+        cin.wait_event(fork)
+        cout.wait_event(fork)
+
+        def load(t):
+            b = t % 2
+            with torch.cuda.stream(cin):
+                if t >= 2:
+                    cin.wait_event(ev_done[b])  # step t - 2 has read slot b
+                xd[b].copy_(x_host[t], non_blocking=True)
+                ev_in[b].record(cin)
+        load(0)
+        for t in range(K):
+            b = t % 2
+            if t + 1 < K:
+                load(t + 1)
+            comp.wait_event(ev_in[b])
+            if t >= 2:
+                comp.wait_event(ev_out[b])  # y of step t - 2 has left slot b
+            ffn(t, b, comp)
+            ev_done[b].record(comp)
+            with torch.cuda.stream(cout):
+                cout.wait_event(ev_done[b])
+                y_host[t].copy_(yd[b], non_blocking=True)
+                ev_out[b].record(cout)
+        comp.wait_event(ev_out[(K - 1) % 2])  # join the output stream
+
+    def eager(body, sync_each=False):
+        comp = torch.cuda.current_stream()
+        if not sync_each:
+            return lambda: body(comp)
+
+        def run():
+            for t in range(K):
+                xd[0].copy_(x_host[t], non_blocking=True)
+                ffn(t, 0, comp)
+                y_host[t].copy_(yd[0], non_blocking=True)
+                torch.cuda.synchronize()
+        return run
+
+    def graphed(body):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            body(side)
+        torch.cuda.synchronize()
+        return g.replay
+
+    def timed(run):
+        run()  # warm-up pass
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K * 1e6
+
+    out = {}
+    for name, run in (("eager_device_resident", eager(device_resident)),
+                      ("eager_host_io_serialised", eager(host_io_serialised)),
+                      ("eager_host_io_sync_each_step", eager(None, sync_each=True)),
+                      ("eager_host_io_overlapped", eager(host_io_overlapped)),
+                      ("graph_device_resident", graphed(device_resident)),
+                      ("graph_host_io_serialised", graphed(host_io_serialised)),
+                      ("graph_host_io_overlapped", graphed(host_io_overlapped))):
+        y_host.zero_()
+        out[name + "_us_per_step"] = timed(run)
+        if "host_io" in name:  # the outputs that came back equal eager ones from the same inputs
+            ok = True
+            for t in sorted({0, 1, K // 2, K - 1}):
+                xd[0].copy_(x_host[t])
+                ffn(t, 0, torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                ok = ok and torch.equal(yd[0].cpu(), y_host[t])
+            out[name + "_outputs_checked"] = bool(ok)
+    out["steps"] = K
+    out["host_bytes_per_step"] = 4 * E * S * (I + Od)
+    return out
 
 
 def cpu_baseline(probs, compute_bound, seconds, ffn=False):
