@@ -19,10 +19,14 @@
 //    refilled with row r+D right after. Reloads in the steady state are
 //    unconditional so the wait counts stay exact.
 //  * Dequantization happens in registers on 32-bit words. For int4 and int2
-//    the code offset is folded out of the inner loop: codes are converted
-//    unshifted (byte masks + v_cvt_f32_ubyteN, with the activations of the
-//    higher fields pre-divided by 16 / 4^k, exact powers of two) and
-//    offset * sum(x) is subtracted once per lane. The lane's sum(x) is formed
+//    the code offset is folded out of the inner loop: codes are used
+//    unshifted and offset * sum(x) is subtracted once per lane. A code is
+//    never converted on its own: one mask of a word leaves two codes in the
+//    low bits of its 16-bit halves, each half read as an f16 subnormal
+//    (code * 2^-24, exact), and v_fma_mix_f32 widens that half inside the
+//    FMA. Codes sitting higher in a byte are 4^k or 16 times larger; the
+//    activations they meet are pre-divided by the same power of two, and
+//    the finished sum is multiplied by 2^24 (all exact). The lane's sum(x) is formed
 //    in the same order as the FMA chain, so a row whose codes all decode to
 //    zero gives exactly 0.
 //  * Lanes are reduced with DPP (quad_perm, row_shr, row_bcast) instead of an
@@ -38,6 +42,7 @@
 //    colibri "第 8 章 · 02 CUDA/Metal/Vulkan 三后端" names in its learning
 //    goals and section recap without giving its activation).
 #include "wq_internal.h"
+
 
 namespace wq {
 namespace {
@@ -74,6 +79,25 @@ template <int LW> __device__ __forceinline__ void load_w(const uint8_t *p, uint3
     }
 }
 
+// The low / high 16 bits of a word read as an f16 value, widened to f32.
+__device__ __forceinline__ float f16_lo(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)p); }
+__device__ __forceinline__ float f16_hi(uint32_t p) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+}
+
+// How int4 / int2 codes reach the FMAs. MIX: two codes per mask, read as
+// f16 subnormals (code * 2^-24) that v_fma_mix_f32 widens inside the FMA --
+// fewest instructions per element when each code meets one activation row.
+// Otherwise (several activation rows) each code is converted once
+// (v_cvt_f32_ubyteN) and meets the rows in plain v_fmac_f32.
+// (Measured: at S = 1 the mixed form is the faster one; at S = 4 the plain
+// FMAs are, the conversion being shared by the rows.)
+template <int FMT, int SMAX> constexpr bool kMix = (FMT == WQ_I4 || FMT == WQ_I2) && SMAX == 1;
+
+// Scale of the accumulated sums: with MIX a row's sum is 2^-24 times the
+// code sum.
+template <int FMT, int SMAX> __device__ constexpr float acc_unscale() { return kMix<FMT, SMAX> ? 16777216.0f : 1.0f; }
+
 // Keeps the compiler from pushing a byte mask into each field extraction
 // (which would turn one v_cvt_f32_ubyteN into v_bfe_u32 + v_cvt_f32_ubyte0).
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
@@ -81,21 +105,32 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
-// acc[s] += sum over the EPW fields of one word of code * xw[e][s].
+// With the mixed form at S = 1, int4 / int2 sums run in two independent
+// chains (fields in the low and in the high f16 half of the masked words),
+// so consecutive mixed FMAs do not depend on each other (back to back they
+// need a wait state); each chain visits its fields in ascending order. With
+// several activation rows the rows already give independent chains.
+template <int FMT, int SMAX> constexpr int kChains = kMix<FMT, SMAX> ? 2 : 1;
+template <int FMT, int SMAX> __device__ constexpr int field_chain(int e) {
+    return !kMix<FMT, SMAX> ? 0 : FMT == WQ_I4 ? (e >= 4) : (e >= 8);
+}
+
+// acc[c][s] += sum over the fields e of chain c of one word of
+// code * xw[e][s] (times 2^-24 for int4 / int2, see acc_unscale).
 template <int FMT, int SMAX>
-__device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], float (&acc)[SMAX]) {
+__device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], float (&acc)[kChains<FMT, SMAX>][SMAX]) {
     if constexpr (FMT == WQ_F32) {
         const float q = __uint_as_float(w);
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) acc[s] = __builtin_fmaf(q, xw[0][s], acc[s]);
+        for (int s = 0; s < SMAX; ++s) acc[0][s] = __builtin_fmaf(q, xw[0][s], acc[0][s]);
     } else if constexpr (FMT == WQ_I8) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float q = (float)(int)(int8_t)(w >> (8 * b));
 #pragma unroll
-            for (int s = 0; s < SMAX; ++s) acc[s] = __builtin_fmaf(q, xw[b][s], acc[s]);
+            for (int s = 0; s < SMAX; ++s) acc[0][s] = __builtin_fmaf(q, xw[b][s], acc[0][s]);
         }
-    } else if constexpr (FMT == WQ_I4) {
+    } else if constexpr (FMT == WQ_I4 && !kMix<FMT, SMAX>) {
         const uint32_t lo = opaque(w & 0x0F0F0F0Fu);  // even fields, code in bits 0..3 of each byte
         const uint32_t hi = opaque(w & 0xF0F0F0F0u);  // odd fields, 16 * code
 #pragma unroll
@@ -104,30 +139,60 @@ __device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], fl
             const float ch = (float)((hi >> (8 * b)) & 0xFFu);
 #pragma unroll
             for (int s = 0; s < SMAX; ++s) {
-                acc[s] = __builtin_fmaf(cl, xw[2 * b][s], acc[s]);
-                acc[s] = __builtin_fmaf(ch, xw[2 * b + 1][s], acc[s]);
+                acc[0][s] = __builtin_fmaf(cl, xw[2 * b][s], acc[0][s]);
+                acc[0][s] = __builtin_fmaf(ch, xw[2 * b + 1][s], acc[0][s]);
             }
         }
-    } else {  // WQ_I2
-        const uint32_t m0 = opaque(w & 0x03030303u);
-        const uint32_t m1 = opaque(w & 0x0C0C0C0Cu);
-        const uint32_t m2 = opaque(w & 0x30303030u);
-        const uint32_t m3 = opaque(w & 0xC0C0C0C0u);
+    } else if constexpr (FMT == WQ_I2 && !kMix<FMT, SMAX>) {
+        const uint32_t m[4] = {opaque(w & 0x03030303u), opaque(w & 0x0C0C0C0Cu), opaque(w & 0x30303030u),
+                               opaque(w & 0xC0C0C0C0u)};
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float c0 = (float)((m0 >> (8 * b)) & 0xFFu);
-            const float c1 = (float)((m1 >> (8 * b)) & 0xFFu);
-            const float c2 = (float)((m2 >> (8 * b)) & 0xFFu);
-            const float c3 = (float)((m3 >> (8 * b)) & 0xFFu);
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int s = 0; s < SMAX; ++s) {
-                acc[s] = __builtin_fmaf(c0, xw[4 * b + 0][s], acc[s]);
-                acc[s] = __builtin_fmaf(c1, xw[4 * b + 1][s], acc[s]);
-                acc[s] = __builtin_fmaf(c2, xw[4 * b + 2][s], acc[s]);
-                acc[s] = __builtin_fmaf(c3, xw[4 * b + 3][s], acc[s]);
+            for (int f = 0; f < 4; ++f) {
+                const float c = (float)((m[f] >> (8 * b)) & 0xFFu);  // code * 4^f
+#pragma unroll
+                for (int s = 0; s < SMAX; ++s)
+                    acc[0][s] = __builtin_fmaf(c, xw[4 * b + f][s], acc[0][s]);
             }
-        }
+    } else if constexpr (FMT == WQ_I4) {
+        // Each 16-bit half of a masked word is an f16 subnormal whose bits
+        // are a code (or 16 x a code): value code * 2^-24, exact and with no
+        // bias, which v_fma_mix_f32 widens inside the FMA. Fields 2b and
+        // 2b + 1 are the low and high nibble of byte b; m[j] holds field j
+        // in its low half (chain 0) and field j + 4 in its high half (chain 1).
+        const uint32_t t = w >> 8;  // bytes 1 and 3 into the low byte of each half
+        const uint32_t m[4] = {w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+                for (int s = 0; s < SMAX; ++s)
+                    acc[hi][s] = __builtin_fmaf(hi ? f16_hi(m[j]) : f16_lo(m[j]), xw[4 * hi + j][s], acc[hi][s]);
+    } else {  // WQ_I2: fields 4b..4b + 3 in bit pairs 0-1 .. 6-7 of byte b, same f16 reading
+        const uint32_t v[2] = {w, w >> 8};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const uint32_t mf = v[h] & (0x00030003u << (2 * f));  // code * 4^f in each half
+#pragma unroll
+                for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+                    for (int s = 0; s < SMAX; ++s)
+                        acc[hi][s] = __builtin_fmaf(hi ? f16_hi(mf) : f16_lo(mf), xw[8 * hi + 4 * h + f][s],
+                                                    acc[hi][s]);
+            }
     }
+}
+
+// A load of one fp32 value at a wave-uniform address through the scalar data
+// cache (s_load). A vector load there would queue behind the weight loads in
+// flight (vector loads complete in order) and its wait would drain the ring.
+// Only for data no kernel writes while this one runs (row scales).
+__device__ __forceinline__ float uniform_ld(const float *p) {
+    return *(const __attribute__((address_space(4))) float *)p;
 }
 
 // silu(g) * u with silu(z) = z / (1 + e^-z), in fp32 (expf from the device
@@ -158,7 +223,8 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
 // PAIR: O counts virtual rows (twice the output rows); virtual row 2o is row
 // o of (w, scales), 2o + 1 row o of (w2, scales2); y is S x O/2 and receives
 // gated(g, u). D is even, row_begin and rpt are multiples of D.
-template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool XL = false, bool GS = false, bool PAIR = false>
+//
+template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool GS = false, bool PAIR = false>
 __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long stride, int nfull,
                                           const float *__restrict__ scales, const float *__restrict__ x,
                                           float *__restrict__ y, int O, int I, int S, int team, int tl,
@@ -219,8 +285,31 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
     // wave-uniform: no activation of this wave needs masking
     const bool wave_in = __builtin_amdgcn_ballot_w64(!lane_in) == 0;
 #define WQ_XE(k, g) (xb[k] + xs_step[k] * (g))
+    // The weight ring: D rows of this wave's weights in registers.
+    uint32_t ring[D][KMAX][WPC];
+    float gring[D][KMAX];  // GS: the group scale of each slot, per row in flight
+    int grp[KMAX];         // GS: group of each slot (clamped: dead slots have zero activations)
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) grp[k] = GS ? min(xb[k] / max(gs, 1), ng - 1) : 0;
+    auto load_row = [&](uint32_t (&b)[KMAX][WPC], float (&gv)[KMAX], int row) {
+        const long r = min(row, row_last);
+        // wave-uniform tensor, row and scale pointer
+        const long rr = PAIR ? (r >> 1) : r;
+        const uint8_t *wb = (PAIR && (r & 1)) ? w2 : w;
+        const float *sb = (PAIR && (r & 1)) ? scales2 : scales;
+        const uint8_t *p = wb + rr * stride;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) load_w<LW>(p + cb[k], b[k]);
+        if constexpr (GS) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) gv[k] = sb[rr * ng + grp[k]];
+        }
+    };
+    // The activations are requested first, straight from global memory (an
+    // LDS copy per block measured slower: its barrier holds back the weight
+    // stream), then the first D weight rows; vector loads complete in order,
+    // so staging the activations waits for them alone.
     if constexpr (XV) {  // x 16-byte aligned and I % 4 == 0: a run is entirely inside or outside the row
-        // (with XL, x points at the block's LDS copy of the activations)
         const uint32_t last4 = (uint32_t)(I - 4) * 4u;  // clamp: runs past the row are masked below
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
@@ -260,39 +349,26 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     for (int e = 0; e < EPC; ++e) xr[k][e][s] = 0.0f;
                 }
     }
-    // Weight ring prologue, issued after the activation loads: the
-    // activations (cache hits) complete first and are prepared while the
-    // first rows stream in.
-    uint32_t ring[D][KMAX][WPC];
-    float gring[D][KMAX];  // GS: the group scale of each slot, per row in flight
-    int grp[KMAX];         // GS: group of each slot (clamped: dead slots have zero activations)
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) grp[k] = GS ? min(xb[k] / max(gs, 1), ng - 1) : 0;
-    auto load_row = [&](uint32_t (&b)[KMAX][WPC], float (&gv)[KMAX], int row) {
-        const long r = min(row, row_last);
-        // wave-uniform tensor, row and scale pointer
-        const long rr = PAIR ? (r >> 1) : r;
-        const uint8_t *wb = (PAIR && (r & 1)) ? w2 : w;
-        const float *sb = (PAIR && (r & 1)) ? scales2 : scales;
-        const uint8_t *p = wb + rr * stride;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) load_w<LW>(p + cb[k], b[k]);
-        if constexpr (GS) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) gv[k] = sb[rr * ng + grp[k]];
-        }
-    };
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_row(ring[d], gring[d], row_begin + d);
+    for (int d = 0; d < D; ++d) {
+        load_row(ring[d], gring[d], row_begin + d);
+        __builtin_amdgcn_sched_barrier(0);  // rows issued in ring order (waits count whole rows)
+    }
 
-    float sx[SMAX];
+    // Activation sums per FMA chain, in each chain's own order.
+    constexpr int NC = kChains<FMT, SMAX>;
+    float sx[NC][SMAX];
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s) sx[s] = 0.0f;
-    float sxk[KMAX][SMAX];  // GS: activation sums per slot
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s) sx[c][s] = 0.0f;
+    float sxk[KMAX][NC][SMAX];  // GS: activation sums per slot
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) sxk[k][s] = 0.0f;
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int s = 0; s < SMAX; ++s) sxk[k][c][s] = 0.0f;
     if (wave_in) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
@@ -303,8 +379,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     const float v = xr[k][e][s];
                     xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
                     if constexpr (OFF != 0) {
-                        if constexpr (GS) sxk[k][s] += v;
-                        else sx[s] += v;
+                        if constexpr (GS) sxk[k][field_chain<FMT, SMAX>(e % EPW)][s] += v;
+                        else sx[field_chain<FMT, SMAX>(e % EPW)][s] += v;
                     }
                 }
     } else {
@@ -319,8 +395,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     const float v = in ? xr[k][e][s] : 0.0f;
                     xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
                     if constexpr (OFF != 0) {
-                        if constexpr (GS) sxk[k][s] += v;
-                        else sx[s] += v;
+                        if constexpr (GS) sxk[k][field_chain<FMT, SMAX>(e % EPW)][s] += v;
+                        else sx[field_chain<FMT, SMAX>(e % EPW)][s] += v;
                     }
                 }
     }
@@ -336,25 +412,37 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     for (int j = 0; j < WPC; ++j) b[k][j] = 0u;
                 }
         }
-        float acc[SMAX];
+        float acc[NC][SMAX];  // code sums per chain (not GS)
+        float gacc[SMAX];     // GS: sum of the group-scaled slot sums
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) acc[s] = 0.0f;
+        for (int s = 0; s < SMAX; ++s) {
+            gacc[s] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c][s] = 0.0f;
+        }
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (k < K) {
                 if constexpr (GS) {
                     // the slot's sum (offset removed with its own activation
                     // sum, so all-zero codes give exactly 0) times its group scale
-                    float t[SMAX];
+                    float t[NC][SMAX];
 #pragma unroll
-                    for (int s = 0; s < SMAX; ++s) t[s] = 0.0f;
+                    for (int c = 0; c < NC; ++c)
+#pragma unroll
+                        for (int s = 0; s < SMAX; ++s) t[c][s] = 0.0f;
 #pragma unroll
                     for (int j = 0; j < WPC; ++j) word_fma<FMT, SMAX>(b[k][j], &xr[k][j * EPW], t);
 #pragma unroll
                     for (int s = 0; s < SMAX; ++s) {
-                        float u = t[s];
-                        if constexpr (OFF != 0) u -= (float)OFF * sxk[k][s];
-                        acc[s] = fmaf(gv[k], u, acc[s]);
+                        float u = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < NC; ++c) {
+                            float uc = t[c][s] * acc_unscale<FMT, SMAX>();
+                            if constexpr (OFF != 0) uc -= (float)OFF * sxk[k][c][s];
+                            u += uc;
+                        }
+                        gacc[s] = fmaf(gv[k], u, gacc[s]);
                     }
                 } else {
 #pragma unroll
@@ -363,8 +451,17 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             }
 #pragma unroll
         for (int s = 0; s < SMAX; ++s) {
-            float t = acc[s];
-            if constexpr (OFF != 0 && !GS) t -= (float)OFF * sx[s];
+            float t = 0.0f;
+            if constexpr (GS) {
+                t = gacc[s];
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    float tc = acc[c][s] * acc_unscale<FMT, SMAX>();
+                    if constexpr (OFF != 0) tc -= (float)OFF * sx[c][s];
+                    t += tc;
+                }
+            }
             part[s] = wave_sum_lane63(t);
         }
     };
@@ -380,8 +477,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     if (d < nvalid) {
                         const int o = (row0 + d) >> 1;
                         const int oc = min(o, Oy - 1);
-                        const float sg = GS ? 1.0f : scales[oc];  // wave-uniform: scalar loads
-                        const float su = GS ? 1.0f : scales2[oc];
+                        const float sg = GS ? 1.0f : uniform_ld(scales + oc);
+                        const float su = GS ? 1.0f : uniform_ld(scales2 + oc);
                         if (lane == 63 && row0 + d <= row_last) {
 #pragma unroll
                             for (int s = 0; s < SMAX; ++s)
@@ -401,8 +498,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 #pragma unroll
                 for (int j = 0; j < D / 2; ++j) {
                     const int oc = min((row0 >> 1) + j, Oy - 1);
-                    sg[j] = GS ? 1.0f : scales[oc];
-                    su[j] = GS ? 1.0f : scales2[oc];
+                    sg[j] = GS ? 1.0f : uniform_ld(scales + oc);
+                    su[j] = GS ? 1.0f : uniform_ld(scales2 + oc);
                 }
                 __syncthreads();
                 if (wave_in_team == 0 && lane < (D / 2) * SMAX) {
@@ -431,7 +528,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             for (int d = 0; d < D; ++d) {
                 if (d < nvalid) {
                     const int row = row0 + d;
-                    const float sc = GS ? 1.0f : scales[min(row, O - 1)];  // wave-uniform: scalar load
+                    const float sc = GS ? 1.0f : uniform_ld(scales + min(row, O - 1));
                     if (lane == 63 && row <= row_last) {
 #pragma unroll
                         for (int s = 0; s < SMAX; ++s)
@@ -449,7 +546,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             }
             float sc[D];  // wave-uniform rows: scalar loads
 #pragma unroll
-            for (int d = 0; d < D; ++d) sc[d] = GS ? 1.0f : scales[min(row0 + d, O - 1)];
+            for (int d = 0; d < D; ++d) sc[d] = GS ? 1.0f : uniform_ld(scales + min(row0 + d, O - 1));
             __syncthreads();
             if (wave_in_team == 0 && lane < D * SMAX) {
                 const int d = lane / SMAX, s = lane % SMAX;
@@ -473,6 +570,10 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
         for (int d = 0; d < D; ++d) {
             row_partials(ring[d], gring[d], part[d]);
             load_row(ring[d], gring[d], row_begin + i + d + D);
+            // keep the refill of this ring slot right here: left to itself
+            // the scheduler sinks it below the next row's arithmetic, and the
+            // wave then has no weight load in flight between ring passes
+            __builtin_amdgcn_sched_barrier(0);
         }
         finish(row_begin + i, part, D);
     }
@@ -491,33 +592,19 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
     }
 }
 
-// XL: the block first copies the S x I activations into LDS (one coalesced
-// pass per block instead of one per wave) and the waves stage their
-// registers from there; used when x fits (host check) and XV holds.
-template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool XL, bool GS = false, bool PAIR = false>
+template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool GS = false, bool PAIR = false>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     __shared__ float red[2 * kMaxTeam * D * SMAX];
-    extern __shared__ __attribute__((aligned(16))) float xl[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int team_in_block = wave / a.team;
     const int wave_in_team = wave - team_in_block * a.team;
     const int team_id = blockIdx.x * a.teams_per_block + team_in_block;
     const int row_begin = team_id * a.rows_per_team;
-    const float *xsrc = a.x;
-    if constexpr (XL) {
-        const int n4 = a.S * a.I / 4;
-        const float4 *src = reinterpret_cast<const float4 *>(a.x);
-        float4 *dst = reinterpret_cast<float4 *>(xl);
-        for (int i = threadIdx.x; i < n4; i += blockDim.x) dst[i] = src[i];
-        __syncthreads();
-        xsrc = xl;
-    }
     if (row_begin >= a.O) return;  // uniform over the team (and the block when team > 1)
-    team_rows<FMT, SMAX, LW, KS, D, XV, XL, GS, PAIR>(a.w, a.stride, a.nfull, a.scales, xsrc, a.y, a.O, a.I,
-                                                      a.S, a.team, wave_in_team * 64 + lane, wave_in_team,
-                                                      row_begin, a.rows_per_team, red, a.gs, a.ng, a.w2,
-                                                      a.scales2);
+    team_rows<FMT, SMAX, LW, KS, D, XV, GS, PAIR>(a.w, a.stride, a.nfull, a.scales, a.x, a.y, a.O, a.I, a.S, a.team,
+                                                  wave_in_team * 64 + lane, wave_in_team, row_begin,
+                                                  a.rows_per_team, red, a.gs, a.ng, a.w2, a.scales2);
 }
 
 // PAIR: every problem is a (gate, up) pair; its work items count virtual rows.
@@ -537,7 +624,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
     const GroupDesc d = a.desc[p];
     const int r0 = __builtin_amdgcn_readfirstlane(it.row_begin);
     const int nr = __builtin_amdgcn_readfirstlane(it.row_end - it.row_begin);
-    team_rows<FMT, SMAX, LW, KS, ring_depth(KMAX, D, KS), XV, false, false, PAIR>(
+    team_rows<FMT, SMAX, LW, KS, ring_depth(KMAX, D, KS), XV, false, PAIR>(
         d.w, d.stride, d.nfull, d.scales, a.x[p], a.y[p], PAIR ? 2 * d.O : d.O, d.I, S, 1, lane, 0, r0, nr, nullptr,
         0, 1, d.w2, d.scales2);
 }
@@ -629,48 +716,33 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu) {
 
 template <int F, int SM, int LW, int KM, int D>
 hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStream_t st) {
-    // exact slot count: 1..KM; activations through LDS when they fit
-    const size_t xbytes = (size_t)a.S * a.I * sizeof(float);
-    const bool xl = xv && xbytes <= (size_t)kXLdsMaxBytes;
-#define WQ_K(KS)                                                                                          \
-    if constexpr (KS <= KM) {                                                                             \
-        if (p.k == KS) {                                                                                  \
-            if (a.w2 != nullptr) {                                                                        \
-                if (a.gs > 0) return hipErrorInvalidValue;                                                \
-                if (xl)                                                                                   \
-                    hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, true, false, true>), dim3(p.grid), \
-                                       dim3(p.block), xbytes, st, a);                                     \
-                else if (xv)                                                                              \
-                    hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, false, false, true>), dim3(p.grid), \
-                                       dim3(p.block), 0, st, a);                                          \
-                else                                                                                      \
-                    hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, false, false, true>),        \
-                                       dim3(p.grid), dim3(p.block), 0, st, a);                            \
-                return hipGetLastError();                                                                 \
-            }                                                                                             \
-            if constexpr (F != WQ_F32) {                                                                  \
-                if (a.gs > 0) {                                                                           \
-                    if (xl)                                                                               \
-                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, true, true>), dim3(p.grid), \
-                                           dim3(p.block), xbytes, st, a);                                 \
-                    else                                                                                  \
-                        hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, false, true>), dim3(p.grid), \
-                                           dim3(p.block), 0, st, a);                                      \
-                    return hipGetLastError();                                                             \
-                }                                                                                         \
-            }                                                                                             \
-            if (xl)                                                                                       \
-                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, true>), dim3(p.grid), dim3(p.block), \
-                                   xbytes, st, a);                                                        \
-            else if (xv)                                                                                  \
-                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
-            else                                                                                          \
-                hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, false>), dim3(p.grid), dim3(p.block), 0, st, a); \
-            return hipGetLastError();                                                                     \
-        }                                                                                                 \
+    // exact slot count: 1..KM; 16-byte activation loads when x allows (xv)
+#define WQ_GO(KS, GS_, PAIR_)                                                                                   \
+    do {                                                                                                        \
+        if (xv)                                                                                                 \
+            hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, GS_, PAIR_>), dim3(p.grid), \
+                               dim3(p.block), 0, st, a);                                                        \
+        else                                                                                                    \
+            hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, GS_, PAIR_>),         \
+                               dim3(p.grid), dim3(p.block), 0, st, a);                                          \
+        return hipGetLastError();                                                                               \
+    } while (0)
+#define WQ_K(KS)                                                     \
+    if constexpr (KS <= KM) {                                        \
+        if (p.k == KS) {                                             \
+            if (a.w2 != nullptr) {                                   \
+                if (a.gs > 0) return hipErrorInvalidValue;           \
+                WQ_GO(KS, false, true);                              \
+            }                                                        \
+            if constexpr (F != WQ_F32) {                             \
+                if (a.gs > 0) WQ_GO(KS, true, false);                \
+            }                                                        \
+            WQ_GO(KS, false, false);                                 \
+        }                                                            \
     }
     WQ_K(1) WQ_K(2) WQ_K(3) WQ_K(4)
 #undef WQ_K
+#undef WQ_GO
     return hipErrorInvalidValue;
 }
 

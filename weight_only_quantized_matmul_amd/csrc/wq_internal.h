@@ -18,7 +18,6 @@ constexpr uint32_t kGroupMagic = 0x57514731u;  // "WQG1"
 constexpr int kRowAlign = 16;                  // device row stride alignment (bytes)
 constexpr int kGroupMaxPerLaunch = 64;         // problems passed by value per grouped launch
 constexpr int kMaxTeam = 8;                    // waves that may share one row
-constexpr int kXLdsMaxBytes = 64 * 1024;       // activations staged through LDS up to this size
 
 // Bits per stored element, by format code.
 inline int fmt_bits(int fmt) {
