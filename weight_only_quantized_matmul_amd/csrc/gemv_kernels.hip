@@ -469,7 +469,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
     // Finish D rows starting at row0: part[d][s] holds this wave's totals.
     int pb = 0;
     const int Oy = PAIR ? O / 2 : O;  // output rows (row stride of y)
-    auto finish = [&](int row0, float (&part)[D][SMAX], int nvalid) {
+    int cpos = 0;  // rows of the open chunk (team > 1, not PAIR)
+    auto finish = [&](int row0, float (&part)[D][SMAX], int nvalid, bool last) {
         if constexpr (PAIR) {
             if (team == 1) {
 #pragma unroll
@@ -537,28 +538,43 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 }
             }
         } else {
-            float *rbuf = red + pb * (kMaxTeam * D * SMAX);
+            // Several waves share each row: their totals (and the row scales)
+            // collect in LDS over a chunk of kTeamChunk rows, and the block
+            // syncs once per chunk; wave 0 then adds the team's totals in
+            // wave order. Two chunk buffers: the barrier that closes chunk
+            // n + 1 also tells that wave 0 has read chunk n.
+            float *cbuf = red + pb * (kTeamChunk * kMaxTeam * SMAX);
+            float *sbuf = red + 2 * (kTeamChunk * kMaxTeam * SMAX) + pb * kTeamChunk;
             if (lane == 63) {
 #pragma unroll
                 for (int d = 0; d < D; ++d)
 #pragma unroll
-                    for (int s = 0; s < SMAX; ++s) rbuf[(wave_in_team * D + d) * SMAX + s] = part[d][s];
+                    for (int s = 0; s < SMAX; ++s)
+                        cbuf[((cpos + d) * kMaxTeam + wave_in_team) * SMAX + s] = part[d][s];
             }
-            float sc[D];  // wave-uniform rows: scalar loads
+            if (wave_in_team == 0) {
 #pragma unroll
-            for (int d = 0; d < D; ++d) sc[d] = GS ? 1.0f : uniform_ld(scales + min(row0 + d, O - 1));
-            __syncthreads();
-            if (wave_in_team == 0 && lane < D * SMAX) {
-                const int d = lane / SMAX, s = lane % SMAX;
-                const int row = row0 + d;
-                float t = 0.0f;
-                for (int w2 = 0; w2 < team; ++w2) t += rbuf[(w2 * D + d) * SMAX + s];
-                float scd = sc[0];
-#pragma unroll
-                for (int j = 1; j < D; ++j) scd = (d == j) ? sc[j] : scd;
-                if (d < nvalid && row <= row_last && s < S) y[(long)s * O + row] = scd * t;
+                for (int d = 0; d < D; ++d) {
+                    const float sc = GS ? 1.0f : uniform_ld(scales + min(row0 + d, O - 1));  // scalar load
+                    if (lane == 63) sbuf[cpos + d] = sc;
+                }
             }
-            pb ^= 1;
+            cpos += D;
+            if (cpos == kTeamChunk || last) {
+                __syncthreads();
+                if (wave_in_team == 0) {
+                    const int crow0 = row0 + D - cpos;  // first row of the chunk
+                    for (int j = lane; j < cpos * SMAX; j += 64) {
+                        const int r = j / SMAX, s = j % SMAX;
+                        const int row = crow0 + r;
+                        float t = 0.0f;
+                        for (int w2 = 0; w2 < team; ++w2) t += cbuf[(r * kMaxTeam + w2) * SMAX + s];
+                        if (r < cpos - D + nvalid && row <= row_last && s < S) y[(long)s * O + row] = sbuf[r] * t;
+                    }
+                }
+                pb ^= 1;
+                cpos = 0;
+            }
         }
     };
 
@@ -575,7 +591,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             // wave then has no weight load in flight between ring passes
             __builtin_amdgcn_sched_barrier(0);
         }
-        finish(row_begin + i, part, D);
+        finish(row_begin + i, part, D, false);
     }
     {
         float part[D][SMAX];
@@ -588,13 +604,17 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 for (int s = 0; s < SMAX; ++s) part[d][s] = 0.0f;
             }
         }
-        finish(row_begin + i, part, rpt - i);
+        finish(row_begin + i, part, rpt - i, true);
     }
 }
 
 template <int FMT, int SMAX, int LW, int KS, int D, bool XV, bool GS = false, bool PAIR = false>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
-    __shared__ float red[2 * kMaxTeam * D * SMAX];
+    // team > 1: two chunk buffers of totals and scales (paired rows: two
+    // ring passes of totals, which fit in the same space)
+    __shared__ float red[2 * kTeamChunk * kMaxTeam * SMAX + 2 * kTeamChunk];
+    static_assert(2 * kMaxTeam * D * SMAX <= 2 * kTeamChunk * kMaxTeam * SMAX, "paired reduction space");
+    static_assert(kTeamChunk % D == 0, "a chunk holds whole ring passes");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int team_in_block = wave / a.team;
@@ -684,7 +704,7 @@ GemvShape gemv_shape(int fmt, int smax) {
     return GemvShape{0, 0, 0};
 }
 
-GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu) {
+GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool split) {
     GemvPlan p;
     p.fmt = fmt;
     p.smax = gemv_smax_bucket(S);
@@ -694,7 +714,10 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu) {
     p.lw = sh.lw;
     p.kmax = sh.kmax;
     const long stride = round_up(row_bytes(fmt, I), kRowAlign);
-    const long per_wave = 64L * sh.lw * sh.kmax;
+    // Slots per lane: up to kmax, a team of waves sharing a longer row; with
+    // split, one slot per lane (fewer activations staged per wave).
+    const long slots = (split && (stride + 64L * sh.lw - 1) / (64L * sh.lw) <= kMaxTeam) ? 1 : sh.kmax;
+    const long per_wave = 64L * sh.lw * slots;
     const long team = (stride + per_wave - 1) / per_wave;
     if (team > kMaxTeam) return p;  // row too long for the register GEMV
     p.team = (int)team;

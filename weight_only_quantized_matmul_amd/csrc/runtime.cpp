@@ -136,13 +136,15 @@ int gemv_limit(int fmt) {
 }
 
 // Which path a call takes. Returns 1 (gemv) or 2 (tiled).
-int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp) {
+// Group-scaled tensors split each row over a team of one-slot waves (their
+// natural-order rows stage activations less efficiently; measured faster).
+int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool split = false) {
     if (g_cfg.force_path != 2 && S <= gemv_limit(fmt)) {
-        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu);
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
         if (gp->ok) return 1;
     }
     if (g_cfg.force_path == 1) {
-        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu);
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
         if (gp->ok) return 1;
     }
     return 2;
@@ -181,7 +183,7 @@ int ensure_workspace(DeviceCtx &d, size_t bytes, hipStream_t st, uint16_t **out)
 int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t st) {
     DeviceCtx &d = g_dev[t->device];
     wq::GemvPlan gp;
-    if (choose_path(t->fmt, t->O, t->I, S, d.cus, &gp) == 1) {
+    if (choose_path(t->fmt, t->O, t->I, S, d.cus, &gp, t->gs > 0) == 1) {
         wq::GemvArgs a;
         a.w = t->d_w;
         a.scales = t->d_scales;

@@ -18,6 +18,7 @@ constexpr uint32_t kGroupMagic = 0x57514731u;  // "WQG1"
 constexpr int kRowAlign = 16;                  // device row stride alignment (bytes)
 constexpr int kGroupMaxPerLaunch = 64;         // problems passed by value per grouped launch
 constexpr int kMaxTeam = 8;                    // waves that may share one row
+constexpr int kTeamChunk = 32;                 // rows a team collects in LDS between barriers
 
 // Bits per stored element, by format code.
 inline int fmt_bits(int fmt) {
@@ -174,7 +175,9 @@ __host__ __device__ constexpr int ring_depth(int kmax, int d, int ks) {
 }
 int gemv_smax_bucket(int S); // 1,2,4,8 or 0 if S > 8
 
-GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu);
+// split: one load slot per lane, the row shared by as many waves as that
+// needs (when at most kMaxTeam); else up to the shape's slots per lane.
+GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool split = false);
 hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);  // a.gs, a.w2 select the variant
 
 // h[j] = silu(h[j]) * u[j], j < n (gated feed-forward after separate gate and up matmuls)
