@@ -275,6 +275,14 @@ def main():
                 "peak": BF16_MFMA_PEAK_TFLOPS if bf16x3 else FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
         if bf16x3:
             roof["issued_mfma_flops_per_launch"] = 3.0 * alg_flops
+    elif args.workload in ("int2_gemv_s4", "int2_gemv_s8"):
+        # int2 with S >= 4 activation rows: S fp32 FMAs per 0.25-byte weight
+        # element bind the vector ALUs before HBM (packed fp32 FMAs are not
+        # used), so the roofline is the vector FMA rate; HBM rate alongside.
+        value = weight_bytes * K / wall / 1e9
+        unit = "GB/s"
+        roof = {"bound": "alu", "achieved": alg_flops / per_launch / 1e12, "peak": FP32_VALU_FMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "hbm_achieved_gbs": alg_bytes / per_launch / 1e9}
     else:
         value = weight_bytes * K / wall / 1e9
         unit = "GB/s"
