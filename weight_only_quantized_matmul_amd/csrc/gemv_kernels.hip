@@ -204,15 +204,23 @@ __device__ __forceinline__ float dpp_move(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
 }
 
-// Sum over the 64 lanes; the total lands in lane 63.
-__device__ __forceinline__ float wave_sum_lane63(float v) {
-    v += dpp_move<0xB1>(v);        // quad_perm [1,0,3,2]
-    v += dpp_move<0x4E>(v);        // quad_perm [2,3,0,1]
-    v += dpp_move<0x114>(v);       // row_shr:4
-    v += dpp_move<0x118>(v);       // row_shr:8
-    v += dpp_move<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-    v += dpp_move<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-    return v;
+// Sums of N values over the 64 lanes; each total lands in lane 63. The N
+// butterflies advance together, one step at a time, so independent DPP adds
+// sit back to back (one butterfly alone needs wait states between its
+// dependent steps).
+template <int N> __device__ __forceinline__ void wave_sums_lane63(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_move<0xB1>(v[i]);        // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x4E>(v[i]);        // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x114>(v[i]);       // row_shr:4
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x118>(v[i]);       // row_shr:8
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x142, 0xA>(v[i]);  // row_bcast:15 into rows 1 and 3
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x143, 0xC>(v[i]);  // row_bcast:31 into rows 2 and 3
 }
 
 // One team processes rows [row_begin, row_begin + rpt) (rows >= O are not
@@ -321,7 +329,14 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
 #pragma unroll
                     for (int g = 0; g < EPC / 4; ++g) {
                         const uint32_t off = min(b4 + st4 * (uint32_t)g, last4);
-                        const float4 t = *reinterpret_cast<const float4 *>(xs + off);
+                        float4 t = *reinterpret_cast<const float4 *>(xs + off);
+                        if (!wave_in) {  // runs past the row (or of a dead slot) are zero
+                            const bool in = live[k] && WQ_XE(k, g) + 4 <= I;
+                            t.x = in ? t.x : 0.0f;
+                            t.y = in ? t.y : 0.0f;
+                            t.z = in ? t.z : 0.0f;
+                            t.w = in ? t.w : 0.0f;
+                        }
                         xr[k][4 * g][s] = t.x;
                         xr[k][4 * g + 1][s] = t.y;
                         xr[k][4 * g + 2][s] = t.z;
@@ -369,7 +384,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int s = 0; s < SMAX; ++s) sxk[k][c][s] = 0.0f;
-    if (wave_in) {
+    // (16-byte activation runs are already zero where they leave the row)
+    if (XV || wave_in) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
 #pragma unroll
@@ -383,7 +399,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                         else sx[field_chain<FMT, SMAX>(e % EPW)][s] += v;
                     }
                 }
-    } else {
+    } else if constexpr (!XV) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
 #pragma unroll
@@ -402,7 +418,8 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
     }
 #undef WQ_XE
 
-    // Partial sums of one row (wave total in lane 63).
+    // This lane's partial sums of one row (reduced over the wave later, for
+    // all rows of a ring pass at once).
     auto row_partials = [&](uint32_t (&b)[KMAX][WPC], const float (&gv)[KMAX], float (&part)[SMAX]) {
         if constexpr (FMT == WQ_F32) {
 #pragma unroll
@@ -462,7 +479,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     t += tc;
                 }
             }
-            part[s] = wave_sum_lane63(t);
+            part[s] = t;
         }
     };
 
@@ -591,6 +608,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             // wave then has no weight load in flight between ring passes
             __builtin_amdgcn_sched_barrier(0);
         }
+        wave_sums_lane63(reinterpret_cast<float(&)[D * SMAX]>(part));
         finish(row_begin + i, part, D, false);
     }
     {
@@ -604,6 +622,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 for (int s = 0; s < SMAX; ++s) part[d][s] = 0.0f;
             }
         }
+        wave_sums_lane63(reinterpret_cast<float(&)[D * SMAX]>(part));
         finish(row_begin + i, part, rpt - i, true);
     }
 }
