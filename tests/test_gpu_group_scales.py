@@ -155,3 +155,14 @@ def test_group_scale_reupload_checks_gs():
         assert ei.value.code == wq.WQ_E_MISMATCH
     finally:
         wq.wq_tensor_free(t)
+
+
+def test_group_scales_split_team_over_several_chunks():
+    """Group-scaled rows are split over one-slot teams; with one wave per CU
+    requested each team's totals pass through several 32-row LDS chunks."""
+    gu.reinit_with_env(WQ_WAVES_PER_CU=1)
+    try:
+        check(I4, 3000, 6144, 1, 128, seed=9500, what="gs-team-chunks")
+        check(I2, 2100, 8192, 2, 256, seed=9510, what="gs-team-chunks")
+    finally:
+        gu.reinit_with_env(WQ_WAVES_PER_CU=None)

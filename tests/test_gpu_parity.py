@@ -369,3 +369,40 @@ def test_deterministic_repeat():
     finally:
         wq.wq_tensor_free(t)
     np.testing.assert_array_equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------------------
+# teams of waves sharing rows, collecting row totals in LDS chunks of 32 rows
+
+# With one wave per CU requested, each team gets many rows, so its totals
+# pass through several chunks, the last one partly filled (and the last team
+# ragged): int2 S=1 (two-wave teams), int4 with 10 KB rows (three-wave teams,
+# 4 slots), int2 S=4 (four-wave teams, ring of 4), int8 S=8 (six-wave teams).
+TEAM_CHUNK_CASES = [(I2, 5000, 8192, 1), (I4, 3001, 20000, 1), (I2, 4000, 8192, 4), (I8, 2000, 3000, 8)]
+
+
+@pytest.mark.parametrize("fmt,O,I,S", TEAM_CHUNK_CASES)
+def test_team_rows_over_several_chunks(fmt, O, I, S):
+    gu.reinit_with_env(WQ_WAVES_PER_CU=1)
+    try:
+        plan = wq.wq_describe_plan(fmt, O, I, S)
+        fields = dict(kv.split("=") for kv in plan.split()[1:])
+        assert plan.startswith("gemv") and int(fields["team"]) > 1 and int(fields["rows_per_team"]) > 32, plan
+        p = synth.ragged(fmt, O, I, S, seed=9100 + fmt * 10 + S)
+        check_problem(p, "team-chunks")
+    finally:
+        gu.reinit_with_env(WQ_WAVES_PER_CU=None)
+
+
+# ---------------------------------------------------------------------------------------
+# S = 1 int4 / int2: codes enter the FMAs as f16 subnormals (code * 2^-24) and
+# the sums are scaled back by 2^24; activations spanning 1e-35 .. 1e35 stay
+# within the bound (tiny products underflow far below its 1e-30 term)
+
+
+@pytest.mark.parametrize("fmt,O,I", [(I4, 300, 6144), (I2, 260, 8192), (I4, 64, 1000)])
+def test_s1_wide_dynamic_range_activations(fmt, O, I):
+    p = synth.ragged(fmt, O, I, 1, seed=9300 + fmt)
+    g = synth.rng(9301 + fmt)
+    p.x = (p.x * np.power(10.0, g.uniform(-35, 35, size=p.x.shape))).astype(np.float32)
+    check_problem(p, "wide-range")
