@@ -577,7 +577,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 }
             }
             cpos += D;
-            if (cpos == kTeamChunk || last) {
+            if (cpos + D > kTeamChunk || last) {  // the chunk holds kTeamChunk / D whole passes
                 __syncthreads();
                 if (wave_in_team == 0) {
                     const int crow0 = row0 + D - cpos;  // first row of the chunk
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     // ring passes of totals, which fit in the same space)
     __shared__ float red[2 * kTeamChunk * kMaxTeam * SMAX + 2 * kTeamChunk];
     static_assert(2 * kMaxTeam * D * SMAX <= 2 * kTeamChunk * kMaxTeam * SMAX, "paired reduction space");
-    static_assert(kTeamChunk % D == 0, "a chunk holds whole ring passes");
+    static_assert(D <= kTeamChunk, "a chunk holds whole ring passes");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int team_in_block = wave / a.team;
@@ -669,17 +669,22 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
 }
 
 // ---- compiled shapes -------------------------------------------------------
-// (fmt, S bucket) -> bytes per lane load, load slots, ring depth.
-// Registers: activations KMAX * (LW/4 * EPW) * SMAX, ring D * KMAX * LW/4.
-#define WQ_SHAPES(X)                                   \
-    X(WQ_F32, 1, 16, 4, 2) X(WQ_F32, 2, 16, 4, 2)      \
-    X(WQ_F32, 4, 16, 4, 2) X(WQ_F32, 8, 16, 2, 2)      \
-    X(WQ_I8, 1, 16, 4, 2) X(WQ_I8, 2, 16, 2, 2)        \
-    X(WQ_I8, 4, 16, 1, 4) X(WQ_I8, 8, 8, 1, 4)         \
-    X(WQ_I4, 1, 16, 4, 2) X(WQ_I4, 2, 16, 1, 2)        \
-    X(WQ_I4, 4, 16, 1, 4) X(WQ_I4, 8, 8, 1, 4)         \
-    X(WQ_I2, 1, 16, 1, 2) X(WQ_I2, 2, 8, 1, 4)         \
-    X(WQ_I2, 4, 8, 1, 4) X(WQ_I2, 8, 4, 1, 4)
+// (fmt, S bucket) -> bytes per lane load, load slots, ring depth of the
+// grouped launch, ring depth and default waves per CU of the single-tensor
+// GEMV. Registers: activations KMAX * (LW/4 * EPW) * SMAX, ring
+// D * KMAX * LW/4. int4 at S = 1 runs one wave per SIMD with a 4-row ring:
+// half the activation staging of 8 waves per CU and enough rows in flight
+// (9.0 us vs 9.6 for dense_gemv); the grouped launches keep 2 rows and 8
+// waves per CU (their expert rows are few per wave).
+#define WQ_SHAPES(X)                                                   \
+    X(WQ_F32, 1, 16, 4, 2, 2, 8) X(WQ_F32, 2, 16, 4, 2, 2, 8)          \
+    X(WQ_F32, 4, 16, 4, 2, 2, 8) X(WQ_F32, 8, 16, 2, 2, 2, 8)          \
+    X(WQ_I8, 1, 16, 4, 2, 2, 8) X(WQ_I8, 2, 16, 2, 2, 2, 8)            \
+    X(WQ_I8, 4, 16, 1, 4, 4, 8) X(WQ_I8, 8, 8, 1, 4, 4, 8)             \
+    X(WQ_I4, 1, 16, 4, 2, 4, 4) X(WQ_I4, 2, 16, 1, 2, 2, 8)            \
+    X(WQ_I4, 4, 16, 1, 4, 4, 8) X(WQ_I4, 8, 8, 1, 4, 4, 8)             \
+    X(WQ_I2, 1, 16, 1, 2, 2, 8) X(WQ_I2, 2, 8, 1, 4, 4, 8)             \
+    X(WQ_I2, 4, 8, 1, 4, 4, 8) X(WQ_I2, 8, 4, 1, 4, 4, 8)
 
 __global__ void relayout_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int fmt, int O,
                                 long rb, long stride, int nfull) {
@@ -716,11 +721,11 @@ int gemv_smax_bucket(int S) {
 }
 
 GemvShape gemv_shape(int fmt, int smax) {
-#define WQ_SHAPE_CASE(F, SM, LW, KM, D) \
-    if (fmt == F && smax == SM) return GemvShape{LW, KM, D};
+#define WQ_SHAPE_CASE(F, SM, LW, KM, D, DG, WG) \
+    if (fmt == F && smax == SM) return GemvShape{LW, KM, D, DG, WG};
     WQ_SHAPES(WQ_SHAPE_CASE)
 #undef WQ_SHAPE_CASE
-    return GemvShape{0, 0, 0};
+    return GemvShape{0, 0, 0, 0, 0};
 }
 
 GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool split) {
@@ -741,11 +746,15 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool
     if (team > kMaxTeam) return p;  // row too long for the register GEMV
     p.team = (int)team;
     p.k = (int)((stride + 64L * p.lw * p.team - 1) / (64L * p.lw * p.team));
-    p.d = ring_depth(sh.kmax, sh.d, p.k);
+    // split (group-scaled tensors) keeps the grouped launch's ring depth and
+    // 8 waves per CU (measured: 11.3 us vs 12.1 for int4 gs=128); the
+    // launch compiles the same depth for them
+    p.d = ring_depth(sh.kmax, split ? sh.d : sh.dg, p.k);
     p.teams_per_block = (p.team == 1) ? 4 : 1;
     p.block = 64 * p.team * p.teams_per_block;
     // teams: enough waves to keep HBM busy, rows per team a multiple of the ring depth
-    const long want_teams = std::max(1L, (long)cus * waves_per_cu / p.team);
+    const int wpc = waves_per_cu > 0 ? waves_per_cu : split ? 8 : sh.wg;
+    const long want_teams = std::max(1L, (long)cus * wpc / p.team);
     long teams = std::min(want_teams, ((long)O + p.d - 1) / p.d);
     long rpt = ((long)O + teams - 1) / teams;
     rpt = (rpt + p.d - 1) / p.d * p.d;
@@ -756,17 +765,20 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool
     return p;
 }
 
-template <int F, int SM, int LW, int KM, int D>
+// D: ring depth of group-scaled tensors (planned as split teams), DG: of
+// the others (the plan's ring depth is the same one, see plan_gemv).
+template <int F, int SM, int LW, int KM, int D, int DG>
 hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStream_t st) {
     // exact slot count: 1..KM; 16-byte activation loads when x allows (xv)
 #define WQ_GO(KS, GS_, PAIR_)                                                                                   \
     do {                                                                                                        \
+        constexpr int RD = ring_depth(KM, GS_ ? D : DG, KS);                                                    \
         if (xv)                                                                                                 \
-            hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), true, GS_, PAIR_>), dim3(p.grid), \
-                               dim3(p.block), 0, st, a);                                                        \
+            hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, RD, true, GS_, PAIR_>), dim3(p.grid), dim3(p.block), \
+                               0, st, a);                                                                       \
         else                                                                                                    \
-            hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, ring_depth(KM, D, KS), false, GS_, PAIR_>),         \
-                               dim3(p.grid), dim3(p.block), 0, st, a);                                          \
+            hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, RD, false, GS_, PAIR_>), dim3(p.grid), dim3(p.block),\
+                               0, st, a);                                                                       \
         return hipGetLastError();                                                                               \
     } while (0)
 #define WQ_K(KS)                                                     \
@@ -790,8 +802,8 @@ hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStrea
 
 hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st) {
     const bool xv = (a.I % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
-#define WQ_LAUNCH_CASE(F, SM, LW, KM, D) \
-    if (p.fmt == F && p.smax == SM) return launch_gemv_k<F, SM, LW, KM, D>(p, a, xv, st);
+#define WQ_LAUNCH_CASE(F, SM, LW, KM, D, DG, WG) \
+    if (p.fmt == F && p.smax == SM) return launch_gemv_k<F, SM, LW, KM, D, DG>(p, a, xv, st);
     WQ_SHAPES(WQ_LAUNCH_CASE)
 #undef WQ_LAUNCH_CASE
     return hipErrorInvalidValue;
@@ -825,7 +837,7 @@ hipError_t launch_grouped_k(const GroupedPlan &p, const GroupedArgs &a, bool xv,
 
 hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, bool pair, int ks,
                           hipStream_t st) {
-#define WQ_GLAUNCH_CASE(F, SM, LW, KM, D) \
+#define WQ_GLAUNCH_CASE(F, SM, LW, KM, D, DG, WG) \
     if (fmt == F && p.smax == SM) return launch_grouped_k<F, SM, LW, KM, D>(p, a, xv, pair, ks, st);
     WQ_SHAPES(WQ_GLAUNCH_CASE)
 #undef WQ_GLAUNCH_CASE

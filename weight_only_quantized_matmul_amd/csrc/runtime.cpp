@@ -42,7 +42,7 @@ struct Config {
     long long mem_limit = 0;  // 0: none
     int fault = 0;            // 0 none, 1 upload, 2 launch
     int verbose = 0;
-    int waves_per_cu = 8;
+    int waves_per_cu = 0;  // 0: per kernel shape (GEMV) / 8 (grouped launches)
     int tiled_mode = wq::kTiledBF16X3;  // quantized weights: exact bf16 split of x
     int tiled_shape = 0;                // 0: by size; else bm * 1000000 + bn * 1000 + bk
 };
@@ -585,7 +585,7 @@ int create_group(wq_tensor *const *ts, wq_tensor *const *ts2, int G, wq_group **
         // k): each launch runs the kernel compiled for exactly its k, whose
         // register count (and so occupancy) is that of its own rows, and
         // splits its own bytes over about waves_per_cu waves per CU.
-        const long target_items = std::max(1L, (long)d.cus * g_cfg.waves_per_cu);
+        const long target_items = std::max(1L, (long)d.cus * (g_cfg.waves_per_cu > 0 ? g_cfg.waves_per_cu : 8));
         std::vector<wq::WorkItem> items;
         for (int c0 = 0; c0 < G; c0 += wq::kGroupMaxPerLaunch) {
             const int c1 = std::min(G, c0 + wq::kGroupMaxPerLaunch);

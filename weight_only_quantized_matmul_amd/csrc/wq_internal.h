@@ -159,10 +159,12 @@ struct GemvArgs {
     const float *scales2 = nullptr;
 };
 
-// Kernel shape for (fmt, S bucket): bytes per lane load, compiled slot count
-// and ring depth. Row coverage per wave = 64 * lw * kmax bytes.
+// Kernel shape for (fmt, S bucket): bytes per lane load, compiled slot count,
+// ring depth of the grouped launch (d) and of the single-tensor GEMV (dg),
+// and the GEMV's default waves per CU (wg). Row coverage per wave =
+// 64 * lw * kmax bytes.
 struct GemvShape {
-    int lw, kmax, d;
+    int lw, kmax, d, dg, wg;
 };
 GemvShape gemv_shape(int fmt, int smax);
 
@@ -177,6 +179,7 @@ int gemv_smax_bucket(int S); // 1,2,4,8 or 0 if S > 8
 
 // split: one load slot per lane, the row shared by as many waves as that
 // needs (when at most kMaxTeam); else up to the shape's slots per lane.
+// waves_per_cu <= 0: the shape's default.
 GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool split = false);
 hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);  // a.gs, a.w2 select the variant
 
