@@ -116,17 +116,30 @@ def test_tiled_plan(fmt, O, I, S):
     kind, p = _plan(fmt, O, I, S)
     assert kind == "tiled"
     assert int(p["tiles_s"]) * int(p["bm"]) >= S and int(p["tiles_o"]) * int(p["bn"]) >= O
-    assert int(p["grid"]) == int(p["tiles_s"]) * int(p["tiles_o"])
+    ks = int(p["ksplit"])
+    assert int(p["grid"]) == int(p["tiles_s"]) * int(p["tiles_o"]) * ks
     # plane rows hold every tile row the kernel reads: bm divides the 128-row padding
     assert 128 % int(p["bm"]) == 0 and 128 % int(p["bk"]) == 0
     if fmt == wq.WQ_F32:
-        assert p["mode"] == "fp32" and p["workspace"] == "0"
+        assert p["mode"] == "fp32" and p["workspace"] == "0" and ks == 1
     else:
         # three bf16 planes of round_up(S, 128) rows by round_up(fields per row, 128)
         stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
         fields = stride * {wq.WQ_I8: 1, wq.WQ_I4: 2, wq.WQ_I2: 4}[fmt]
         assert p["mode"] == "bf16x3"
-        assert int(p["workspace"]) == 3 * (-(-S // 128) * 128) * (-(-fields // 128) * 128) * 2
+        planes = 3 * (-(-S // 128) * 128) * (-(-fields // 128) * 128) * 2
+        if ks == 1:
+            assert int(p["workspace"]) == planes
+        else:  # split K: fp32 partials per chunk after the planes
+            assert int(p["workspace"]) == -(-planes // 256) * 256 + ks * S * O * 4
+
+
+@pytest.mark.parametrize("fmt,O,I,S,ks", [(wq.WQ_I4, 12288, 6144, 8, 3), (wq.WQ_I2, 16384, 8192, 12, 2),
+                                          (wq.WQ_I8, 6144, 6144, 512, 1), (wq.WQ_I4, 100, 200, 9, 1)])
+def test_tiled_split_k_plan(fmt, O, I, S, ks):
+    """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves."""
+    kind, p = _plan(fmt, O, I, S)
+    assert kind == "tiled" and int(p["ksplit"]) == ks, p
 
 
 def test_prefill_plan_uses_large_tiles():

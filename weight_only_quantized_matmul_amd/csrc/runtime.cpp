@@ -225,6 +225,10 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
         int rc = ensure_workspace(d, tp.ws_bytes, st, &ws);
         if (rc != WQ_OK) return rc;
         a.xp = ws;
+        if (tp.ksplit > 1) {
+            a.ksplit = tp.ksplit;
+            a.part = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + tp.part_off);
+        }
     }
     return hip_status(wq::launch_tiled(t->fmt, tp, a, st));
 }
@@ -843,9 +847,10 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
     } else {
         const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S, g_cfg.tiled_mode, g_cfg.tiled_shape);
         snprintf(buf, buflen,
-                 "tiled fmt=%d mode=%s bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d grid=%d block=%d workspace=%zu", fmt,
-                 tp.mode == wq::kTiledBF16X3 ? "bf16x3" : "fp32", tp.bm, tp.bn, tp.bk, tp.tiles_s, tp.tiles_o,
-                 tp.grid, tp.block, tp.ws_bytes);
+                 "tiled fmt=%d mode=%s bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d ksplit=%d grid=%d block=%d "
+                 "workspace=%zu",
+                 fmt, tp.mode == wq::kTiledBF16X3 ? "bf16x3" : "fp32", tp.bm, tp.bn, tp.bk, tp.tiles_s, tp.tiles_o,
+                 tp.ksplit, tp.grid, tp.block, tp.ws_bytes);
     }
     return WQ_OK;
 }

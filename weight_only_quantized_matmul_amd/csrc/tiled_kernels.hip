@@ -48,15 +48,20 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // XCD-aware tile order: block b runs on XCD b % 8; XCD x owns a contiguous
-// range of tiles, walked with s fastest so consecutive tiles share W.
-__device__ __forceinline__ void tile_origin(const TiledArgs &a, int bm, int bn, int &s0, int &o0) {
-    const int nt = a.tiles_s * a.tiles_o;
+// range of work items, walked with the K chunk fastest, then s, so the
+// blocks of one tile (and consecutive tiles, which share W) meet in one L2.
+// Returns the work item's K chunk (0 without split K).
+__device__ __forceinline__ int tile_origin(const TiledArgs &a, int bm, int bn, int &s0, int &o0) {
+    const int ks = a.ksplit;
+    const int nt = a.tiles_s * a.tiles_o * ks;
     const int b = blockIdx.x;
     const int xcd = b & 7, local = b >> 3;
     const int base = nt >> 3, extra = nt & 7;
     const int t = xcd * base + min(xcd, extra) + local;
-    s0 = (t % a.tiles_s) * bm;
-    o0 = (t / a.tiles_s) * bn;
+    const int tile = t / ks;
+    s0 = (tile % a.tiles_s) * bm;
+    o0 = (tile / a.tiles_s) * bn;
+    return t - tile * ks;
 }
 
 // Epilogue: lane holds rows 4*(lane/16) + r, column lane % 16 of each 16x16
@@ -272,6 +277,7 @@ __global__ __launch_bounds__(256) void split_x_kernel(const float *__restrict__ 
                                                       int vec_ok, int sp, int kp, long plane,
                                                       uint16_t *__restrict__ xp) {
     const long t = (long)blockIdx.x * 256 + threadIdx.x;
+
     const int kcs = kp / 32;
     if (t >= (long)sp / 16 * kcs * 64) return;
     const int l = (int)(t & 63), li = l & 15, g = l >> 4;
@@ -409,12 +415,14 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds16[];
 
     int s0, o0;
-    tile_origin(a, BM, BN, s0, o0);
+    const int kc = tile_origin(a, BM, BN, s0, o0);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int nk = a.kp / BK;
+    // this block's K steps [kb, ke) (all of them without split K)
+    const int kb = (int)((long)kc * nk / a.ksplit), ke = (int)((long)(kc + 1) * nk / a.ksplit);
 
     // A fragments of one step: [m][plane][32-position part], lane (li, g)
     // holds row 16m + li, positions 32 * part + 8g .. +8 of the step: one
@@ -471,8 +479,8 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     // data nobody reads).
     f32x4 tacc[WM][WN];  // GS: the current group's sums
     auto iter = [&](int kt, const AFrag &cur, AFrag &nxt, const WSet &wnext, WSet &wload) {
-        const int buf = kt & 1;
-        load_a(min(kt + PD, nk - 1), nxt);
+        const int buf = (kt - kb) & 1;
+        load_a(min(kt + PD, ke - 1), nxt);
         float gsc[WN];
         bool group_ends = false;
         if constexpr (GS) {
@@ -499,7 +507,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
                 bv[n] = *reinterpret_cast<const bf16x8 *>(Bs + (16 * n + li) * LDB + 32 * h + 8 * g);
             if (h == KH / 2) {
                 stash_w(buf ^ 1, wnext);
-                load_w(min(kt + NW, nk - 1), wload);
+                load_w(min(kt + NW, ke - 1), wload);
             }
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl)
@@ -530,34 +538,63 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     AFrag af[PD + 1];
     WSet wg[NW];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) load_w(min(i, nk - 1), wg[i]);
+    for (int i = 0; i < NW; ++i) load_w(min(kb + i, ke - 1), wg[i]);
     stash_w(0, wg[0]);
 #pragma unroll
-    for (int i = 0; i < PD; ++i) load_a(min(i, nk - 1), af[i]);
+    for (int i = 0; i < PD; ++i) load_a(min(kb + i, ke - 1), af[i]);
     __syncthreads();
-    int kt = 0;
-    for (; kt + U <= nk; kt += U) {
+    int kt = kb;
+    for (; kt + U <= ke; kt += U) {
 #pragma unroll
         for (int i = 0; i < U; ++i)
             iter(kt + i, af[i % (PD + 1)], af[(i + PD) % (PD + 1)], wg[(i + 1) % NW], wg[i % NW]);
     }
 #pragma unroll
     for (int i = 0; i + 1 < U; ++i)
-        if (kt + i < nk) iter(kt + i, af[i % (PD + 1)], af[(i + PD) % (PD + 1)], wg[(i + 1) % NW], wg[i % NW]);
+        if (kt + i < ke) iter(kt + i, af[i % (PD + 1)], af[(i + PD) % (PD + 1)], wg[(i + 1) % NW], wg[i % NW]);
 
     // epilogue: lane holds rows 4g + r, column li of each 16x16 fragment
+    if (a.ksplit == 1) {
+#pragma unroll
+        for (int n = 0; n < WN; ++n) {
+            const int o = o0 + 16 * n + li;
+            if (o >= a.O) continue;
+            const float sc = GS ? 1.0f : a.scales[o];
+#pragma unroll
+            for (int m = 0; m < WM; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = s0 + 16 * WM * wave + 16 * m + 4 * g + r;
+                    if (s < a.S) a.y[(long)s * a.O + o] = sc * acc[m][n][r];
+                }
+        }
+        return;
+    }
+    // split K: store this chunk's sums; splitk_sum_kernel adds the chunks
+    const long pstride = (long)a.S * a.O;
 #pragma unroll
     for (int n = 0; n < WN; ++n) {
         const int o = o0 + 16 * n + li;
         if (o >= a.O) continue;
-        const float sc = GS ? 1.0f : a.scales[o];
 #pragma unroll
         for (int m = 0; m < WM; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = s0 + 16 * WM * wave + 16 * m + 4 * g + r;
-                if (s < a.S) a.y[(long)s * a.O + o] = sc * acc[m][n][r];
+                if (s < a.S) a.part[kc * pstride + (long)s * a.O + o] = acc[m][n][r];
             }
+    }
+}
+
+// Split K: y[s][o] = scale[o] * (sum over chunks c = 0.. of part[c][s][o]),
+// the chunks added in order (deterministic; exact partial sums stay exact).
+// Runs after the tiled kernel on the same stream.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ part, int ks, long n, int O,
+                                                         const float *__restrict__ scales, float *__restrict__ y) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+        float t = 0.0f;
+        for (int c = 0; c < ks; ++c) t += part[c * n + i];
+        y[i] = scales[i % O] * t;
     }
 }
 
@@ -597,6 +634,11 @@ hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW, GS>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES,
                        st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.ksplit == 1) return e;
+    const long n = (long)a.S * a.O;
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)std::min<long>((n + 255) / 256, 4096)), dim3(256), 0, st,
+                       a.part, a.ksplit, n, a.O, a.scales, a.y);
     return hipGetLastError();
 }
 
@@ -662,6 +704,21 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         p.kp = (int)round_up(npos, kTiledKAlign);
         p.sp = (int)round_up(S, kTiledSAlign);
         p.ws_bytes = (size_t)3 * p.sp * p.kp * sizeof(uint16_t);
+        // Split K when the tiles alone leave the chip short of blocks (few
+        // activation rows): each K chunk of at least kTiledMinChunk steps
+        // becomes a block of its own. Group-scaled tensors keep whole rows.
+        const int nk = p.kp / p.bk;
+        const int waves = p.grid * (p.block / 64);
+        if (gs == 0 && waves < kTiledSplitWaves && nk >= 2 * kTiledMinChunk) {
+            int ks = (kTiledSplitWaves + waves - 1) / waves;
+            ks = std::min(ks, nk / kTiledMinChunk);
+            if (ks > 1 && (long)ks * S * O <= (long)INT_MAX) {
+                p.ksplit = ks;
+                p.grid *= ks;
+                p.part_off = round_up((long)p.ws_bytes, 256);
+                p.ws_bytes = p.part_off + (size_t)ks * S * O * sizeof(float);
+            }
+        }
     }
     return p;
 }

@@ -246,6 +246,11 @@ struct TiledArgs {
     const uint16_t *xp;
     long plane;  // bf16 elements per plane (sp * kp)
     int kp;      // bf16 elements per plane row
+    // split K (bf16x3, ksplit > 1): block (tile, c) sums K steps
+    // [c * nk / ksplit, (c + 1) * nk / ksplit) into part[c][S][O]; a
+    // second kernel adds the ksplit partials in order c = 0.. and writes y
+    int ksplit = 1;
+    float *part = nullptr;
 };
 
 constexpr int kTiledF32 = 0;     // fp32 operands, v_mfma_f32_16x16x4_f32
@@ -258,8 +263,12 @@ struct TiledPlan {
     int bm = 64, bn = 64, bk = 32;
     int tiles_s = 0, tiles_o = 0, grid = 0, block = 256;
     int sp = 0, kp = 0;   // bf16x3: plane rows and row length
-    size_t ws_bytes = 0;  // device workspace the call needs (bf16x3: 3 planes)
+    int ksplit = 1;       // bf16x3: K chunks per tile (grid = tiles * ksplit)
+    size_t part_off = 0;  // split K: byte offset of the partials in the workspace
+    size_t ws_bytes = 0;  // device workspace the call needs (bf16x3: 3 planes [+ partials])
 };
+constexpr int kTiledSplitWaves = 2048;  // split K until the grid holds this many waves (8 per CU)
+constexpr int kTiledMinChunk = 4;       // K steps per chunk at least
 
 // shape: 0 picks by size; bm * 1000000 + bn * 1000 + bk forces a compiled tile shape
 // gs > 0 (group-wise scales) always takes the bf16x3 mode
