@@ -263,10 +263,12 @@ def main():
         per_launch = e0.elapsed_time(e1) / 1e3 / K
 
     plans = [wq.wq_describe_plan(p.fmt, p.O, p.I, p.S) for p in probs]
-    bf16x3 = compute_bound and all("mode=bf16x3" in pl for pl in plans)
-    if compute_bound:
-        value = alg_flops * K / wall / 1e9
-        unit = "GFLOP/s"
+    tiled = all(pl.startswith("tiled") for pl in plans)
+    bf16x3 = tiled and all("mode=bf16x3" in pl for pl in plans)
+    if compute_bound or tiled:
+        # (int2 at S = 8 also runs on the tiled MFMA path; its value stays GB/s)
+        value = alg_flops * K / wall / 1e9 if compute_bound else weight_bytes * K / wall / 1e9
+        unit = "GFLOP/s" if compute_bound else "GB/s"
         # The contraction runs on the matrix type of its mode: fp32 MFMA, or
         # bf16 MFMA on three exact bf16 parts of every activation (three
         # matrix products per algorithmic product, so frac <= 1/3 there).
@@ -275,10 +277,13 @@ def main():
                 "peak": BF16_MFMA_PEAK_TFLOPS if bf16x3 else FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
         if bf16x3:
             roof["issued_mfma_flops_per_launch"] = 3.0 * alg_flops
+        if not compute_bound:
+            roof["hbm_achieved_gbs"] = alg_bytes / per_launch / 1e9
     elif args.workload in ("int2_gemv_s4", "int2_gemv_s8"):
-        # int2 with S >= 4 activation rows: S fp32 FMAs per 0.25-byte weight
-        # element bind the vector ALUs before HBM (packed fp32 FMAs are not
-        # used), so the roofline is the vector FMA rate; HBM rate alongside.
+        # int2 with S >= 4 activation rows on the register GEMV: S fp32 FMAs
+        # per 0.25-byte weight element bind the vector ALUs before HBM (packed
+        # fp32 FMAs are not used), so the roofline is the vector FMA rate;
+        # HBM rate alongside.
         value = weight_bytes * K / wall / 1e9
         unit = "GB/s"
         roof = {"bound": "alu", "achieved": alg_flops / per_launch / 1e12, "peak": FP32_VALU_FMA_PEAK_TFLOPS,

@@ -85,8 +85,9 @@ def _plan(fmt, O, I, S):
 
 @pytest.mark.parametrize("fmt,O,I,S", [
     (wq.WQ_I4, 12288, 6144, 1), (wq.WQ_I2, 16384, 8192, 1), (wq.WQ_I2, 16384, 8192, 4),
-    (wq.WQ_I2, 16384, 8192, 8), (wq.WQ_I4, 2048, 6144, 1), (wq.WQ_I4, 6144, 2048, 1),
-    (wq.WQ_I8, 256, 512, 1), (wq.WQ_F32, 256, 512, 1), (wq.WQ_I4, 256, 512, 3), (wq.WQ_I2, 256, 512, 8),
+    (wq.WQ_I2, 16384, 8192, 2), (wq.WQ_I4, 2048, 6144, 1), (wq.WQ_I4, 6144, 2048, 1),
+    (wq.WQ_I8, 256, 512, 1), (wq.WQ_F32, 256, 512, 1), (wq.WQ_I4, 256, 512, 3), (wq.WQ_I2, 256, 512, 4),
+    (wq.WQ_I8, 256, 512, 8),
     (wq.WQ_I8, 7, 33, 5), (wq.WQ_F32, 1, 1, 1), (wq.WQ_I2, 3, 5, 2), (wq.WQ_F32, 100, 3000, 8),
 ])
 def test_gemv_plan_invariants(fmt, O, I, S):
@@ -134,12 +135,15 @@ def test_tiled_plan(fmt, O, I, S):
             assert int(p["workspace"]) == -(-planes // 256) * 256 + ks * S * O * 4
 
 
-@pytest.mark.parametrize("fmt,O,I,S,ks", [(wq.WQ_I4, 12288, 6144, 8, 3), (wq.WQ_I2, 16384, 8192, 12, 2),
+@pytest.mark.parametrize("fmt,O,I,S,ks", [(wq.WQ_I4, 12288, 6144, 8, 11), (wq.WQ_I2, 16384, 8192, 12, 8),
+                                          (wq.WQ_I4, 12288, 6144, 32, 3),
                                           (wq.WQ_I8, 6144, 6144, 512, 1), (wq.WQ_I4, 100, 200, 9, 1)])
 def test_tiled_split_k_plan(fmt, O, I, S, ks):
     """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves."""
     kind, p = _plan(fmt, O, I, S)
     assert kind == "tiled" and int(p["ksplit"]) == ks, p
+    if S <= 16 and fmt != wq.WQ_F32:  # one wave per 16 x 64 tile
+        assert (p["bm"], p["bn"], p["block"]) == ("16", "64", "64"), p
 
 
 def test_prefill_plan_uses_large_tiles():
@@ -212,9 +216,10 @@ def test_init_without_gpu_reports_nodev():
 
 
 @pytest.mark.parametrize("fmt,S,kind", [(wq.WQ_I4, 4, "gemv"), (wq.WQ_I4, 5, "tiled"), (wq.WQ_I4, 8, "tiled"),
-                                        (wq.WQ_I8, 8, "gemv"), (wq.WQ_I2, 8, "gemv"), (wq.WQ_F32, 8, "gemv")])
+                                        (wq.WQ_I2, 4, "gemv"), (wq.WQ_I2, 5, "tiled"), (wq.WQ_I2, 8, "tiled"),
+                                        (wq.WQ_I8, 8, "gemv"), (wq.WQ_F32, 8, "gemv")])
 def test_default_gemv_limit_per_format(fmt, S, kind):
-    """int4 leaves the register GEMV above S = 4; the other formats stay on it up to S = 8."""
+    """int4 and int2 leave the register GEMV above S = 4; int8 and f32 stay on it up to S = 8."""
     assert _plan(fmt, 4096, 2048, S)[0] == kind
 
 

@@ -127,12 +127,14 @@ void dev_free(DeviceCtx &d, void *p, size_t bytes) {
     }
 }
 
-// Largest S served by the register GEMV. int4 at S >= 5 runs faster on the
-// tiled MFMA path (measured, 12288 x 6144: S = 8 took 79 us on the GEMV and
-// 56 us tiled); other formats keep the GEMV up to S = 8.
+// Largest S served by the register GEMV. int4 and int2 at S >= 5 run faster
+// on the tiled MFMA path (measured at S = 8: int4 12288 x 6144 72.8 us on the
+// GEMV, 42.1 us tiled; int2 16384 x 8192 59.5 us GEMV, 50.8 us tiled; at
+// S = 4 the GEMV wins, 26.7 / 27.0 us against 41-50 us); int8 and f32 keep
+// the GEMV up to S = 8.
 int gemv_limit(int fmt) {
     if (g_cfg.gemv_max_s >= 0) return g_cfg.gemv_max_s;
-    return fmt == WQ_I4 ? 4 : WQ_GEMV_MAX_S;
+    return (fmt == WQ_I4 || fmt == WQ_I2) ? 4 : WQ_GEMV_MAX_S;
 }
 
 // Which path a call takes. Returns 1 (gemv) or 2 (tiled).
