@@ -135,15 +135,15 @@ def test_tiled_plan(fmt, O, I, S):
             assert int(p["workspace"]) == -(-planes // 256) * 256 + ks * S * O * 4
 
 
-@pytest.mark.parametrize("fmt,O,I,S,ks", [(wq.WQ_I4, 12288, 6144, 8, 11), (wq.WQ_I2, 16384, 8192, 12, 8),
+@pytest.mark.parametrize("fmt,O,I,S,ks", [(wq.WQ_I4, 12288, 6144, 8, 6), (wq.WQ_I2, 16384, 8192, 12, 4),
                                           (wq.WQ_I4, 12288, 6144, 32, 3),
                                           (wq.WQ_I8, 6144, 6144, 512, 1), (wq.WQ_I4, 100, 200, 9, 1)])
 def test_tiled_split_k_plan(fmt, O, I, S, ks):
     """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves."""
     kind, p = _plan(fmt, O, I, S)
     assert kind == "tiled" and int(p["ksplit"]) == ks, p
-    if S <= 16 and fmt != wq.WQ_F32:  # one wave per 16 x 64 tile
-        assert (p["bm"], p["bn"], p["block"]) == ("16", "64", "64"), p
+    if S <= 16 and fmt != wq.WQ_F32:  # one wave per 16 x 32 tile
+        assert (p["bm"], p["bn"], p["block"]) == ("16", "32", "64"), p
 
 
 def test_prefill_plan_uses_large_tiles():
