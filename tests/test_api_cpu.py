@@ -124,11 +124,12 @@ def test_tiled_plan(fmt, O, I, S):
     if fmt == wq.WQ_F32:
         assert p["mode"] == "fp32" and p["workspace"] == "0" and ks == 1
     else:
-        # three bf16 planes of round_up(S, 128) rows by round_up(fields per row, 128)
+        # three bf16 planes of round_up(S, 128) rows (16 for the 16-row tile) by round_up(fields per row, 128)
         stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
         fields = stride * {wq.WQ_I8: 1, wq.WQ_I4: 2, wq.WQ_I2: 4}[fmt]
         assert p["mode"] == "bf16x3"
-        planes = 3 * (-(-S // 128) * 128) * (-(-fields // 128) * 128) * 2
+        sp_align = 16 if p["bm"] == "16" else 128
+        planes = 3 * (-(-S // sp_align) * sp_align) * (-(-fields // 128) * 128) * 2
         if ks == 1:
             assert int(p["workspace"]) == planes
         else:  # split K: fp32 partials per chunk after the planes

@@ -708,7 +708,9 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         const long stride = round_up(row_bytes(fmt, I), kRowAlign);
         const long npos = stride * elems_per_byte(fmt);
         p.kp = (int)round_up(npos, kTiledKAlign);
-        p.sp = (int)round_up(S, kTiledSAlign);
+        // plane rows: the 16-row tile reads 16-row blocks only; the larger
+        // tiles read up to 128-row multiples
+        p.sp = (int)round_up(S, p.bm == 16 ? 16 : kTiledSAlign);
         p.ws_bytes = (size_t)3 * p.sp * p.kp * sizeof(uint16_t);
         // Split K when the tiles alone leave the chip short of blocks (few
         // activation rows): each K chunk of at least kTiledMinChunk steps
