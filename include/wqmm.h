@@ -48,7 +48,7 @@ extern "C" {
 #endif
 
 #define WQ_MAX_DEVICES 16   /* size of the static device table */
-#define WQ_GEMV_MAX_S 8     /* largest S the register GEMV serves (by default 4 for int4, which is faster on the tiled path above that) */
+#define WQ_GEMV_MAX_S 8     /* largest S the register GEMV serves (by default 4 for int4 and int2, which are faster on the tiled path above that) */
 
 enum wq_fmt { WQ_F32 = 0, WQ_I8 = 1, WQ_I4 = 2, WQ_I2 = 3 };
 
@@ -151,7 +151,9 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
  * S <= the GEMV limit: one kernel launch, no workspace. Larger S with a
  * quantized format (tiled path, bf16x3 mode): two launches that use the
  * device's workspace (3 * round_up(S, 128) * round_up(fields per row, 128)
- * bf16 values; wq_describe_plan prints the size). The workspace grows on
+ * bf16 values, 16-row padding for S <= 16; when K is split across blocks,
+ * a third launch adds ksplit * S * O fp32 partials kept after them;
+ * wq_describe_plan prints the size). The workspace grows on
  * demand: growth waits for the device to go idle and allocates; a call being
  * captured into a HIP graph never grows it and returns WQ_E_UNSUPPORTED
  * instead, so run the largest S once before capturing. The workspace is
@@ -240,7 +242,8 @@ const char *wq_strerror(int code);
 /*
  * Introspection for tests and tools: the kernel path wq_matmul_dev would take
  * for (fmt, O, I, S) on this build, written as a NUL-terminated string into
- * buf (e.g. "gemv fmt=2 smax=1 lw=16 k=3 team=1 r=2 grid=512 block=256").
+ * buf (e.g. "gemv fmt=2 smax=1 lw=16 kmax=4 k=3 team=1 d=4 rows_per_team=12 grid=256 block=256",
+ * or "tiled fmt=3 mode=bf16x3 bm=16 bn=32 bk=64 tiles_s=1 tiles_o=512 ksplit=4 grid=2048 block=64 workspace=...").
  * Host-only: needs no device. Returns WQ_OK or WQ_E_INVAL.
  */
 int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen);
