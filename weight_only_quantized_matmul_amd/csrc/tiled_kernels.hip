@@ -598,6 +598,180 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
     }
 }
 
+// bf16x3 tile for few activation rows (S <= 16): the block's WAVES waves
+// sit side by side along o. The block's 16 activation rows are shared: each
+// K step's fragments (3 planes x 2 halves x 64 lanes x 16 bytes) are loaded
+// once per block and staged in LDS next to the weight tile, instead of
+// every wave loading them itself (which made the activation stream ~12x the
+// int2 weight bytes). Wave w owns columns [16 WN w, 16 WN (w + 1)) of the
+// block's BN = 16 WN WAVES. K steps of 64 positions.
+template <int WAVES, int WN>
+struct X3OCfg {
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BM = 16, BN = 16 * WN * WAVES, BK = 64, KH = 2;
+    static constexpr int LDB = BK + 16;
+    static constexpr int CH = BK / 8;
+    static constexpr int WU = (BN * CH + THREADS - 1) / THREADS;
+    static constexpr int BROWS = WU * THREADS / CH;
+    static constexpr int WSTAGE = BROWS * LDB;                // bf16 per weight stage
+    static constexpr int ACH = 3 * KH * 64;                   // 16-byte activation chunks per step
+    static constexpr int AU = (ACH + THREADS - 1) / THREADS;  // per thread
+    static constexpr int STAGE = WSTAGE + ACH * 8;            // bf16 per stage (weights, then activations)
+    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static_assert((WU * THREADS) % CH == 0 && BROWS >= BN, "weight chunks must fill whole rows");
+    static_assert(kTiledKAlign % BK == 0 && ((LDB * 2 / 32) & 1) == 1, "K step and LDS row stride");
+};
+
+template <int FMT, int WAVES, int WN, int NW, bool GS>
+__global__ __launch_bounds__(64 * WAVES) void tiled_x3o_kernel(TiledArgs a) {
+    using C = X3OCfg<WAVES, WN>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LDB = C::LDB, CH = C::CH, KH = C::KH;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds16[];
+
+    int s0, o0;
+    const int kc = tile_origin(a, BM, BN, s0, o0);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int nk = a.kp / BK;
+    const int kb = (int)((long)kc * nk / a.ksplit), ke = (int)((long)(kc + 1) * nk / a.ksplit);
+
+    // activation chunk c of step kt: plane c / 128, half (c / 64) % 2, lane slot c % 64
+    const int kcs = a.kp / 32;
+    const uint16_t *ab = a.xp + (long)(s0 / 16) * kcs * 512;
+    typedef u32x4 ARaw[C::AU];
+    auto load_a = [&](int kt, ARaw &r) {
+#pragma unroll
+        for (int j = 0; j < C::AU; ++j) {
+            const int c = tid + C::THREADS * j;
+            if (c < C::ACH)
+                r[j] = *reinterpret_cast<const u32x4 *>(ab + (c >> 7) * a.plane +
+                                                        ((long)KH * kt + ((c >> 6) & 1)) * 512 + (c & 63) * 8);
+        }
+    };
+    auto stash_a = [&](int buf, const ARaw &r) {
+        uint16_t *st = lds16 + buf * C::STAGE + C::WSTAGE;
+#pragma unroll
+        for (int j = 0; j < C::AU; ++j) {
+            const int c = tid + C::THREADS * j;
+            if (c < C::ACH) *reinterpret_cast<u32x4 *>(st + c * 8) = r[j];
+        }
+    };
+    typedef RawW<FMT> WSet[C::WU];
+    auto load_w = [&](int kt, WSet &w) {
+        const long k0 = (long)kt * BK;
+#pragma unroll
+        for (int j = 0; j < C::WU; ++j) {
+            const int u = tid + C::THREADS * j;
+            const int row = min(o0 + u / CH, a.O - 1);
+            w[j].load(a.w + (long)row * a.stride, a.stride, k0 + 8 * (u % CH));
+        }
+    };
+    auto stash_w = [&](int buf, const WSet &w) {
+        uint16_t *st = lds16 + buf * C::STAGE;
+#pragma unroll
+        for (int j = 0; j < C::WU; ++j) {
+            const int u = tid + C::THREADS * j;
+            *reinterpret_cast<u32x4 *>(st + (u / CH) * LDB + 8 * (u % CH)) = codes_bf16x8<FMT>(w[j]);
+        }
+    };
+
+    f32x4 acc[WN], tacc[WN];
+#pragma unroll
+    for (int n = 0; n < WN; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Step kt reads stage (kt - kb) & 1 and fills the other one: the weights
+    // of step kt + 1 (set wnext, loaded NW - 1 steps ago) and its
+    // activations (ar, loaded one step ago); then requests the weights of
+    // step kt + NW (into the set just consumed) and the activations of step
+    // kt + 2 (clamped: the last steps reload data nobody reads).
+    ARaw ar;
+    auto iter = [&](int kt, const WSet &wnext, WSet &wload) {
+        const int buf = (kt - kb) & 1;
+        float gsc[WN];
+        bool group_ends = false;
+        if constexpr (GS) {
+            const long first = (long)kt * BK;
+            const int grp = min((int)(first / a.gs), a.ng - 1);
+            group_ends = (first + BK) % a.gs == 0 || kt + 1 == nk;  // wave-uniform
+#pragma unroll
+            for (int n = 0; n < WN; ++n)
+                gsc[n] = a.scales[(long)grp * a.O + min(o0 + 16 * (WN * wave + n) + li, a.O - 1)];
+            if (first % a.gs == 0) {
+#pragma unroll
+                for (int n = 0; n < WN; ++n) tacc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        auto &dst = *(GS ? &tacc : &acc);
+        const uint16_t *Bs = lds16 + buf * C::STAGE;
+        const uint16_t *As = Bs + C::WSTAGE;
+#pragma unroll
+        for (int h = 0; h < KH; ++h) {
+            bf16x8 bv[WN], av[3];
+#pragma unroll
+            for (int n = 0; n < WN; ++n)
+                bv[n] = *reinterpret_cast<const bf16x8 *>(Bs + (16 * (WN * wave + n) + li) * LDB + 32 * h + 8 * g);
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+                av[pl] = *reinterpret_cast<const bf16x8 *>(As + ((pl * KH + h) * 64 + lane) * 8);
+            if (h == KH / 2) {
+                stash_w(buf ^ 1, wnext);
+                stash_a(buf ^ 1, ar);
+                load_w(min(kt + NW, ke - 1), wload);
+                load_a(min(kt + 2, ke - 1), ar);
+            }
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                for (int n = 0; n < WN; ++n)
+                    dst[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[pl], bv[n], dst[n], 0, 0, 0);
+        }
+        if constexpr (GS) {
+            if (group_ends) {
+#pragma unroll
+                for (int n = 0; n < WN; ++n)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[n][r] = fmaf(gsc[n], tacc[n][r], acc[n][r]);
+            }
+        }
+        __syncthreads();
+    };
+
+    WSet wg[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) load_w(min(kb + i, ke - 1), wg[i]);
+    load_a(kb, ar);
+    stash_w(0, wg[0]);
+    stash_a(0, ar);
+    load_a(min(kb + 1, ke - 1), ar);
+    __syncthreads();
+    int kt = kb;
+    for (; kt + NW <= ke; kt += NW) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) iter(kt + i, wg[(i + 1) % NW], wg[i % NW]);
+    }
+#pragma unroll
+    for (int i = 0; i + 1 < NW; ++i)
+        if (kt + i < ke) iter(kt + i, wg[(i + 1) % NW], wg[i % NW]);
+
+    // epilogue: lane holds rows 4g + r, column li of each 16x16 fragment
+    const long pstride = (long)a.S * a.O;
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+        const int o = o0 + 16 * (WN * wave + n) + li;
+        if (o >= a.O) continue;
+        const float sc = (GS || a.ksplit > 1) ? 1.0f : a.scales[o];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = s0 + 4 * g + r;
+            if (s >= a.S) continue;
+            if (a.ksplit == 1) a.y[(long)s * a.O + o] = sc * acc[n][r];
+            else a.part[kc * pstride + (long)s * a.O + o] = acc[n][r];
+        }
+    }
+}
+
 // ===========================================================================
 // launch
 
@@ -642,12 +816,33 @@ hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int FMT, int WAVES, int WN, bool GS = false>
+hipError_t launch_x3o(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
+    using C = X3OCfg<WAVES, WN>;
+    constexpr int NW = kX3WeightSets;
+    static_assert(C::LDS_BYTES <= 64 * 1024, "tile does not fit the default LDS limit");
+    const int vec_ok = ((a.I & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
+    const long slots = (long)p.sp * p.kp / 8;
+    hipLaunchKernelGGL((split_x_kernel<FMT>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st, a.x, a.S,
+                       a.I, a.nfull, vec_ok, p.sp, p.kp, (long)p.sp * p.kp, const_cast<uint16_t *>(a.xp));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((tiled_x3o_kernel<FMT, WAVES, WN, NW, GS>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES, st,
+                       a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.ksplit == 1) return e;
+    const long n = (long)a.S * a.O;
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)std::min<long>((n + 255) / 256, 4096)), dim3(256), 0, st,
+                       a.part, a.ksplit, n, a.O, a.scales, a.y);
+    return hipGetLastError();
+}
+
 // Compiled tile shapes {bm, bn, bk}; the first entry is the large-problem
 // default, the last the small-problem default.
 struct Shape {
     int bm, bn, bk;
 };
-constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 128}, {64, 64, 64}, {16, 32, 64}};
+constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 128}, {64, 64, 64}, {16, 128, 64}};
 constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
 
 template <int FMT>
@@ -655,7 +850,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if constexpr (FMT != WQ_F32) {
         if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: 64-position K steps
             if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true>(p, a, st);
-            if (p.bm == 16) return launch_x3<FMT, 1, 1, 2, 64, kX3ActPrefetch, true>(p, a, st);
+            if (p.bm == 16) return launch_x3o<FMT, 4, 2, true>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true>(p, a, st);
         }
         if (p.mode == kTiledBF16X3) {
@@ -663,7 +858,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
                 if (p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch>(p, a, st);
                 return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch>(p, a, st);
             }
-            if (p.bm == 16) return launch_x3<FMT, 1, 1, 2, 64, kX3ActPrefetch>(p, a, st);
+            if (p.bm == 16) return launch_x3o<FMT, 4, 2>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch>(p, a, st);
         }
     }
@@ -703,7 +898,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
     p.tiles_s = (S + p.bm - 1) / p.bm;
     p.tiles_o = (O + p.bn - 1) / p.bn;
     p.grid = p.tiles_s * p.tiles_o;
-    p.block = (p.mode == kTiledBF16X3 && p.bm == 128) ? 512 : (p.mode == kTiledBF16X3 && p.bm == 16) ? 64 : 256;
+    p.block = (p.mode == kTiledBF16X3 && p.bm == 128) ? 512 : 256;
     if (p.mode == kTiledBF16X3) {
         const long stride = round_up(row_bytes(fmt, I), kRowAlign);
         const long npos = stride * elems_per_byte(fmt);
