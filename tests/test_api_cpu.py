@@ -143,8 +143,8 @@ def test_tiled_split_k_plan(fmt, O, I, S, ks):
     """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves."""
     kind, p = _plan(fmt, O, I, S)
     assert kind == "tiled" and int(p["ksplit"]) == ks, p
-    if S <= 16 and fmt != wq.WQ_F32:  # 16 x 128 tiles of four waves side by side along o
-        assert (p["bm"], p["bn"], p["block"]) == ("16", "128", "256"), p
+    if S <= 16 and fmt != wq.WQ_F32:  # 16 x 128 tiles of eight waves side by side along o
+        assert (p["bm"], p["bn"], p["block"]) == ("16", "128", "512"), p
 
 
 def test_prefill_plan_uses_large_tiles():

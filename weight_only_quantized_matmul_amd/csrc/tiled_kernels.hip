@@ -850,7 +850,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if constexpr (FMT != WQ_F32) {
         if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: 64-position K steps
             if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true>(p, a, st);
-            if (p.bm == 16) return launch_x3o<FMT, 4, 2, true>(p, a, st);
+            if (p.bm == 16) return launch_x3o<FMT, 8, 1, true>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true>(p, a, st);
         }
         if (p.mode == kTiledBF16X3) {
@@ -858,7 +858,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
                 if (p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch>(p, a, st);
                 return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch>(p, a, st);
             }
-            if (p.bm == 16) return launch_x3o<FMT, 4, 2>(p, a, st);
+            if (p.bm == 16) return launch_x3o<FMT, 8, 1>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch>(p, a, st);
         }
     }
@@ -880,10 +880,8 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
     const bool use_big = S >= 128 && big >= 128;
     Shape sh;
     if (p.mode == kTiledBF16X3) {
-        // S <= 16: one wave per 16 x 32 tile (a 4-wave block stacks its
-        // waves along S, so three of them would multiply zero rows; 32
-        // columns measured faster than 16, 64 or 128: fewer registers, more
-        // waves per CU)
+        // S <= 16: 16 x 128 tiles of eight waves side by side along o,
+        // sharing the activation fragments (tiled_x3o_kernel)
         sh = use_big ? kX3Shapes[0] : S <= 16 ? kX3Shapes[3] : kX3Shapes[2];
         for (const Shape &c : kX3Shapes)
             if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign)) sh = c;
@@ -898,7 +896,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
     p.tiles_s = (S + p.bm - 1) / p.bm;
     p.tiles_o = (O + p.bn - 1) / p.bn;
     p.grid = p.tiles_s * p.tiles_o;
-    p.block = (p.mode == kTiledBF16X3 && p.bm == 128) ? 512 : 256;
+    p.block = (p.mode == kTiledBF16X3 && (p.bm == 128 || p.bm == 16)) ? 512 : 256;
     if (p.mode == kTiledBF16X3) {
         const long stride = round_up(row_bytes(fmt, I), kRowAlign);
         const long npos = stride * elems_per_byte(fmt);
@@ -911,9 +909,12 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         // activation rows): each K chunk of at least kTiledMinChunk steps
         // becomes a block of its own. Group-scaled tensors keep whole rows.
         const int nk = p.kp / p.bk;
+        // (the 16-row tile's eight waves share one activation stage: it takes
+        // twice the waves, measured 3-5 % faster than four-wave blocks)
         const int waves = p.grid * (p.block / 64);
-        if (gs == 0 && waves < kTiledSplitWaves && nk >= 2 * kTiledMinChunk) {
-            int ks = (kTiledSplitWaves + waves - 1) / waves;
+        const int target = p.bm == 16 ? 2 * kTiledSplitWaves : kTiledSplitWaves;
+        if (gs == 0 && waves < target && nk >= 2 * kTiledMinChunk) {
+            int ks = (target + waves - 1) / waves;
             ks = std::min(ks, nk / kTiledMinChunk);
             if (ks > 1 && (long)ks * S * O <= (long)INT_MAX) {
                 p.ksplit = ks;
