@@ -35,6 +35,12 @@
 //    b1*q + b2*q + b3*q in fp32 with every product exact: fp32-level
 //    results at the bf16 matrix rate, and the split is done once per
 //    activation instead of once per output tile.
+//
+// Few activation rows (S <= 16, bf16x3): 16 x 128 tiles whose eight waves
+// sit side by side along o and share each K step's activation fragments
+// through LDS (tiled_x3o_kernel). When the tiles alone leave the chip short
+// of waves, K is split across blocks: each stores fp32 partials and a small
+// kernel adds them in fixed order (splitk_sum_kernel).
 #include <climits>
 
 #include "wq_internal.h"
