@@ -72,6 +72,22 @@ def matmul_exact(fmt: int, w: np.ndarray, scales, x: np.ndarray, I: int):
     return out
 
 
+def bound_exact(fmt: int, w: np.ndarray, scales, x: np.ndarray, I: int):
+    """Exact A[s,o] = sum_i |scale[o] * q[o,i] * x[s,i]| (Fractions), the magnitude the
+    acceptance bound 1e-5 * A + 1e-30 is stated against; written term by term
+    from the same bit-stream codes, independently of the oracle."""
+    O = w.shape[0]
+    S = x.shape[0]
+    xs = [[Fraction(float(v)) for v in x[s]] for s in range(S)]
+    out = [[None] * O for _ in range(S)]
+    for o in range(O):
+        q = codes(fmt, w[o].tobytes(), I)
+        sc = Fraction(1) if scales is None else Fraction(float(scales[o]))
+        for s in range(S):
+            out[s][o] = sum((abs(sc * q[i] * xs[s][i]) for i in range(I)), Fraction(0))
+    return out
+
+
 def matmul_rounded(fmt: int, w, scales, x, I: int) -> np.ndarray:
     ex = matmul_exact(fmt, w, scales, x, I)
     return np.array([[round_to_f32(v) for v in row] for row in ex], dtype=np.float32)
@@ -88,6 +104,20 @@ def matmul_gs_exact(fmt: int, w: np.ndarray, gscales: np.ndarray, gs: int, x: np
         sc = [Fraction(float(v)) for v in gscales[o]]
         for s in range(S):
             out[s][o] = sum((sc[i // gs] * q[i] * xs[s][i] for i in range(I)), Fraction(0))
+    return out
+
+
+def bound_gs_exact(fmt: int, w: np.ndarray, gscales: np.ndarray, gs: int, x: np.ndarray, I: int):
+    """Exact A[s,o] = sum_i |gscales[o, i // gs] * q[o,i] * x[s,i]| (Fractions)."""
+    O = w.shape[0]
+    S = x.shape[0]
+    xs = [[Fraction(float(v)) for v in x[s]] for s in range(S)]
+    out = [[None] * O for _ in range(S)]
+    for o in range(O):
+        q = codes(fmt, w[o].tobytes(), I)
+        sc = [Fraction(float(v)) for v in gscales[o]]
+        for s in range(S):
+            out[s][o] = sum((abs(sc[i // gs] * q[i] * xs[s][i]) for i in range(I)), Fraction(0))
     return out
 
 

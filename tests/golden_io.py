@@ -25,7 +25,8 @@ def dequant_table():
 
 
 def worked_examples():
-    """List of dicts: name, fmt, O, I, S, w (uint8 [O, rb]), scales (or None), x, y."""
+    """List of dicts: name, fmt, O, I, S, w (uint8 [O, rb]), scales (or None), x, y and
+    A (the bound magnitude sum_i |scale * q * x|, float64 [S, O])."""
     cases, cur = [], None
     with open(os.path.join(GOLDEN, "worked_examples.txt")) as f:
         for line in f:
@@ -34,11 +35,12 @@ def worked_examples():
                 continue
             key, _, rest = line.partition(" ")
             if key == "case":
-                cur = {"name": rest, "w": [], "x": [], "y": []}
+                cur = {"name": rest, "w": [], "x": [], "y": [], "A": []}
             elif key == "end":
                 cur["w"] = np.array([list(bytes.fromhex(h)) for h in cur["w"]], dtype=np.uint8)
                 cur["x"] = np.array(cur["x"], dtype=np.float32)
                 cur["y"] = np.array(cur["y"], dtype=np.float32)
+                cur["A"] = np.array(cur["A"], dtype=np.float64)
                 cases.append(cur)
                 cur = None
             elif key == "fmt":
@@ -50,7 +52,7 @@ def worked_examples():
             elif key == "scales":
                 cur["scales"] = None if rest == "none" else np.array(
                     [float(v) for v in rest.split()], dtype=np.float32)
-            elif key in ("x", "y"):
+            elif key in ("x", "y", "A"):
                 cur[key].append([float(v) for v in rest.split()])
             else:
                 raise ValueError("bad fixture line: %r" % line)
@@ -67,11 +69,12 @@ def group_scale_examples():
                 continue
             key, _, rest = line.partition(" ")
             if key == "case":
-                cur = {"name": rest, "w": [], "x": [], "y": [], "gscales": []}
+                cur = {"name": rest, "w": [], "x": [], "y": [], "A": [], "gscales": []}
             elif key == "end":
                 cur["w"] = np.array([list(bytes.fromhex(h)) for h in cur["w"]], dtype=np.uint8)
                 cur["x"] = np.array(cur["x"], dtype=np.float32)
                 cur["y"] = np.array(cur["y"], dtype=np.float32)
+                cur["A"] = np.array(cur["A"], dtype=np.float64)
                 cur["gscales"] = np.array(cur["gscales"], dtype=np.float32)
                 cases.append(cur)
                 cur = None
@@ -83,7 +86,7 @@ def group_scale_examples():
                 cur["w"].append(rest)
             elif key == "gscales":
                 cur["gscales"].append([float(v) for v in rest.split()])
-            elif key in ("x", "y"):
+            elif key in ("x", "y", "A"):
                 cur[key].append([float(v) for v in rest.split()])
             else:
                 raise ValueError("bad fixture line: %r" % line)

@@ -12,6 +12,8 @@ description, colibri "第 8 章 · 02 CUDA/Metal/Vulkan 三后端", section 三)
 """
 from __future__ import annotations
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -39,9 +41,11 @@ def gscales(g, O, I, gs, lo=0.001, hi=0.05):
 def test_group_scale_worked_examples(case):
     y, a = oracle.matmul_gs(case["fmt"], case["w"], case["gscales"], case["gs"], case["x"], I=case["I"])
     np.testing.assert_array_equal(y, case["y"])
-    assert np.all(a >= np.abs(y))
+    np.testing.assert_array_equal(a, case["A"])  # hand-worked bound magnitudes (exact)
     yb = brute.matmul_gs_rounded(case["fmt"], case["w"], case["gscales"], case["gs"], case["x"], case["I"])
     np.testing.assert_array_equal(yb, case["y"])
+    ab = brute.bound_gs_exact(case["fmt"], case["w"], case["gscales"], case["gs"], case["x"], case["I"])
+    np.testing.assert_array_equal(np.array([[float(v) for v in r] for r in ab]), case["A"])
 
 
 @pytest.mark.parametrize("fmt", QUANT + (F32,))
@@ -53,11 +57,18 @@ def test_group_scale_brute_force(fmt, shape, gs):
     w = synth.weights(g, fmt, O, I)
     sc = gscales(g, O, I, gs)
     x = synth.activations(g, S, I)
-    y, _ = oracle.matmul_gs(fmt, w, sc, gs, x)
+    y, a = oracle.matmul_gs(fmt, w, sc, gs, x)
     yb = brute.matmul_gs_rounded(fmt, w, sc, gs, x, I)
     d = ulp_diff(y, yb)
     assert d.max() <= 1.0, d.max()
     assert np.mean(d == 0) >= 0.8
+    # the bound magnitude against exact rationals (n exact terms summed in double)
+    ab = brute.bound_gs_exact(fmt, w, sc, gs, x, I)
+    for s_ in range(S):
+        for o in range(O):
+            v = ab[s_][o]
+            err = abs(Fraction(float(a[s_, o])) - v)
+            assert (err == 0) if v == 0 else float(err / v) <= 1e-12, (s_, o)
 
 
 @pytest.mark.parametrize("fmt", QUANT)

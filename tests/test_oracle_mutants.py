@@ -34,6 +34,12 @@ MUTANTS = {
     "f32_byte_offset": ("memcpy(&f, row + 4 * i, sizeof f);", "memcpy(&f, row + 2 * i, sizeof f);"),
     "sign_flipped": ("acc += t;", "acc -= t;"),
     "sum_in_float": ("double acc = 0.0, mag = 0.0;", "float acc = 0.0f; double mag = 0.0;"),
+    # bound magnitude A (every parity tolerance is 1e-5 * A + 1e-30)
+    "bound_times_100": ("absb[s * O + o] = mag * fabs(scale);", "absb[s * O + o] = 100.0 * mag * fabs(scale);"),
+    "bound_signed_sum": ("mag += fabs(t);", "mag += t;"),
+    "bound_scale_dropped": ("absb[s * O + o] = mag * fabs(scale);", "absb[s * O + o] = mag;"),
+    "gs_bound_times_100": ("absb[s * O + o] = magnitude;", "absb[s * O + o] = 100.0 * magnitude;"),
+    "gs_bound_signed_sum": ("group_mag += fabs(prod);", "group_mag += prod;"),
     # group-wise scales
     "gs_group_shifted": ("long first = g * gs, end", "long first = g * gs + 1, end"),
     "gs_scales_transposed": ("const float *srow = scales + o * ng;", "const float *srow = scales + o;"),

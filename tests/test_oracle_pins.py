@@ -10,6 +10,8 @@
 """
 from __future__ import annotations
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -55,9 +57,11 @@ def test_packer_reproduces_table(case):
 def test_worked_examples(case):
     y, a = oracle.matmul(case["fmt"], case["w"], case["scales"], case["x"], I=case["I"])
     np.testing.assert_array_equal(y, case["y"])
-    assert np.all(a >= np.abs(y))
+    np.testing.assert_array_equal(a, case["A"])  # hand-worked bound magnitudes (exact)
     yb = brute.matmul_rounded(case["fmt"], case["w"], case["scales"], case["x"], case["I"])
     np.testing.assert_array_equal(yb, case["y"])
+    ab = brute.bound_exact(case["fmt"], case["w"], case["scales"], case["x"], case["I"])
+    np.testing.assert_array_equal(np.array([[float(v) for v in r] for r in ab]), case["A"])
 
 
 # --------------------------------------------------------------------------------------
@@ -77,6 +81,51 @@ def test_brute_force(fmt, shape):
     d = ulp_diff(y, yb)
     assert d.max() <= 1.0, d.max()
     assert np.mean(d == 0) >= 0.9
+
+
+def rel_to_exact(a: np.ndarray, exact) -> float:
+    """Largest |a - exact| / exact over the entries (0 where both are 0)."""
+    worst = 0.0
+    for s, row in enumerate(exact):
+        for o, v in enumerate(row):
+            d = abs(Fraction(float(a[s, o])) - v)
+            if v == 0:
+                assert d == 0, (s, o, float(a[s, o]))
+            else:
+                worst = max(worst, float(d / v))
+    return worst
+
+
+@pytest.mark.parametrize("fmt", ALL)
+@pytest.mark.parametrize("shape", [(3, 7, 1), (5, 16, 2), (8, 33, 3), (2, 64, 1)])
+def test_bound_magnitude_brute_force(fmt, shape):
+    """A = sum_i |scale q x| against exact rationals: every parity tolerance is 1e-5 * A + 1e-30,
+    so A itself needs a pin. The oracle sums |q x| in double (n terms, each exact): relative
+    error <= n * 2^-53, far inside 1e-12."""
+    O, I, S = shape
+    g = synth.rng(1000 + 10 * fmt + O)
+    w = synth.weights(g, fmt, O, I)
+    sc = synth.scales(g, O, 0.001, 0.05)
+    x = synth.activations(g, S, I)
+    _, a = oracle.matmul(fmt, w, sc, x)
+    assert rel_to_exact(a, brute.bound_exact(fmt, w, sc, x, I)) <= 1e-12
+
+
+def test_bound_magnitude_signs_and_zero_codes():
+    """Mixed signs in q, x and the scale (a negative scale is |scale|): A is the sum of the
+    magnitudes, not the magnitude of the sum; zero-point codes add nothing to it."""
+    vals = np.array([[-2, 1, 0, -1, 1, 0, -2, 1], [0, 0, 0, 0, 0, 0, 0, 1]])
+    x = np.array([[1.5, -2.0, 7.0, 0.25, -4.0, 3.0, -0.5, 1.0]], np.float32)
+    for fmt in (I8, I4, I2):
+        w = packing.pack(fmt, vals)
+        sc = np.array([-0.5, 2.0], np.float32)
+        y, a = oracle.matmul(fmt, w, sc, x)
+        # row 0: |q x| = 3 + 2 + 0 + 0.25 + 4 + 0 + 1 + 1 = 11.25 ; row 1: 1
+        np.testing.assert_array_equal(a, [[5.625, 2.0]])
+        # signed sum: -3 - 2 + 0 - 0.25 - 4 + 0 + 1 + 1 = -7.25 -> * -0.5
+        np.testing.assert_array_equal(y, np.array([[3.625, 2.0]], np.float32))
+        ab = brute.bound_exact(fmt, w, sc, x, 8)
+        assert [float(v) for v in ab[0]] == [5.625, 2.0]
 
 
 def test_brute_force_f32_without_scales():
