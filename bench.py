@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the stream-read ceiling measured beside HBM-bound workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (10 times) for counter calibration")
     return ap.parse_args()
@@ -300,6 +302,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_counters(args.workload)
 
+    if roof["bound"] == "hbm" and not args.no_calibration:
+        roof["ceiling"] = stream_read_ceiling(torch, wq, weight_bytes, n_rot, min(K, 400), plans[0])
+
     pipe = None
     if args.workload == "moe_ffn_pipeline":
         pipe = pipeline_modes(torch, wq, gated, downs, probs, n_rot, min(K, 400))
@@ -347,6 +352,51 @@ def main():
     for c in copies:
         for t in c:
             wq.wq_tensor_free(t)
+
+
+def stream_read_ceiling(torch, wq, nbytes, n_rot, K, plan):
+    """Practical HBM read ceiling for this step's weight bytes: a plain 128-bit non-temporal
+    stream read of the same byte count, over the same number of rotated copies, for a few
+    launch shapes (waves x 1 KiB loads in flight per wave), each timed over K launches in
+    one HIP graph like the workload. Returns the best rate and every shape's rate (GB/s)."""
+    dev = torch.device("cuda:0")
+    n16 = (nbytes + 15) // 16 * 16
+    bufs = [torch.ones(n16 // 4, dtype=torch.int32, device=dev) for _ in range(n_rot)]
+    # whole chunk in flight at once (one round trip per wave) at 1, 2, 4 and 8 waves per
+    # SIMD, plus the shape of a 4-row ring of 3 KiB rows (12 loads of 1 KiB)
+    kib = -(-nbytes // 1024)
+    shapes = [(1024, 12)]
+    for waves in (1024, 2048, 4096, 8192):
+        need = -(-kib // waves)
+        loads = next((L for L in (1, 2, 4, 5, 8, 9, 12, 16, 18, 24, 36) if L >= need), 36)
+        shapes.append((waves, loads))
+    out = torch.empty(64 * max(w for w, _ in shapes), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for waves, loads in shapes:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(K):
+                wq.wq_stream_read_dev(bufs[i % n_rot], waves, loads, out)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        rates["%dx%d" % (waves, loads)] = {"us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1)}
+        del g
+    best = max(rates.items(), key=lambda kv: kv[1]["gbs"])
+    del bufs
+    return {"kernel": "stream read, 128-bit non-temporal loads, same byte count and rotation",
+            "bytes_per_launch": nbytes, "best_shape": best[0], "best_gbs": best[1]["gbs"],
+            "best_us": best[1]["us"], "shapes_waves_x_loads": rates}
 
 
 def pipeline_modes(torch, wq, gated, downs, probs, n_rot, K):

@@ -248,6 +248,25 @@ const char *wq_strerror(int code);
  */
 int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen);
 
+/*
+ * Measurement helper (not part of the matmul): the practical HBM read
+ * ceiling. Reads `bytes` (a multiple of 16) from the device buffer buf_dev
+ * (16-byte aligned) exactly once with the 128-bit non-temporal loads the
+ * GEMV streams its weights with: `waves` waves (a positive multiple of 4,
+ * blocks of 4 waves) each read one contiguous chunk, keeping
+ * loads_in_flight (1, 2, 4, 5, 8, 9, 12, 16, 18, 24 or 36) loads of 1 KiB in
+ * flight.
+ * out_dev (device, 4-byte aligned) receives 64 * waves words (an
+ * exclusive-or of the words read, so the loads cannot be dropped).
+ * Stream-ordered on hip_stream, no host synchronisation. The survey's
+ * measurement protocol asks for such a kernel beside the GEMV timings
+ * (colibri docs "CUDA backend (Linux)" print no kernel-level rates, so
+ * the ceiling is measured, not quoted). Errors: WQ_E_INVAL for a bad
+ * argument, WQ_E_HIP.
+ */
+int wq_stream_read_dev(const void *buf_dev, size_t bytes, int waves, int loads_in_flight, unsigned *out_dev,
+                       void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,3 +84,36 @@ def assert_within_bound(y, y_ref, A, what=""):
         raise AssertionError("%s: %d of %d elements outside |y-y_ref| <= 1e-5*A + 1e-30; first %s; "
                              "worst err/bound %.3g" % (what, int(bad.sum()), bad.size, idx.tolist(),
                                                         float(np.max(err / bound))))
+
+
+# ---------------------------------------------------------------------------------------
+# gated feed-forward: tolerance of h = silu(g) * u derived from the matmul contract
+# (|g - g_ref| <= Eg = 1e-5*Ag + ulp(g_ref) + 1e-30, the same for u) and silu's slope,
+# which never exceeds 1.1 in magnitude; 2e-6 relative covers the fp32 evaluation of
+# silu and the product (a few ulps).
+
+
+def silu64(z):
+    z = z.astype(np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def ulp32(v):
+    return np.spacing(np.abs(v).astype(np.float32)).astype(np.float64)
+
+
+def h_bound(g, Ag, u, Au, h):
+    Eg = 1e-5 * Ag + ulp32(g) + 1e-30
+    Eu = 1e-5 * Au + ulp32(u) + 1e-30
+    t = 1.1 * Eg * (np.abs(u) + Eu) + np.abs(silu64(g)) * Eu
+    return t + 2e-6 * (np.abs(h).astype(np.float64) + t) + 1e-30
+
+
+def assert_h(h, ref, what):
+    bh = h_bound(ref["g"], ref["Ag"], ref["u"], ref["Au"], ref["h"])
+    err = np.abs(h.astype(np.float64) - ref["h"].astype(np.float64))
+    assert np.all(np.isfinite(h)), what
+    bad = err > bh
+    assert not bad.any(), "%s: %d of %d h elements out of bound; worst err/bound %.3g at %s" % (
+        what, int(bad.sum()), bad.size, float(np.max(err / bh)), np.argwhere(bad)[:3].tolist())
+    return bh

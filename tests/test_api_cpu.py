@@ -240,3 +240,17 @@ def test_upload_gs_validation_without_device():
     assert up(wq.WQ_I8, 100) == wq.WQ_E_UNSUPPORTED
     assert up(wq.WQ_I8, 64, scales=None) == wq.WQ_E_INVAL
     assert up(wq.WQ_I8, 64) in (wq.WQ_E_NOTINIT, wq.WQ_OK)  # valid: needs an opened device
+
+
+def test_stream_read_rejects_bad_arguments_before_any_device_call():
+    out = ctypes.c_void_p(0x10000)
+    buf = ctypes.c_void_p(0x20000)
+    f = wq.lib.wq_stream_read_dev
+    assert f(None, 1024, 4, 4, out, None) == wq.WQ_E_INVAL
+    assert f(buf, 1024, 4, 4, None, None) == wq.WQ_E_INVAL
+    assert f(buf, 1024, 6, 4, out, None) == wq.WQ_E_INVAL      # waves not a multiple of 4
+    assert f(buf, 1024, 0, 4, out, None) == wq.WQ_E_INVAL
+    assert f(buf, 1024, 4, 3, out, None) == wq.WQ_E_INVAL      # uncompiled loads-in-flight count
+    assert f(buf, 1000, 4, 4, out, None) == wq.WQ_E_INVAL      # not a multiple of 16 bytes
+    assert f(ctypes.c_void_p(0x20008), 1024, 4, 4, out, None) == wq.WQ_E_INVAL  # misaligned
+    assert f(buf, 0, 4, 4, out, None) == wq.WQ_OK              # nothing to read: no launch

@@ -46,30 +46,7 @@ def device():
     gu.reinit_with_env(WQ_FORCE_PATH=None)
 
 
-def silu64(z):
-    z = z.astype(np.float64)
-    return z / (1.0 + np.exp(-z))
-
-
-def ulp32(v):
-    return np.spacing(np.abs(v).astype(np.float32)).astype(np.float64)
-
-
-def h_bound(g, Ag, u, Au, h):
-    Eg = 1e-5 * Ag + ulp32(g) + 1e-30
-    Eu = 1e-5 * Au + ulp32(u) + 1e-30
-    t = 1.1 * Eg * (np.abs(u) + Eu) + np.abs(silu64(g)) * Eu
-    return t + 2e-6 * (np.abs(h).astype(np.float64) + t) + 1e-30
-
-
-def assert_h(h, ref, what):
-    bh = h_bound(ref["g"], ref["Ag"], ref["u"], ref["Au"], ref["h"])
-    err = np.abs(h.astype(np.float64) - ref["h"].astype(np.float64))
-    assert np.all(np.isfinite(h)), what
-    bad = err > bh
-    assert not bad.any(), "%s: %d of %d h elements out of bound; worst err/bound %.3g at %s" % (
-        what, int(bad.sum()), bad.size, float(np.max(err / bh)), np.argwhere(bad)[:3].tolist())
-    return bh
+silu64, ulp32, h_bound, assert_h = gu.silu64, gu.ulp32, gu.h_bound, gu.assert_h
 
 
 def assert_y(y, fmt_dn, dw, dsc, ref_h, bh, y_ref, what):

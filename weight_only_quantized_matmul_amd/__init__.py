@@ -72,6 +72,7 @@ def _bind(lib):
         "wq_tensor_free": (ci, [vp]),
         "wq_strerror": (ctypes.c_char_p, [ci]),
         "wq_describe_plan": (ci, [ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t]),
+        "wq_stream_read_dev": (ci, [vp, ctypes.c_size_t, ci, ci, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -339,3 +340,16 @@ def wq_describe_plan(fmt: int, O: int, I: int, S: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib.wq_describe_plan(int(fmt), int(O), int(I), int(S), buf, 256), "wq_describe_plan")
     return buf.value.decode()
+
+
+def wq_stream_read_dev(buf_dev, waves: int, loads_in_flight: int, out_dev, stream=None) -> None:
+    """Read every byte of the device tensor buf_dev once (HBM read ceiling);
+    out_dev: int32 device tensor of >= 64 * waves elements."""
+    nbytes = buf_dev.numel() * buf_dev.element_size()
+    if not buf_dev.is_cuda or not buf_dev.is_contiguous() or not out_dev.is_cuda:
+        raise ValueError("device tensors expected")
+    if out_dev.numel() * out_dev.element_size() < 4 * 64 * int(waves):
+        raise ValueError("out_dev too small")
+    _check(lib.wq_stream_read_dev(ctypes.c_void_p(buf_dev.data_ptr()), nbytes, int(waves), int(loads_in_flight),
+                                  ctypes.c_void_p(out_dev.data_ptr()), _stream_handle(stream, buf_dev.device)),
+           "wq_stream_read_dev")

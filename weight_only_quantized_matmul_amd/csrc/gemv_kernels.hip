@@ -18,17 +18,22 @@
 //    reduced while rows r+1..r+D-1 are still arriving, and its registers are
 //    refilled with row r+D right after. Reloads in the steady state are
 //    unconditional so the wait counts stay exact.
-//  * Dequantization happens in registers on 32-bit words. For int4 and int2
-//    the code offset is folded out of the inner loop: codes are used
-//    unshifted and offset * sum(x) is subtracted once per lane. A code is
-//    never converted on its own: one mask of a word leaves two codes in the
-//    low bits of its 16-bit halves, each half read as an f16 subnormal
-//    (code * 2^-24, exact), and v_fma_mix_f32 widens that half inside the
-//    FMA. Codes sitting higher in a byte are 4^k or 16 times larger; the
-//    activations they meet are pre-divided by the same power of two, and
-//    the finished sum is multiplied by 2^24 (all exact). The lane's sum(x) is formed
-//    in the same order as the FMA chain, so a row whose codes all decode to
-//    zero gives exactly 0.
+//  * Dequantization happens in registers on 32-bit words, and every code
+//    becomes its exact value q = code - offset before it meets an
+//    activation, so each product q * x is exact and the rounding of the sum
+//    is bounded by sum |q * x| (the offset is never folded into a separate
+//    offset * sum(x) term, whose rounding would scale with sum |code * x|).
+//    One activation row (S = 1): one and-or of a word leaves two codes in
+//    the mantissas of its 16-bit halves under the f16 exponent of 1024
+//    (half value 1024 + code * 2^k, exact); one packed f16 subtraction of
+//    1024 + offset * 2^k leaves 2^k * q in each half, exact, and
+//    v_fma_mix_f32 widens that half inside the FMA. Several rows: an
+//    exclusive-or turns every field into the two's complement of q, a shift
+//    and mask place it at the top of a byte (byte = 2^k * q), and one
+//    sign-extending byte conversion per code feeds the S plain FMAs. The
+//    activations meeting a field scaled by 2^k are pre-divided by 2^k
+//    (exact). A row whose codes all decode to zero therefore gives exactly
+//    0.
 //  * Lanes are reduced with DPP (quad_perm, row_shr, row_bcast) instead of an
 //    LDS tree; teams of several waves add their wave totals through LDS in a
 //    fixed order, so results are deterministic. Row scales are read with
@@ -51,21 +56,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT> struct FmtInfo;
-template <> struct FmtInfo<WQ_F32> { static constexpr int EPW = 1;  static constexpr int OFF = 0; };
-template <> struct FmtInfo<WQ_I8>  { static constexpr int EPW = 4;  static constexpr int OFF = 0; };
-template <> struct FmtInfo<WQ_I4>  { static constexpr int EPW = 8;  static constexpr int OFF = 8; };
-template <> struct FmtInfo<WQ_I2>  { static constexpr int EPW = 16; static constexpr int OFF = 2; };
+template <> struct FmtInfo<WQ_F32> { static constexpr int EPW = 1; };
+template <> struct FmtInfo<WQ_I8>  { static constexpr int EPW = 4; };
+template <> struct FmtInfo<WQ_I4>  { static constexpr int EPW = 8; };
+template <> struct FmtInfo<WQ_I2>  { static constexpr int EPW = 16; };
 
-// Factor applied to the activation that meets field e (0..EPW-1) of a word,
-// compensating the unshifted field position used by the folded dequant.
-template <int FMT> __device__ constexpr float x_prescale(int e) {
-    if (FMT == WQ_I4) return (e & 1) ? 0.0625f : 1.0f;
-    if (FMT == WQ_I2) {
-        const int f = e & 3;
-        return f == 0 ? 1.0f : f == 1 ? 0.25f : f == 2 ? 0.0625f : 0.015625f;
-    }
-    return 1.0f;
-}
 
 template <int LW> __device__ __forceinline__ void load_w(const uint8_t *p, uint32_t (&v)[LW / 4]) {
     if constexpr (LW == 16) {
@@ -79,30 +74,49 @@ template <int LW> __device__ __forceinline__ void load_w(const uint8_t *p, uint3
     }
 }
 
-// The low / high 16 bits of a word read as an f16 value, widened to f32.
-__device__ __forceinline__ float f16_lo(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)p); }
-__device__ __forceinline__ float f16_hi(uint32_t p) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
-}
-
-// How int4 / int2 codes reach the FMAs. MIX: two codes per mask, read as
-// f16 subnormals (code * 2^-24) that v_fma_mix_f32 widens inside the FMA --
-// fewest instructions per element when each code meets one activation row.
-// Otherwise (several activation rows) each code is converted once
-// (v_cvt_f32_ubyteN) and meets the rows in plain v_fmac_f32.
-// (Measured: at S = 1 the mixed form is the faster one; at S = 4 the plain
-// FMAs are, the conversion being shared by the rows.)
+// How int4 / int2 codes reach the FMAs. MIX: two codes per and-or and one
+// packed f16 subtraction, as f16 halves holding 2^k * q that v_fma_mix_f32
+// widens inside the FMA -- fewest instructions per element when each code
+// meets one activation row. Otherwise (several activation rows) each code is
+// converted once, from a byte holding 2^k * q, and meets the rows in plain
+// v_fmac_f32. (Measured: at S = 1 the mixed form is the faster one; at S = 4
+// the plain FMAs are, the conversion being shared by the rows.)
 template <int FMT, int SMAX> constexpr bool kMix = (FMT == WQ_I4 || FMT == WQ_I2) && SMAX == 1;
 
-// Scale of the accumulated sums: with MIX a row's sum is 2^-24 times the
-// code sum.
-template <int FMT, int SMAX> __device__ constexpr float acc_unscale() { return kMix<FMT, SMAX> ? 16777216.0f : 1.0f; }
+// Factor applied to the activation that meets field e (0..EPW-1) of a word:
+// 2^-k for a field whose dequantized value is carried as 2^k * q.
+template <int FMT, int SMAX> __device__ constexpr float x_prescale(int e) {
+    if (FMT == WQ_I4) return kMix<FMT, SMAX> ? ((e & 1) ? 0.0625f : 1.0f) : 0.0625f;
+    if (FMT == WQ_I2) {
+        if (!kMix<FMT, SMAX>) return 0.015625f;
+        const int f = e & 3;
+        return f == 0 ? 1.0f : f == 1 ? 0.25f : f == 2 ? 0.0625f : 0.015625f;
+    }
+    return 1.0f;
+}
 
-// Keeps the compiler from pushing a byte mask into each field extraction
-// (which would turn one v_cvt_f32_ubyteN into v_bfe_u32 + v_cvt_f32_ubyte0).
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Keeps a value in a register as computed: stops the compiler from pushing a
+// byte mask into each field extraction, and keeps constants that
+// three-operand instructions need in registers.
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm("" : "+v"(v));
     return v;
+}
+
+// Two fields of v, selected by mask (each inside mantissa bits 0..9 of its
+// 16-bit half, value f * 2^k), as the exact f16 pair 2^k * (f - off): the
+// and-or gives halves 1024 + 2^k * f (below 2048, so exact), and one packed
+// f16 subtraction of 1024 + 2^k * off leaves an integer of magnitude below
+// 2048, exact as well. The mask and the exponent bits are passed in
+// registers (opaque values) so that the and-or is one v_and_or_b32: a
+// three-operand instruction takes no literal constants on this target.
+template <int BIAS>
+__device__ __forceinline__ half2v exact_pair(uint32_t v, uint32_t mask, uint32_t expo) {
+    const half2v b = __builtin_bit_cast(half2v, (v & mask) | expo);
+    constexpr _Float16 c = (_Float16)(1024 + BIAS);
+    return b - half2v{c, c};
 }
 
 // With the mixed form at S = 1, int4 / int2 sums run in two independent
@@ -116,7 +130,7 @@ template <int FMT, int SMAX> __device__ constexpr int field_chain(int e) {
 }
 
 // acc[c][s] += sum over the fields e of chain c of one word of
-// code * xw[e][s] (times 2^-24 for int4 / int2, see acc_unscale).
+// q * xw[e][s] (xw pre-scaled by x_prescale, so each product is q * x).
 template <int FMT, int SMAX>
 __device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], float (&acc)[kChains<FMT, SMAX>][SMAX]) {
     if constexpr (FMT == WQ_F32) {
@@ -131,12 +145,15 @@ __device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], fl
             for (int s = 0; s < SMAX; ++s) acc[0][s] = __builtin_fmaf(q, xw[b][s], acc[0][s]);
         }
     } else if constexpr (FMT == WQ_I4 && !kMix<FMT, SMAX>) {
-        const uint32_t lo = opaque(w & 0x0F0F0F0Fu);  // even fields, code in bits 0..3 of each byte
-        const uint32_t hi = opaque(w & 0xF0F0F0F0u);  // odd fields, 16 * code
+        // nibble ^ 8 is the 4-bit two's complement of q = nibble - 8; moved
+        // to the top of its byte it reads as the signed byte 16 * q
+        const uint32_t v = w ^ 0x88888888u;
+        const uint32_t lo = opaque((v << 4) & 0xF0F0F0F0u);  // even fields
+        const uint32_t hi = opaque(v & 0xF0F0F0F0u);         // odd fields
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const float cl = (float)((lo >> (8 * b)) & 0xFFu);
-            const float ch = (float)((hi >> (8 * b)) & 0xFFu);
+            const float cl = (float)(int)(int8_t)(lo >> (8 * b));
+            const float ch = (float)(int)(int8_t)(hi >> (8 * b));
 #pragma unroll
             for (int s = 0; s < SMAX; ++s) {
                 acc[0][s] = __builtin_fmaf(cl, xw[2 * b][s], acc[0][s]);
@@ -144,46 +161,52 @@ __device__ __forceinline__ void word_fma(uint32_t w, const float (*xw)[SMAX], fl
             }
         }
     } else if constexpr (FMT == WQ_I2 && !kMix<FMT, SMAX>) {
-        const uint32_t m[4] = {opaque(w & 0x03030303u), opaque(w & 0x0C0C0C0Cu), opaque(w & 0x30303030u),
-                               opaque(w & 0xC0C0C0C0u)};
+        // code ^ 2 is the 2-bit two's complement of q = code - 2; at the top
+        // of its byte it reads as the signed byte 64 * q
+        const uint32_t v = w ^ 0xAAAAAAAAu;
+        const uint32_t m[4] = {opaque((v << 6) & 0xC0C0C0C0u), opaque((v << 4) & 0xC0C0C0C0u),
+                               opaque((v << 2) & 0xC0C0C0C0u), opaque(v & 0xC0C0C0C0u)};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                const float c = (float)((m[f] >> (8 * b)) & 0xFFu);  // code * 4^f
+                const float c = (float)(int)(int8_t)(m[f] >> (8 * b));  // 64 * q
 #pragma unroll
                 for (int s = 0; s < SMAX; ++s)
                     acc[0][s] = __builtin_fmaf(c, xw[4 * b + f][s], acc[0][s]);
             }
     } else if constexpr (FMT == WQ_I4) {
-        // Each 16-bit half of a masked word is an f16 subnormal whose bits
-        // are a code (or 16 x a code): value code * 2^-24, exact and with no
-        // bias, which v_fma_mix_f32 widens inside the FMA. Fields 2b and
-        // 2b + 1 are the low and high nibble of byte b; m[j] holds field j
-        // in its low half (chain 0) and field j + 4 in its high half (chain 1).
+        // Fields 2b and 2b + 1 are the low and high nibble of byte b; q[j]
+        // holds field j in its low half (chain 0) and field j + 4 in its
+        // high half (chain 1), the odd fields as 16 * q.
         const uint32_t t = w >> 8;  // bytes 1 and 3 into the low byte of each half
-        const uint32_t m[4] = {w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u};
+        const uint32_t e = opaque(0x64006400u), m0 = opaque(0x000F000Fu), m1 = opaque(0x00F000F0u);
+        const half2v q[4] = {exact_pair<8>(w, m0, e), exact_pair<128>(w, m1, e), exact_pair<8>(t, m0, e),
+                             exact_pair<128>(t, m1, e)};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
                 for (int s = 0; s < SMAX; ++s)
-                    acc[hi][s] = __builtin_fmaf(hi ? f16_hi(m[j]) : f16_lo(m[j]), xw[4 * hi + j][s], acc[hi][s]);
-    } else {  // WQ_I2: fields 4b..4b + 3 in bit pairs 0-1 .. 6-7 of byte b, same f16 reading
+                    acc[hi][s] = __builtin_fmaf(hi ? (float)q[j].y : (float)q[j].x, xw[4 * hi + j][s], acc[hi][s]);
+    } else {  // WQ_I2: fields 4b..4b + 3 in bit pairs 0-1 .. 6-7 of byte b, as 4^f * q
         const uint32_t v[2] = {w, w >> 8};
+        const uint32_t e = opaque(0x64006400u);
+        const uint32_t m[4] = {opaque(0x00030003u), opaque(0x000C000Cu), opaque(0x00300030u), opaque(0x00C000C0u)};
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+            const half2v q[4] = {exact_pair<2>(v[h], m[0], e), exact_pair<8>(v[h], m[1], e),
+                                 exact_pair<32>(v[h], m[2], e), exact_pair<128>(v[h], m[3], e)};
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const uint32_t mf = v[h] & (0x00030003u << (2 * f));  // code * 4^f in each half
+            for (int f = 0; f < 4; ++f)
 #pragma unroll
                 for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
                     for (int s = 0; s < SMAX; ++s)
-                        acc[hi][s] = __builtin_fmaf(hi ? f16_hi(mf) : f16_lo(mf), xw[8 * hi + 4 * h + f][s],
+                        acc[hi][s] = __builtin_fmaf(hi ? (float)q[f].y : (float)q[f].x, xw[8 * hi + 4 * h + f][s],
                                                     acc[hi][s]);
-            }
+        }
     }
 }
 
@@ -245,7 +268,6 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
     // below), which keeps the compiler's memory wait counts exact.
     constexpr int K = KMAX;
     constexpr int EPW = FmtInfo<FMT>::EPW;
-    constexpr int OFF = FmtInfo<FMT>::OFF;
     constexpr int WPC = LW / 4;     // 32-bit words per lane load
     constexpr int EPC = WPC * EPW;  // fields per lane load
     const int team_lanes = team * 64;
@@ -370,35 +392,15 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
         __builtin_amdgcn_sched_barrier(0);  // rows issued in ring order (waits count whole rows)
     }
 
-    // Activation sums per FMA chain, in each chain's own order.
-    constexpr int NC = kChains<FMT, SMAX>;
-    float sx[NC][SMAX];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int s = 0; s < SMAX; ++s) sx[c][s] = 0.0f;
-    float sxk[KMAX][NC][SMAX];  // GS: activation sums per slot
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int s = 0; s < SMAX; ++s) sxk[k][c][s] = 0.0f;
     // (16-byte activation runs are already zero where they leave the row)
+    constexpr int NC = kChains<FMT, SMAX>;
     if (XV || wave_in) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
 #pragma unroll
             for (int s = 0; s < SMAX; ++s)
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    const float v = xr[k][e][s];
-                    xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
-                    if constexpr (OFF != 0) {
-                        if constexpr (GS) sxk[k][field_chain<FMT, SMAX>(e % EPW)][s] += v;
-                        else sx[field_chain<FMT, SMAX>(e % EPW)][s] += v;
-                    }
-                }
+                for (int e = 0; e < EPC; ++e) xr[k][e][s] *= x_prescale<FMT, SMAX>(e % EPW);
     } else if constexpr (!XV) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
@@ -408,12 +410,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 for (int e = 0; e < EPC; ++e) {
                     const int ei = WQ_XE(k, e / 4) + (e & 3);
                     const bool in = live[k] && ei < I;
-                    const float v = in ? xr[k][e][s] : 0.0f;
-                    xr[k][e][s] = v * x_prescale<FMT>(e % EPW);
-                    if constexpr (OFF != 0) {
-                        if constexpr (GS) sxk[k][field_chain<FMT, SMAX>(e % EPW)][s] += v;
-                        else sx[field_chain<FMT, SMAX>(e % EPW)][s] += v;
-                    }
+                    xr[k][e][s] = (in ? xr[k][e][s] : 0.0f) * x_prescale<FMT, SMAX>(e % EPW);
                 }
     }
 #undef WQ_XE
@@ -441,8 +438,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
         for (int k = 0; k < KMAX; ++k)
             if (k < K) {
                 if constexpr (GS) {
-                    // the slot's sum (offset removed with its own activation
-                    // sum, so all-zero codes give exactly 0) times its group scale
+                    // the slot's sum times its group scale
                     float t[NC][SMAX];
 #pragma unroll
                     for (int c = 0; c < NC; ++c)
@@ -454,11 +450,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                     for (int s = 0; s < SMAX; ++s) {
                         float u = 0.0f;
 #pragma unroll
-                        for (int c = 0; c < NC; ++c) {
-                            float uc = t[c][s] * acc_unscale<FMT, SMAX>();
-                            if constexpr (OFF != 0) uc -= (float)OFF * sxk[k][c][s];
-                            u += uc;
-                        }
+                        for (int c = 0; c < NC; ++c) u += t[c][s];
                         gacc[s] = fmaf(gv[k], u, gacc[s]);
                     }
                 } else {
@@ -473,11 +465,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 t = gacc[s];
             } else {
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    float tc = acc[c][s] * acc_unscale<FMT, SMAX>();
-                    if constexpr (OFF != 0) tc -= (float)OFF * sx[c][s];
-                    t += tc;
-                }
+                for (int c = 0; c < NC; ++c) t += acc[c][s];
             }
             part[s] = t;
         }

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <iterator>
 #include <mutex>
 #include <new>
 
@@ -833,6 +834,16 @@ const char *wq_strerror(int code) {
     case WQ_E_UNSUPPORTED: return "unsupported request";
     default: return "unknown status code";
     }
+}
+
+int wq_stream_read_dev(const void *buf_dev, size_t bytes, int waves, int loads_in_flight, unsigned *out_dev,
+                       void *hip_stream) {
+    if (buf_dev == nullptr || out_dev == nullptr || waves <= 0 || waves % 4 != 0 || waves > (1 << 20)) return WQ_E_INVAL;
+    if (((uintptr_t)buf_dev & 15) || ((uintptr_t)out_dev & 3) || bytes % 16 != 0) return WQ_E_INVAL;
+    const int ok[] = {1, 2, 4, 5, 8, 9, 12, 16, 18, 24, 36};
+    if (std::find(std::begin(ok), std::end(ok), loads_in_flight) == std::end(ok)) return WQ_E_INVAL;
+    if (bytes == 0) return WQ_OK;
+    return hip_status(wq::launch_stream_read(buf_dev, bytes, waves, loads_in_flight, out_dev, (hipStream_t)hip_stream));
 }
 
 int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {

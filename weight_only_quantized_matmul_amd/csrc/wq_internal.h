@@ -276,6 +276,12 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs =
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Stream-read calibration: `waves` waves (a multiple of 4) each read one
+// contiguous chunk of the buffer with `loads` 1 KiB loads in flight; out
+// receives 64 words per wave.
+hipError_t launch_stream_read(const void *buf, size_t bytes, int waves, int loads, uint32_t *out, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Upload: natural packed rows (O x rb, device) -> device layout (O x stride).
 hipError_t launch_relayout(int fmt, const uint8_t *src, uint8_t *dst, int O, long rb, long stride, int nfull,
                            hipStream_t st);
