@@ -163,6 +163,28 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
 int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, void *hip_stream);
 
 /*
+ * wq_matmul_dev for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results as wq_matmul_dev (bit for bit), but
+ * the call never allocates or frees anything: the tiled path's workspace is
+ * a fixed device array of WQ_NOALLOC_SCRATCH_BYTES per device, reserved for
+ * this call when the library is loaded and held until the process ends (its
+ * address is looked up in wq_init). A call whose workspace would exceed it
+ * (wq_describe_plan prints the size; e.g. S = 2048 with I = 8192 int8)
+ * returns WQ_E_UNSUPPORTED before any launch. Every call on a device shares
+ * that device's array, which keeps the last call's contents (each call
+ * rewrites every part it reads, so nothing needs clearing): calls that
+ * overlap in time on one device -- from two streams, or two host threads --
+ * race on it and must not be issued. Calls on different devices do not
+ * share it. Errors as wq_matmul_dev, plus WQ_E_UNSUPPORTED.
+ */
+#define WQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int wq_matmul_dev_noalloc(const wq_tensor *t, const float *x_dev, int S, float *y_dev, void *hip_stream);
+
+/* Size in bytes of the fixed device array wq_matmul_dev_noalloc uses. Host-only. */
+size_t wq_noalloc_scratch_bytes(void);
+
+/*
  * Build a group of G resident tensors that run together in one launch (the
  * grouped expert matmul of a mixture-of-experts decode step; grouped expert
  * handling at prefill is described in colibri docs "CUDA backend (Linux)",

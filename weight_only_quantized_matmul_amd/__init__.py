@@ -73,6 +73,8 @@ def _bind(lib):
         "wq_strerror": (ctypes.c_char_p, [ci]),
         "wq_describe_plan": (ci, [ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t]),
         "wq_stream_read_dev": (ci, [vp, ctypes.c_size_t, ci, ci, vp, vp]),
+        "wq_matmul_dev_noalloc": (ci, [vp, vp, ci, vp, vp]),
+        "wq_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -241,6 +243,20 @@ def wq_matmul_dev(t: Tensor, x_dev, y_dev, stream=None) -> None:
     xp = _dev_f32(x_dev, (S, t.I), t.device, "x_dev")
     yp = _dev_f32(y_dev, (S, t.O), t.device, "y_dev")
     _check(lib.wq_matmul_dev(t.ptr, xp, int(S), yp, _stream_handle(stream, t.device)), "wq_matmul_dev")
+
+
+def wq_matmul_dev_noalloc(t: Tensor, x_dev, y_dev, stream=None) -> None:
+    """As wq_matmul_dev, allocating nothing (the tiled workspace is the library's fixed
+    per-device array of wq_noalloc_scratch_bytes() bytes)."""
+    S = x_dev.shape[0] if x_dev.dim() == 2 else -1
+    xp = _dev_f32(x_dev, (S, t.I), t.device, "x_dev")
+    yp = _dev_f32(y_dev, (S, t.O), t.device, "y_dev")
+    _check(lib.wq_matmul_dev_noalloc(t.ptr, xp, int(S), yp, _stream_handle(stream, t.device)),
+           "wq_matmul_dev_noalloc")
+
+
+def wq_noalloc_scratch_bytes() -> int:
+    return int(lib.wq_noalloc_scratch_bytes())
 
 
 def wq_grouped_create(tensors) -> Group:

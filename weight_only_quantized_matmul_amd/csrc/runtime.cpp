@@ -20,8 +20,18 @@
 
 namespace {
 
+// Device scratch of wq_matmul_dev_noalloc (the tiled path's activation
+// planes and split-K partials), for callers that cannot allocate. One copy
+// per device, held until the process ends. In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is looked
+// up once per device in wq_init (DeviceCtx::scratch) and only that address
+// is passed on.
+constexpr size_t kScratchBytes = (size_t)WQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 struct DeviceCtx {
     bool open = false;
+    uint16_t *scratch = nullptr;   // device address of this device's `scratch`
     hipStream_t stream = nullptr;  // library stream for the host-pointer calls
     int cus = 0;
     size_t total_mem = 0;
@@ -183,7 +193,11 @@ int ensure_workspace(DeviceCtx &d, size_t bytes, hipStream_t st, uint16_t **out)
     return WQ_OK;
 }
 
-int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t st) {
+// fixed_ws != nullptr: the workspace is that buffer of fixed_cap bytes (the
+// no-allocation entry point); a call needing more returns WQ_E_UNSUPPORTED
+// before any launch. Otherwise the device workspace, grown on demand.
+int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t st, uint16_t *fixed_ws = nullptr,
+               size_t fixed_cap = 0) {
     DeviceCtx &d = g_dev[t->device];
     wq::GemvPlan gp;
     if (choose_path(t->fmt, t->O, t->I, S, d.cus, &gp, t->gs > 0) == 1) {
@@ -224,9 +238,13 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
     a.plane = (long)tp.sp * tp.kp;
     a.kp = tp.kp;
     if (tp.ws_bytes > 0) {
-        uint16_t *ws = nullptr;
-        int rc = ensure_workspace(d, tp.ws_bytes, st, &ws);
-        if (rc != WQ_OK) return rc;
+        uint16_t *ws = fixed_ws;
+        if (fixed_ws != nullptr) {
+            if (tp.ws_bytes > fixed_cap) return WQ_E_UNSUPPORTED;
+        } else {
+            int rc = ensure_workspace(d, tp.ws_bytes, st, &ws);
+            if (rc != WQ_OK) return rc;
+        }
         a.xp = ws;
         if (tp.ksplit > 1) {
             a.ksplit = tp.ksplit;
@@ -296,8 +314,16 @@ int wq_init(const int *devices, int ndev) {
         if (hipGetDeviceProperties(&prop, list[i]) != hipSuccess) return WQ_E_HIP;
         if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return WQ_E_NODEV;
         DeviceGuard guard(list[i]);
+        // hipGetSymbolAddress acts on the current device: the guard made
+        // list[i] current (each device holds its own copy of `scratch`)
+        void *sp = nullptr;
+        if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || sp == nullptr) {
+            (void)hipGetLastError();
+            return WQ_E_HIP;
+        }
         hipStream_t st = nullptr;
         if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return WQ_E_HIP;
+        d.scratch = static_cast<uint16_t *>(sp);
         d.stream = st;
         d.cus = prop.multiProcessorCount;
         d.total_mem = prop.totalGlobalMem;
@@ -506,6 +532,21 @@ int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, v
     DeviceGuard guard(t->device);
     return run_matmul(t, x_dev, S, y_dev, (hipStream_t)hip_stream);
 }
+
+int wq_matmul_dev_noalloc(const wq_tensor *t, const float *x_dev, int S, float *y_dev, void *hip_stream) {
+    if (!tensor_ok(t) || S < 0) return WQ_E_INVAL;
+    if (S == 0) return WQ_OK;
+    if (x_dev == nullptr || y_dev == nullptr) return WQ_E_INVAL;
+    if (((uintptr_t)x_dev & 3) || ((uintptr_t)y_dev & 3)) return WQ_E_INVAL;
+    if (!device_open(t->device)) return WQ_E_NOTINIT;
+    if (g_cfg.fault == 2) return WQ_E_FAULT;
+    DeviceCtx &d = g_dev[t->device];
+    if (d.scratch == nullptr) return WQ_E_NOTINIT;
+    DeviceGuard guard(t->device);
+    return run_matmul(t, x_dev, S, y_dev, (hipStream_t)hip_stream, d.scratch, kScratchBytes);
+}
+
+size_t wq_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 } // extern "C"
 
