@@ -59,7 +59,7 @@ def parse():
                              "prefill"])
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the stream-read ceiling measured beside HBM-bound workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -101,7 +101,7 @@ def problems_for(name):
         return [synth.dense_gemv(S=1)], "dense_gemv: int4 W[12288,6144] (codes U{0..15}), scales U[0.002,0.05], x N(0,1), S=1"
     if name == "moe_decode":
         return synth.moe_decode(), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
-                                    "S=1 per expert, one grouped launch")
+                                    "S=1 per expert, all 24 matmuls in one grouped launch")
     if name in ("moe_ffn", "moe_ffn_pipeline"):
         return synth.moe_decode(), ("moe_ffn: 8 experts x int4 {gate,up}[2048,6144] -> h = silu(g)*u -> "
                                     "down[6144,2048], S=1 per expert, fused gate/up launch + grouped down launch")
@@ -159,10 +159,6 @@ def main():
                 + 4 * p.S * p.I + 4 * p.S * p.O)
 
     alg_bytes = sum(io_bytes(p) for p in probs)
-    if grouped:
-        # one launch per slot-count class: the gate/up rows (3 KiB) and the
-        # down rows (1 KiB); the gate/up launch dominates
-        gu_bytes = sum(io_bytes(p) for i, p in enumerate(probs) if i % 3 != 2)
     if ffn:
         # gate and up read one x and write one h between them; down reads h
         gu_bytes = sum(p.weight_bytes + 4 * p.O for i, p in enumerate(probs) if i % 3 != 2) + sum(
@@ -199,17 +195,8 @@ def main():
         else:
             wq.wq_matmul_dev(copies[r][0], xs[0], ys[0])
 
-    if grouped:
-        gu_groups = [wq.wq_grouped_create([t for j, t in enumerate(c) if j % 3 != 2]) for c in copies]
-        groups = groups + gu_groups
-        gu_x = [x for j, x in enumerate(xs) if j % 3 != 2]
-        gu_y = [y for j, y in enumerate(ys) if j % 3 != 2]
-
     def gate_up_only(i):
-        if grouped:
-            wq.wq_grouped_matmul_dev(gu_groups[i % n_rot], gu_x, gu_y)
-        else:
-            wq.wq_swiglu_matmul_dev(gated[i % n_rot], fx, fh)
+        wq.wq_swiglu_matmul_dev(gated[i % n_rot], fx, fh)
 
     stream = torch.cuda.current_stream()
     for i in range(W):
@@ -244,8 +231,9 @@ def main():
     wall = t1 - t0
     ev_s = ev0.elapsed_time(ev1) / 1e3
     per_launch = ev_s / K  # average launch duration on the launch stream (s)
-    if ffn or grouped:
-        # the step is two launches: time the dominant one (gate/up) in a graph of its own
+    if ffn:
+        # the step is two launches (h feeds the down projection): time the
+        # dominant one (the fused gate/up launch) in a graph of its own
         g2 = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -293,12 +281,14 @@ def main():
     else:
         value = weight_bytes * K / wall / 1e9
         unit = "GB/s"
-        roof = {"bound": "hbm", "achieved": (gu_bytes if (ffn or grouped) else alg_bytes) / per_launch / 1e9,
+        roof = {"bound": "hbm", "achieved": (gu_bytes if ffn else alg_bytes) / per_launch / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         if ffn:
             roof["kernel"] = "fused gate/up (paired rows, silu(g)*u epilogue), all experts in one launch"
+            roof["step_frac"] = alg_bytes / step_per_launch / 1e9 / HBM_PEAK_GBS
         elif grouped:
-            roof["kernel"] = "grouped GEMV launch over the 16 gate/up matmuls (3 KiB rows)"
+            roof["kernel"] = ("grouped GEMV: all 24 matmuls (3 KiB gate/up rows and 1 KiB down rows) "
+                              "in one launch; the whole step")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_counters(args.workload)
 
@@ -309,6 +299,10 @@ def main():
     if args.workload == "moe_ffn_pipeline":
         pipe = pipeline_modes(torch, wq, gated, downs, probs, n_rot, min(K, 400))
         pipe["graph_replay_us_per_step"] = wall / K * 1e6
+
+    api = None
+    if len(probs) == 1 and not getattr(probs[0], "gs", 0):
+        api = host_sync_latency(wq, copies[0][0], probs[0].x)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -337,8 +331,9 @@ def main():
             "pct_hbm_peak_weight_stream": None if compute_bound else 100.0 * value / HBM_PEAK_GBS,
             "event_us_per_launch": per_launch * 1e6,
             **({"event_us_per_step_two_launches": step_per_launch * 1e6,
-                "algorithmic_bytes_gate_up_launch": gu_bytes} if (ffn or grouped) else {}),
+                "algorithmic_bytes_gate_up_launch": gu_bytes} if ffn else {}),
             "plan": plans[:3],
+            **({"host_sync_api_latency": api} if api else {}),
             **({"pipeline": pipe} if pipe else {}),
         },
         "roofline": roof,
@@ -518,51 +513,101 @@ def pipeline_modes(torch, wq, gated, downs, probs, n_rot, K):
     return out
 
 
+def host_cpu():
+    """(nproc, cores this process may use, CPU model name) of the host."""
+    nproc = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = nproc
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return nproc, usable, model
+
+
 def cpu_baseline(probs, compute_bound, seconds, ffn=False):
-    """The CPU oracle as it stands, on this host, for about `seconds` of work."""
+    """The CPU oracle as it stands, on this host: one warm-up run, then the median of five
+    timed runs, on one thread and on every core the process may use (capped by
+    OMP_NUM_THREADS when set: the machine's CPU share). A run is a fixed number of passes over
+    a bounded sample of the workload, sized so that the whole measurement takes about
+    `seconds` (single-thread runs dominate)."""
+    import statistics
+
     import oracle
-    threads = oracle.default_threads()
+    nproc, usable, model = host_cpu()
+    all_threads = usable
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        all_threads = max(1, min(all_threads, int(os.environ["OMP_NUM_THREADS"])))
+
     if ffn:  # the oracle's gate, up, silu_mul, down chain per expert
         E = len(probs) // 3
         unit_work = sum(p.weight_bytes for p in probs)
-        reps = 0
-        t0 = time.perf_counter()
-        while True:
+
+        def one_pass(threads):
             for e in range(E):
                 gp, up, dp = probs[3 * e:3 * e + 3]
                 g, _ = oracle.matmul(gp.fmt, gp.w, gp.scales, gp.x, threads=threads, want_bound=False)
                 u, _ = oracle.matmul(up.fmt, up.w, up.scales, gp.x, threads=threads, want_bound=False)
                 h = oracle.silu_mul(g, u)
                 oracle.matmul(dp.fmt, dp.w, dp.scales, h, threads=threads, want_bound=False)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds or reps >= 1000:
-                break
-        return {"value": unit_work * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-                "sample": "%d pass(es) over the 8-expert gate/up/silu/down chain, S=1, %.1f s" % (reps, el)}
-    # bounded sample: whole weight matrices, at most 16 activation rows of each
-    sample = []
-    for p in probs:
-        S = min(p.S, 16)
-        sample.append((p, p.x[:S]))
-    unit_work = sum((2.0 * x.shape[0] * p.O * p.I) if compute_bound else p.weight_bytes for p, x in sample)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for p, x in sample:
-            if getattr(p, "gs", 0):
-                oracle.matmul_gs(p.fmt, p.w, p.gscales, p.gs, x, threads=threads, want_bound=False)
-            else:
-                oracle.matmul(p.fmt, p.w, p.scales, x, threads=threads, want_bound=False)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
-    rate = unit_work * reps / el / 1e9
-    s_desc = "%d pass(es) over %s with S<=16 activation rows, %.1f s" % (
-        reps, "+".join(sorted(set(p.name.split("_")[0] for p, _ in sample)))[:60], el)
-    return {"value": rate, "unit": "GFLOP/s" if compute_bound else "GB/s", "cores": threads,
-            "kind": "oracle", "sample": s_desc}
+        desc = "the 8-expert gate/up/silu/down chain, S=1"
+    else:
+        # bounded sample: whole weight matrices, at most 16 activation rows of each
+        sample = [(p, p.x[:min(p.S, 16)]) for p in probs]
+        unit_work = sum((2.0 * x.shape[0] * p.O * p.I) if compute_bound else p.weight_bytes for p, x in sample)
+
+        def one_pass(threads):
+            for p, x in sample:
+                if getattr(p, "gs", 0):
+                    oracle.matmul_gs(p.fmt, p.w, p.gscales, p.gs, x, threads=threads, want_bound=False)
+                else:
+                    oracle.matmul(p.fmt, p.w, p.scales, x, threads=threads, want_bound=False)
+        desc = "%s with S<=16 activation rows" % "+".join(sorted(set(p.name.split("_")[0] for p, _ in sample)))[:60]
+
+    def timed(threads, passes):
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            one_pass(threads)
+        return time.perf_counter() - t0
+
+    # size the runs: 6 single-thread runs take about `seconds`
+    probe = timed(1, 1)
+    passes = max(1, int(seconds / 6.0 / max(probe, 1e-6)))
+    out = {}
+    for label, threads in (("one_thread", 1), ("all_cores", all_threads)):
+        timed(threads, passes)  # warm-up
+        runs = [timed(threads, passes) for _ in range(5)]
+        med = statistics.median(runs)
+        out[label] = {"threads": threads, "value": unit_work * passes / med / 1e9,
+                      "median_s": med, "runs_s": [round(r, 4) for r in runs]}
+    unit = "GFLOP/s" if compute_bound else "GB/s"
+    return {"value": out["all_cores"]["value"], "unit": unit, "cores": all_threads, "kind": "oracle",
+            "sample": "%d pass(es) per run over %s; median of 5 runs after 1 warm-up" % (passes, desc),
+            "one_thread_value": out["one_thread"]["value"], "nproc": nproc, "usable_cores": usable,
+            "cpu_model": model, "runs": out}
+
+
+def host_sync_latency(wq, t, x, calls=200):
+    """Latency of the synchronous host-pointer call (blocking H2D of x, launch, D2H of y,
+    stream synchronisation): median and spread over `calls` calls after 20 warm-up calls."""
+    import statistics
+    for _ in range(20):
+        wq.wq_matmul_t(t, x)
+    lat = []
+    for _ in range(calls):
+        t0 = time.perf_counter()
+        wq.wq_matmul_t(t, x)
+        lat.append((time.perf_counter() - t0) * 1e6)
+    lat.sort()
+    return {"median_us": statistics.median(lat), "p10_us": lat[len(lat) // 10], "p90_us": lat[9 * len(lat) // 10],
+            "calls": calls, "host_bytes_in": int(x.nbytes), "host_bytes_out": int(4 * x.shape[0] * t.O)}
 
 
 if __name__ == "__main__":

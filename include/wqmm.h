@@ -200,11 +200,13 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
  * y_dev[g] = matmul(ts[g], x_dev[g], S[g]).
  * x_dev, S, y_dev: host arrays of G entries (device pointers inside);
  * S[g] == 0 skips tensor g. When every S[g] <= the GEMV limit and every row
- * fits one wave of the register GEMV, the tensors run as one launch per
- * class of row length (load slots per lane) and per 64 tensors, all on
- * hip_stream (running the classes concurrently on a second stream measured
- * slower: 39.8 vs 34.2 us for 8 int4 experts). Otherwise one wq_matmul_dev per tensor, still stream-ordered (the tiled
- * ones share the device workspace, in stream order).
+ * fits one wave of the register GEMV, up to 64 tensors run as ONE launch on
+ * hip_stream whatever their shapes (e.g. the gate, up and down projections
+ * of 8 experts: 24 tensors with 3 KiB and 1 KiB rows), the work cut into
+ * pieces of equal weight bytes when the group is created; more tensors take
+ * one launch per 64. Otherwise one wq_matmul_dev per tensor, still
+ * stream-ordered (the tiled ones share the device workspace, in stream
+ * order).
  */
 int wq_grouped_matmul_dev(wq_group *group, const float *const *x_dev, const int *S,
                           float *const *y_dev, void *hip_stream);

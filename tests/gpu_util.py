@@ -109,6 +109,20 @@ def h_bound(g, Ag, u, Au, h):
     return t + 2e-6 * (np.abs(h).astype(np.float64) + t) + 1e-30
 
 
+def assert_y(y, fmt_dn, dw, dsc, ref_h, bh, y_ref, what):
+    """Down projection of h: |y - y_ref| <= 1e-5*A_down(|h_ref| + Bh) + A_down(Bh) + ulp(y_ref)
+    + 1e-30, A_down(v)[o] = sum_i |scale[o]*q[o,i]|*v[i] (the oracle's bound magnitude on a
+    non-negative input v)."""
+    import oracle
+    _, a1 = oracle.matmul(fmt_dn, dw, dsc, (np.abs(ref_h).astype(np.float64) + bh).astype(np.float32))
+    _, a2 = oracle.matmul(fmt_dn, dw, dsc, bh.astype(np.float32))
+    by = 1e-5 * a1 + 1.0001 * a2 + ulp32(y_ref) + 1e-30
+    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+    bad = err > by
+    assert not bad.any(), "%s: %d of %d y elements out of bound; worst err/bound %.3g" % (
+        what, int(bad.sum()), bad.size, float(np.max(err / by)))
+
+
 def assert_h(h, ref, what):
     bh = h_bound(ref["g"], ref["Ag"], ref["u"], ref["Au"], ref["h"])
     err = np.abs(h.astype(np.float64) - ref["h"].astype(np.float64))
@@ -117,3 +131,42 @@ def assert_h(h, ref, what):
     assert not bad.any(), "%s: %d of %d h elements out of bound; worst err/bound %.3g at %s" % (
         what, int(bad.sum()), bad.size, float(np.max(err / bh)), np.argwhere(bad)[:3].tolist())
     return bh
+
+
+# ---------------------------------------------------------------------------------------
+# launch counting: capture a call into a HIP graph and count its kernel nodes
+
+
+def _hip():
+    import ctypes
+    lib = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has already loaded
+    lib.hipGraphGetNodes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.hipGraphGetNodes.restype = ctypes.c_int
+    lib.hipGraphNodeGetType.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+    lib.hipGraphNodeGetType.restype = ctypes.c_int
+    return lib
+
+
+def count_kernel_launches(fn) -> int:
+    """Kernel nodes recorded when fn() runs under stream capture (fn must launch on the
+    current stream and allocate nothing); the captured graph is not replayed."""
+    import ctypes
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph(keep_graph=True)
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    torch.cuda.synchronize()
+    hip = _hip()
+    graph = ctypes.c_void_p(g.raw_cuda_graph())
+    n = ctypes.c_size_t(0)
+    assert hip.hipGraphGetNodes(graph, None, ctypes.byref(n)) == 0
+    nodes = (ctypes.c_void_p * n.value)()
+    assert hip.hipGraphGetNodes(graph, nodes, ctypes.byref(n)) == 0
+    kernels = 0
+    for i in range(n.value):
+        t = ctypes.c_int(-1)
+        assert hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) == 0
+        kernels += int(t.value == 0)  # hipGraphNodeTypeKernel
+    del g
+    return kernels

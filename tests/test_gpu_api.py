@@ -165,9 +165,9 @@ def test_graph_capture_replays_match_eager():
         wq.wq_tensor_free(t)
 
 
-def test_grouped_call_capture_two_launches():
-    """A grouped call with launches of two slot counts (gate/up rows and down
-    rows), captured in a graph and replayed, matches eager."""
+def test_grouped_call_capture_mixed_row_lengths():
+    """A grouped call over rows of two slot counts (gate/up rows and down rows,
+    one launch), captured in a graph and replayed, matches eager."""
     probs = synth.moe_decode(n_experts=3, S=1)
     ts = [gu.upload(p) for p in probs]
     g = wq.wq_grouped_create(ts)
@@ -175,7 +175,7 @@ def test_grouped_call_capture_two_launches():
         xs = [torch.from_numpy(p.x).cuda() for p in probs]
         ys_eager = [torch.empty((p.S, p.O), device="cuda") for p in probs]
         ys_graph = [torch.zeros_like(y) for y in ys_eager]
-        gu.banner("grouped capture, two launches")
+        gu.banner("grouped capture, mixed row lengths")
         wq.wq_grouped_matmul_dev(g, xs, ys_eager)
         torch.cuda.synchronize()
         for p, y in zip(probs, ys_eager):

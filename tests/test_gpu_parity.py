@@ -122,6 +122,11 @@ def test_moe_decode_grouped_one_launch():
     try:
         xs = [torch.from_numpy(p.x).cuda() for p in probs]
         bufs, ys = zip(*[gu.guarded_output(p.S, p.O) for p in probs])
+        gu.banner("moe grouped G=%d: launch count" % len(probs))
+        # all 24 matmuls (3 KiB gate/up rows and 1 KiB down rows) in ONE kernel launch
+        assert gu.count_kernel_launches(lambda: wq.wq_grouped_matmul_dev(g, xs, list(ys))) == 1
+        for b in bufs:  # the capture ran nothing: reset the canaries' surroundings anyway
+            b.fill_(int(np.int32(gu.CANARY.view(np.int32))))
         gu.banner("moe grouped G=%d" % len(probs))
         wq.wq_grouped_matmul_dev(g, xs, list(ys))
         torch.cuda.synchronize()
@@ -173,8 +178,9 @@ def test_grouped_mixed_S_and_skips():
 
 @pytest.mark.parametrize("fmt,S", [(I4, 1), (I8, 2), (I2, 1), (F32, 1)])
 def test_grouped_many_problems_mixed_row_lengths(fmt, S):
-    # 70 problems (two launch chunks) whose rows need 1..4 load slots: one
-    # launch per (chunk, slot count); skipped problems in between
+    # 70 problems (two launch chunks of at most 64) whose rows need 1..4 load
+    # slots: one launch per chunk, each wave on the code path of its item's
+    # slot count; skipped problems in between
     g0 = synth.rng(77 + fmt + S)
     Is = [int(v) for v in g0.choice([3, 100, 700, 1500, 2100, 3000, 4000, 6000], size=70)]
     probs = []
@@ -190,6 +196,9 @@ def test_grouped_many_problems_mixed_row_lengths(fmt, S):
         outs = [gu.guarded_output(S, p.O) for p in probs]
         ys = [o[1] if p.x is not None else None for o, p in zip(outs, probs)]
         gu.banner("grouped 70 problems fmt=%d S=%d" % (fmt, S))
+        n = gu.count_kernel_launches(lambda: wq.wq_grouped_matmul_dev(g, xs, ys))
+        if fmt == I4:  # every row fits one wave: one launch per chunk
+            assert n == 2, n
         wq.wq_grouped_matmul_dev(g, xs, ys)
         torch.cuda.synchronize()
         for p, (b, y) in zip(probs, outs):

@@ -49,14 +49,7 @@ def device():
 silu64, ulp32, h_bound, assert_h = gu.silu64, gu.ulp32, gu.h_bound, gu.assert_h
 
 
-def assert_y(y, fmt_dn, dw, dsc, ref_h, bh, y_ref, what):
-    _, a1 = oracle.matmul(fmt_dn, dw, dsc, (np.abs(ref_h).astype(np.float64) + bh).astype(np.float32))
-    _, a2 = oracle.matmul(fmt_dn, dw, dsc, bh.astype(np.float32))
-    by = 1e-5 * a1 + 1.0001 * a2 + ulp32(y_ref) + 1e-30
-    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
-    bad = err > by
-    assert not bad.any(), "%s: %d of %d y elements out of bound; worst err/bound %.3g" % (
-        what, int(bad.sum()), bad.size, float(np.max(err / by)))
+assert_y = gu.assert_y
 
 
 class Expert:

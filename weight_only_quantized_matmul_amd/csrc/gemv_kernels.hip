@@ -635,8 +635,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
 }
 
 // PAIR: every problem is a (gate, up) pair; its work items count virtual rows.
-// KS: the slot count every item of the launch has (the runtime launches each
-// slot count on its own), so the kernel's registers are those of its rows.
+// KS > 0: every item of the launch has KS load slots, and the kernel's
+// registers are those of its rows. KS == 0: the items of one launch may need
+// any slot count 1..KMAX (rows of different lengths, e.g. the gate/up and
+// down projections of a mixture-of-experts layer in one launch); each wave
+// takes the code path compiled for its item's count, and the registers are
+// those of the longest rows present in the compiled set.
 template <int FMT, int SMAX, int LW, int KMAX, int D, bool XV, bool PAIR, int KS>
 __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -644,16 +648,26 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
     const int item_id = blockIdx.x * 4 + wave;
     if (item_id >= a.n_items) return;
     const WorkItem it = a.items[item_id];
-    if (__builtin_amdgcn_readfirstlane(it.k) != KS) return;  // a table built for another slot count
+    const int k = __builtin_amdgcn_readfirstlane(it.k);
     const int p = __builtin_amdgcn_readfirstlane(it.p);
     const int S = a.S[p];
     if (S <= 0) return;
     const GroupDesc d = a.desc[p];
     const int r0 = __builtin_amdgcn_readfirstlane(it.row_begin);
     const int nr = __builtin_amdgcn_readfirstlane(it.row_end - it.row_begin);
-    team_rows<FMT, SMAX, LW, KS, ring_depth(KMAX, D, KS), XV, false, PAIR>(
-        d.w, d.stride, d.nfull, d.scales, a.x[p], a.y[p], PAIR ? 2 * d.O : d.O, d.I, S, 1, lane, 0, r0, nr, nullptr,
-        0, 1, d.w2, d.scales2);
+#define WQ_RUN(KU)                                                                                               \
+    team_rows<FMT, SMAX, LW, KU, ring_depth(KMAX, D, KU), XV, false, PAIR>(                                    \
+        d.w, d.stride, d.nfull, d.scales, a.x[p], a.y[p], PAIR ? 2 * d.O : d.O, d.I, S, 1, lane, 0, r0, nr, nullptr, \
+        0, 1, d.w2, d.scales2)
+    if constexpr (KS > 0) {
+        if (k == KS) WQ_RUN(KS);  // (a table built for another slot count runs nothing)
+    } else {
+        if (k == 1) WQ_RUN(1);
+        if constexpr (KMAX >= 2) if (k == 2) WQ_RUN(2);
+        if constexpr (KMAX >= 3) if (k == 3) WQ_RUN(3);
+        if constexpr (KMAX >= 4) if (k == 4) WQ_RUN(4);
+    }
+#undef WQ_RUN
 }
 
 // ---- compiled shapes -------------------------------------------------------
@@ -818,7 +832,7 @@ hipError_t launch_grouped_k(const GroupedPlan &p, const GroupedArgs &a, bool xv,
             return hipGetLastError();                                                                     \
         }                                                                                                 \
     }
-    WQ_GK(1) WQ_GK(2) WQ_GK(3) WQ_GK(4)
+    WQ_GK(0) WQ_GK(1) WQ_GK(2) WQ_GK(3) WQ_GK(4)
 #undef WQ_GK
     return hipErrorInvalidValue;
 }

@@ -629,50 +629,57 @@ int create_group(wq_tensor *const *ts, wq_tensor *const *ts2, int G, wq_group **
             total += (long)vrows * gd.O * gd.stride;
         }
         if (!fits) continue;
-        // One launch per (chunk of <= kGroupMaxPerLaunch problems, slot count
-        // k): each launch runs the kernel compiled for exactly its k, whose
-        // register count (and so occupancy) is that of its own rows, and
-        // splits its own bytes over about waves_per_cu waves per CU.
-        const long target_items = std::max(1L, (long)d.cus * (g_cfg.waves_per_cu > 0 ? g_cfg.waves_per_cu : 8));
+        // One launch per chunk of <= kGroupMaxPerLaunch problems, whatever
+        // their row lengths: the chunk's weight bytes are cut into about
+        // cus * waves_per_cu items of equal bytes, each a row range of one
+        // problem (a multiple of the ring depth its slot count runs with).
+        // A chunk whose rows all need the same slot count runs the kernel
+        // compiled for exactly that count (8 waves per CU); otherwise the
+        // kernel that picks the count per item, whose registers (those of
+        // the longest rows, about 150 at S = 1) allow 3 waves per SIMD: 12
+        // items per CU fill exactly one resident round (measured on the
+        // 8-expert int4 layer, 24 matmuls: 31.4 us at 12 per CU, 37.2 at 10,
+        // 36.3 at 14, where part of the work waits for a second round).
+        auto slots = [&](const wq::GroupDesc &gd) { return (int)((gd.stride + 64L * sh.lw - 1) / (64L * sh.lw)); };
         std::vector<wq::WorkItem> items;
         for (int c0 = 0; c0 < G; c0 += wq::kGroupMaxPerLaunch) {
             const int c1 = std::min(G, c0 + wq::kGroupMaxPerLaunch);
-            for (int k = 1; k <= sh.kmax; ++k) {
-                auto slots = [&](const wq::GroupDesc &gd) {
-                    return (int)((gd.stride + 64L * sh.lw - 1) / (64L * sh.lw));
-                };
-                long seg_bytes = 0;
-                uint64_t mask = 0;
-                for (int p = c0; p < c1; ++p)
-                    if (slots(g->h_desc[p]) == k) {
-                        seg_bytes += (long)vrows * g->h_desc[p].O * g->h_desc[p].stride;
-                        mask |= 1ull << (p - c0);
-                    }
-                if (mask == 0) continue;
-                const long bytes_per_item = std::max(1L, (seg_bytes + target_items - 1) / target_items);
-                const int dk = wq::ring_depth(sh.kmax, sh.d, k);  // the kernel's ring depth for k slots
-                const int first = (int)items.size();
-                for (int p = c0; p < c1; ++p) {
-                    const auto &gd = g->h_desc[p];
-                    if (slots(gd) != k) continue;
-                    long rows = (bytes_per_item + gd.stride - 1) / gd.stride;
-                    rows = std::max<long>(dk, (rows + dk - 1) / dk * dk);
-                    const long nrows = (long)vrows * gd.O;
-                    for (long r0 = 0; r0 < nrows; r0 += rows) {
-                        wq::WorkItem it;
-                        it.p = p - c0;
-                        it.row_begin = (int)r0;
-                        it.row_end = (int)std::min<long>(nrows, r0 + rows);
-                        it.k = k;
-                        items.push_back(it);
-                    }
-                }
-                bk.seg_chunk.push_back(c0 / wq::kGroupMaxPerLaunch);
-                bk.first_item.push_back(first);
-                bk.n_items.push_back((int)items.size() - first);
-                bk.ks.push_back(k);
-                bk.mask.push_back(mask);
+            long seg_bytes = 0;
+            uint64_t mask = 0;
+            int k_first = 0;
+            bool one_k = true;
+            for (int p = c0; p < c1; ++p) {
+                seg_bytes += (long)vrows * g->h_desc[p].O * g->h_desc[p].stride;
+                mask |= 1ull << (p - c0);
+                const int k = slots(g->h_desc[p]);
+                if (p == c0) k_first = k;
+                one_k = one_k && k == k_first;
             }
+            const int wpc = g_cfg.waves_per_cu > 0 ? g_cfg.waves_per_cu : one_k ? 8 : 12;
+            const long target_items = std::max(1L, (long)d.cus * wpc);
+            const long bytes_per_item = std::max(1L, (seg_bytes + target_items - 1) / target_items);
+            const int first = (int)items.size();
+            for (int p = c0; p < c1; ++p) {
+                const auto &gd = g->h_desc[p];
+                const int k = slots(gd);
+                const int dk = wq::ring_depth(sh.kmax, sh.d, k);  // the kernel's ring depth for k slots
+                long rows = (bytes_per_item + gd.stride - 1) / gd.stride;
+                rows = std::max<long>(dk, (rows + dk - 1) / dk * dk);
+                const long nrows = (long)vrows * gd.O;
+                for (long r0 = 0; r0 < nrows; r0 += rows) {
+                    wq::WorkItem it;
+                    it.p = p - c0;
+                    it.row_begin = (int)r0;
+                    it.row_end = (int)std::min<long>(nrows, r0 + rows);
+                    it.k = k;
+                    items.push_back(it);
+                }
+            }
+            bk.seg_chunk.push_back(c0 / wq::kGroupMaxPerLaunch);
+            bk.first_item.push_back(first);
+            bk.n_items.push_back((int)items.size() - first);
+            bk.ks.push_back(one_k ? k_first : 0);
+            bk.mask.push_back(mask);
         }
         bk.plan.n_items = (int)items.size();
         rc = dev_alloc(d, (void **)&bk.d_items, items.size() * sizeof(wq::WorkItem));

@@ -225,7 +225,8 @@ struct GroupedPlan {
 
 // xv: every activation pointer 16-byte aligned and every I a multiple of 4.
 // pair: every problem is a (gate, up) pair and y receives silu(g) * u.
-// ks: the slot count (WorkItem::k, 1..p.kmax) shared by every item of the launch.
+// ks: the slot count (WorkItem::k, 1..p.kmax) shared by every item of the
+// launch, or 0 when the launch mixes slot counts (each item carries its own).
 hipError_t launch_grouped(int fmt, const GroupedPlan &p, const GroupedArgs &a, bool xv, bool pair, int ks,
                           hipStream_t st);
 
@@ -300,12 +301,12 @@ struct wq_group {
     struct Bucket {
         bool built = false;
         wq::GroupedPlan plan;
-        // per launch segment (the problems of one chunk that need the same
-        // number of load slots):
+        // per launch segment (the problems of one chunk of at most
+        // kGroupMaxPerLaunch problems, whatever their row lengths):
         std::vector<int> seg_chunk;            // chunk index (problems chunk*64 ..)
         std::vector<int> first_item;           // first item index
         std::vector<int> n_items;
-        std::vector<int> ks;                   // slot count of every item of the segment
+        std::vector<int> ks;                   // slot count of every item of the segment, or 0 (mixed)
         std::vector<uint64_t> mask;            // problems of the chunk in the segment
         wq::WorkItem *d_items = nullptr;
     } buckets[4];
