@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dense_gemv",
                     choices=["dense_gemv", "moe_decode", "moe_ffn", "moe_ffn_pipeline", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
-                             "dense_gemv_gs128", "prefill_gs128",
+                             "int2_gemv_s2", "int2_gemv_s16", "dense_gemv_s2", "dense_gemv_s4", "dense_gemv_s8",
+                             "dense_gemv_s16", "dense_gemv_gs128", "prefill_gs128",
                              "prefill"])
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -99,6 +100,10 @@ def problems_for(name):
     import synth
     if name == "dense_gemv":
         return [synth.dense_gemv(S=1)], "dense_gemv: int4 W[12288,6144] (codes U{0..15}), scales U[0.002,0.05], x N(0,1), S=1"
+    if name.startswith("dense_gemv_s"):
+        S = int(name[len("dense_gemv_s"):])
+        return [synth.dense_gemv(S=S)], ("dense_gemv: int4 W[12288,6144] (codes U{0..15}), scales U[0.002,0.05], "
+                                         "x N(0,1), S=%d" % S)
     if name == "moe_decode":
         return synth.moe_decode(), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
                                     "S=1 per expert, all 24 matmuls in one grouped launch")
@@ -269,7 +274,7 @@ def main():
             roof["issued_mfma_flops_per_launch"] = 3.0 * alg_flops
         if not compute_bound:
             roof["hbm_achieved_gbs"] = alg_bytes / per_launch / 1e9
-    elif args.workload in ("int2_gemv_s4", "int2_gemv_s8"):
+    elif all(pl.startswith("gemv") for pl in plans) and probs[0].S >= 4 and probs[0].fmt == 3:
         # int2 with S >= 4 activation rows on the register GEMV: S fp32 FMAs
         # per 0.25-byte weight element bind the vector ALUs before HBM (packed
         # fp32 FMAs are not used), so the roofline is the vector FMA rate;
@@ -283,6 +288,12 @@ def main():
         unit = "GB/s"
         roof = {"bound": "hbm", "achieved": (gu_bytes if ffn else alg_bytes) / per_launch / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        if all(pl.startswith("skinny") for pl in plans):
+            # few activation rows on the matrix cores: bounded by the weight
+            # bytes; the matrix work (three exact bf16 parts, stacked into the
+            # MFMA rows) alongside
+            roof["kernel"] = "matrix-core few-rows kernel (S <= 16), one launch"
+            roof["mfma_tflops_fp32_equivalent"] = alg_flops / per_launch / 1e12
         if ffn:
             roof["kernel"] = "fused gate/up (paired rows, silu(g)*u epilogue), all experts in one launch"
             roof["step_frac"] = alg_bytes / step_per_launch / 1e9 / HBM_PEAK_GBS

@@ -83,12 +83,34 @@ def _plan(fmt, O, I, S):
     return kind, dict(item.split("=") for item in kv)
 
 
+import contextlib
+
+
+@contextlib.contextmanager
+def forced(**env):
+    """WQ_* knobs for host-only plan queries: wq_init reads them before it looks for a
+    device (and fails here, having none)."""
+    old = {k: os.environ.get(k) for k in env}
+    try:
+        for k, v in env.items():
+            os.environ[k] = v
+        wq.lib.wq_init(None, 0)
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+        wq.lib.wq_init(None, 0)
+
+
 @pytest.mark.parametrize("fmt,O,I,S", [
-    (wq.WQ_I4, 12288, 6144, 1), (wq.WQ_I2, 16384, 8192, 1), (wq.WQ_I2, 16384, 8192, 4),
-    (wq.WQ_I2, 16384, 8192, 2), (wq.WQ_I4, 2048, 6144, 1), (wq.WQ_I4, 6144, 2048, 1),
-    (wq.WQ_I8, 256, 512, 1), (wq.WQ_F32, 256, 512, 1), (wq.WQ_I4, 256, 512, 3), (wq.WQ_I2, 256, 512, 4),
-    (wq.WQ_I8, 256, 512, 8),
+    (wq.WQ_I4, 12288, 6144, 1), (wq.WQ_I2, 16384, 8192, 1), (wq.WQ_I4, 2048, 6144, 1), (wq.WQ_I4, 6144, 2048, 1),
+    (wq.WQ_I8, 256, 512, 1), (wq.WQ_F32, 256, 512, 1), (wq.WQ_F32, 256, 512, 4),
+    # rows the matrix-core few-rows kernel cannot read in 16-byte runs (I % 4 != 0)
     (wq.WQ_I8, 7, 33, 5), (wq.WQ_F32, 1, 1, 1), (wq.WQ_I2, 3, 5, 2), (wq.WQ_F32, 100, 3000, 8),
+    (wq.WQ_I4, 255, 511, 3), (wq.WQ_I8, 255, 513, 8),
 ])
 def test_gemv_plan_invariants(fmt, O, I, S):
     kind, p = _plan(fmt, O, I, S)
@@ -111,7 +133,36 @@ def test_headline_plan_shape():
     assert kind == "gemv" and p["team"] == "1" and p["k"] == "3" and p["lw"] == "16"
 
 
-@pytest.mark.parametrize("fmt,O,I,S", [(wq.WQ_I8, 6144, 6144, 512), (wq.WQ_I4, 100, 200, 9),
+@pytest.mark.parametrize("fmt,O,I,S", [
+    (wq.WQ_I4, 12288, 6144, 2), (wq.WQ_I4, 12288, 6144, 8), (wq.WQ_I2, 16384, 8192, 4), (wq.WQ_I2, 16384, 8192, 8),
+    (wq.WQ_I2, 16384, 8192, 16), (wq.WQ_I8, 6144, 6144, 8), (wq.WQ_I8, 6144, 6144, 16), (wq.WQ_I4, 2048, 6144, 4),
+    (wq.WQ_I4, 256, 512, 3), (wq.WQ_I2, 3, 8, 2), (wq.WQ_I8, 100, 4, 11),
+])
+def test_skinny_plan_invariants(fmt, O, I, S):
+    """2 <= S <= 16 on quantized rows read in 16-byte runs: the matrix-core few-rows kernel.
+    Every output row is owned by a block, every 128-position chunk of a row by a wave,
+    and the stacked activation parts (3 S rows) fit the plan's MFMA fragments."""
+    kind, p = _plan(fmt, O, I, S)
+    assert kind == "skinny", (kind, p)
+    p = {k: int(v) for k, v in p.items()}
+    assert p["m"] == (1 if S <= 5 else 2 if S <= 10 else 3) and 3 * S <= 16 * p["m"]
+    assert p["grid"] * 16 * p["nb"] >= O and (p["grid"] - 1) * 16 * p["nb"] < O
+    stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
+    fields = stride * {wq.WQ_I8: 1, wq.WQ_I4: 2, wq.WQ_I2: 4}[fmt]
+    assert p["chunks"] * 128 >= fields and p["chunks"] % 2 == 0
+    assert p["waves"] * p["chunks_per_wave"] >= p["chunks"] and p["chunks_per_wave"] % p["ring"] == 0
+    assert p["block"] == 64 * p["waves"] <= 1024 and p["workspace"] == 0
+    assert p["waves"] == 8 or p["m"] == 1  # 16-wave blocks only with one fragment (registers)
+
+
+def test_skinny_plan_fills_the_chip_for_the_small_s_workloads():
+    for fmt, O, I in ((wq.WQ_I4, 12288, 6144), (wq.WQ_I2, 16384, 8192)):
+        for S in (2, 4, 8, 16):
+            kind, p = _plan(fmt, O, I, S)
+            assert kind == "skinny" and int(p["grid"]) == 256 and int(p["waves"]) == 8, p
+
+
+@pytest.mark.parametrize("fmt,O,I,S", [(wq.WQ_I8, 6144, 6144, 512), (wq.WQ_I4, 100, 200, 17),
                                        (wq.WQ_F32, 64, 300000, 8)])
 def test_tiled_plan(fmt, O, I, S):
     kind, p = _plan(fmt, O, I, S)
@@ -140,8 +191,11 @@ def test_tiled_plan(fmt, O, I, S):
                                           (wq.WQ_I4, 12288, 6144, 32, 3),
                                           (wq.WQ_I8, 6144, 6144, 512, 1), (wq.WQ_I4, 100, 200, 9, 1)])
 def test_tiled_split_k_plan(fmt, O, I, S, ks):
-    """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves."""
-    kind, p = _plan(fmt, O, I, S)
+    """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves
+    (S <= 16 takes the tiled path only when forced, or for rows it cannot read in
+    16-byte runs)."""
+    with forced(WQ_FORCE_PATH="tiled"):
+        kind, p = _plan(fmt, O, I, S)
     assert kind == "tiled" and int(p["ksplit"]) == ks, p
     if S <= 16 and fmt != wq.WQ_F32:  # 16 x 128 tiles of eight waves side by side along o
         assert (p["bm"], p["bn"], p["block"]) == ("16", "128", "512"), p
@@ -216,12 +270,23 @@ def test_init_without_gpu_reports_nodev():
     assert wq.lib.wq_init(None, 0) == wq.WQ_E_NODEV
 
 
-@pytest.mark.parametrize("fmt,S,kind", [(wq.WQ_I4, 4, "gemv"), (wq.WQ_I4, 5, "tiled"), (wq.WQ_I4, 8, "tiled"),
-                                        (wq.WQ_I2, 4, "gemv"), (wq.WQ_I2, 5, "tiled"), (wq.WQ_I2, 8, "tiled"),
-                                        (wq.WQ_I8, 8, "gemv"), (wq.WQ_F32, 8, "gemv")])
-def test_default_gemv_limit_per_format(fmt, S, kind):
-    """int4 and int2 leave the register GEMV above S = 4; int8 and f32 stay on it up to S = 8."""
+@pytest.mark.parametrize("fmt,S,kind", [(wq.WQ_I4, 1, "gemv"), (wq.WQ_I4, 2, "skinny"), (wq.WQ_I4, 16, "skinny"),
+                                        (wq.WQ_I4, 17, "tiled"), (wq.WQ_I2, 1, "gemv"), (wq.WQ_I2, 4, "skinny"),
+                                        (wq.WQ_I8, 1, "gemv"), (wq.WQ_I8, 8, "skinny"), (wq.WQ_F32, 8, "gemv"),
+                                        (wq.WQ_F32, 9, "tiled")])
+def test_default_path_per_format_and_s(fmt, S, kind):
+    """Quantized formats: the register GEMV for one activation row, the matrix-core
+    few-rows kernel for 2..16, the tiled kernel above; f32 weights keep the GEMV up to
+    S = 8."""
     assert _plan(fmt, 4096, 2048, S)[0] == kind
+
+
+@pytest.mark.parametrize("fmt,S", [(wq.WQ_I4, 4), (wq.WQ_I2, 4), (wq.WQ_I8, 8)])
+def test_unaligned_rows_keep_the_gemv(fmt, S):
+    """Rows the few-rows kernel cannot read in 16-byte runs (I % 4 != 0) stay on the GEMV
+    over its grouped range (S <= 4 for int4 / int2, 8 otherwise)."""
+    assert _plan(fmt, 4096, 2046, S)[0] == "gemv"
+    assert _plan(fmt, 4096, 2046, S + 1)[0] == "tiled"
 
 
 def test_upload_gs_validation_without_device():

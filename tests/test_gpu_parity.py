@@ -238,9 +238,9 @@ def test_misaligned_activations(fmt, O, I, S):
     check_problem(p, "misaligned-x", x_offset=1)
 
 
-@pytest.mark.parametrize("path", ["gemv", "tiled"])
-@pytest.mark.parametrize("fmt,O,I,S", [(I4, 300, 777, 1), (I2, 64, 1024, 8), (I8, 128, 513, 5),
-                                       (F32, 33, 100, 8), (I4, 129, 64, 2)])
+@pytest.mark.parametrize("path", ["gemv", "tiled", "skinny"])
+@pytest.mark.parametrize("fmt,O,I,S", [(I4, 300, 776, 1), (I2, 64, 1024, 8), (I8, 128, 512, 5),
+                                       (F32, 33, 100, 8), (I4, 129, 64, 2), (I8, 70, 1000, 16)])
 def test_forced_paths_agree(path, fmt, O, I, S):
     p = synth.ragged(fmt, O, I, S, seed=90 + O + S)
     try:
@@ -392,7 +392,7 @@ TEAM_CHUNK_CASES = [(I2, 5000, 8192, 1), (I4, 3001, 20000, 1), (I2, 4000, 8192, 
 
 @pytest.mark.parametrize("fmt,O,I,S", TEAM_CHUNK_CASES)
 def test_team_rows_over_several_chunks(fmt, O, I, S):
-    gu.reinit_with_env(WQ_WAVES_PER_CU=1)
+    gu.reinit_with_env(WQ_WAVES_PER_CU=1, WQ_FORCE_PATH="gemv")
     try:
         plan = wq.wq_describe_plan(fmt, O, I, S)
         fields = dict(kv.split("=") for kv in plan.split()[1:])
@@ -400,7 +400,7 @@ def test_team_rows_over_several_chunks(fmt, O, I, S):
         p = synth.ragged(fmt, O, I, S, seed=9100 + fmt * 10 + S)
         check_problem(p, "team-chunks")
     finally:
-        gu.reinit_with_env(WQ_WAVES_PER_CU=None)
+        gu.reinit_with_env(WQ_WAVES_PER_CU=None, WQ_FORCE_PATH=None)
 
 
 # ---------------------------------------------------------------------------------------

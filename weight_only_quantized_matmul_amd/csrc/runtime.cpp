@@ -48,7 +48,7 @@ struct DeviceCtx {
 };
 
 struct Config {
-    int force_path = 0;  // 0 auto, 1 gemv, 2 tiled
+    int force_path = 0;  // 0 auto, 1 gemv, 2 tiled, 3 skinny
     int gemv_max_s = -1;  // -1: per-format default (gemv_limit); else WQ_GEMV_MAX_S
     long long mem_limit = 0;  // 0: none
     int fault = 0;            // 0 none, 1 upload, 2 launch
@@ -69,6 +69,7 @@ void read_env(Config &c) {
     if (const char *v = getenv("WQ_FORCE_PATH")) {
         if (!strcmp(v, "gemv")) c.force_path = 1;
         else if (!strcmp(v, "tiled")) c.force_path = 2;
+        else if (!strcmp(v, "skinny")) c.force_path = 3;
     }
     if (const char *v = getenv("WQ_GEMV_MAX_S")) {
         int n = atoi(v);
@@ -138,25 +139,50 @@ void dev_free(DeviceCtx &d, void *p, size_t bytes) {
     }
 }
 
-// Largest S served by the register GEMV. int4 and int2 at S >= 5 run faster
-// on the tiled MFMA path (measured at S = 8: int4 12288 x 6144 72.8 us on the
-// GEMV, 42.1 us tiled; int2 16384 x 8192 59.5 us GEMV, 50.8 us tiled; at
-// S = 4 the GEMV wins, 26.7 / 27.0 us against 41-50 us); int8 and f32 keep
+// Largest S served by the register GEMV for one tensor: one activation
+// row for the quantized formats (from two rows on, the vector ALUs run S
+// FMAs per weight element while the matrix-core kernel for few rows spends
+// about two instructions per element on the decode alone); f32 weights keep
 // the GEMV up to S = 8.
 int gemv_limit(int fmt) {
+    if (g_cfg.gemv_max_s >= 0) return g_cfg.gemv_max_s;
+    return fmt == WQ_F32 ? WQ_GEMV_MAX_S : 1;
+}
+
+// Largest S for which a group runs as one grouped GEMV launch (above it,
+// one call per tensor): the grouped launch keeps the register GEMV up to
+// S = 4 for int4 / int2 and S = 8 otherwise.
+int group_gemv_limit(int fmt) {
     if (g_cfg.gemv_max_s >= 0) return g_cfg.gemv_max_s;
     return (fmt == WQ_I4 || fmt == WQ_I2) ? 4 : WQ_GEMV_MAX_S;
 }
 
-// Which path a call takes. Returns 1 (gemv) or 2 (tiled).
+// Which path a call takes: 1 (register GEMV), 2 (tiled), 3 (matrix-core
+// kernel for few rows). x_vec: x is 16-byte aligned (the few-rows kernel
+// reads it in 16-byte runs and also needs I % 4 == 0).
 // Group-scaled tensors split each row over a team of one-slot waves (their
-// natural-order rows stage activations less efficiently; measured faster).
-int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool split = false) {
-    if (g_cfg.force_path != 2 && S <= gemv_limit(fmt)) {
+// natural-order rows stage activations less efficiently; measured faster)
+// and never take the few-rows kernel.
+int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool split = false, bool x_vec = true,
+                wq::SkinnyPlan *sp = nullptr) {
+    auto skinny_ok = [&]() {
+        if (split || !x_vec) return false;
+        const wq::SkinnyPlan p = wq::plan_skinny(fmt, O, I, S, cus);
+        if (sp) *sp = p;
+        return p.ok;
+    };
+    if (g_cfg.force_path == 3 && skinny_ok()) return 3;
+    if (g_cfg.force_path != 2 && g_cfg.force_path != 3 && S <= gemv_limit(fmt)) {
         *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
         if (gp->ok) return 1;
     }
     if (g_cfg.force_path == 1) {
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
+        if (gp->ok) return 1;
+    }
+    if (g_cfg.force_path == 0 && skinny_ok()) return 3;
+    // x misaligned or I % 4 != 0: the register GEMV keeps its grouped range
+    if (g_cfg.force_path == 0 && S <= group_gemv_limit(fmt)) {
         *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
         if (gp->ok) return 1;
     }
@@ -200,7 +226,24 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
                size_t fixed_cap = 0) {
     DeviceCtx &d = g_dev[t->device];
     wq::GemvPlan gp;
-    if (choose_path(t->fmt, t->O, t->I, S, d.cus, &gp, t->gs > 0) == 1) {
+    wq::SkinnyPlan skp;
+    const bool x_vec = ((uintptr_t)x & 15) == 0;
+    const int path = choose_path(t->fmt, t->O, t->I, S, d.cus, &gp, t->gs > 0, x_vec, &skp);
+    if (path == 3) {
+        wq::SkinnyArgs a;
+        a.w = t->d_w;
+        a.scales = t->d_scales;
+        a.x = x;
+        a.y = y;
+        a.stride = t->stride;
+        a.nfull = t->nfull;
+        a.O = t->O;
+        a.I = t->I;
+        a.S = S;
+        a.chunks_per_wave = skp.chunks_per_wave;
+        return hip_status(wq::launch_skinny(t->fmt, skp, a, st));
+    }
+    if (path == 1) {
         wq::GemvArgs a;
         a.w = t->d_w;
         a.scales = t->d_scales;
@@ -699,13 +742,20 @@ int create_group(wq_tensor *const *ts, wq_tensor *const *ts2, int G, wq_group **
 }
 
 // One expert's gated front half: h[S, O] = silu(gate . x) * (up . x).
-// S within the GEMV limit and one scale per row: one paired-row launch.
-// Otherwise gate -> h and up -> u (in the device workspace, after the tiled
-// planes) as two ordinary matmuls, then the in-place activation kernel.
+// S within the grouped GEMV limit and one scale per row: one paired-row
+// launch (both dot products of an output from one read of x). Otherwise
+// gate -> h and up -> u (in the device workspace, after the tiled planes
+// when the matmuls take the tiled path) as two ordinary matmuls, then the
+// in-place activation kernel.
 int run_swiglu(const wq_tensor *gt, const wq_tensor *ut, const float *x, int S, float *h, hipStream_t st) {
     DeviceCtx &d = g_dev[gt->device];
     wq::GemvPlan gp;
-    if (gt->gs == 0 && choose_path(gt->fmt, 2 * gt->O, gt->I, S, d.cus, &gp) == 1) {
+    bool paired = false;
+    if (gt->gs == 0 && g_cfg.force_path != 2 && g_cfg.force_path != 3 && S <= group_gemv_limit(gt->fmt)) {
+        gp = wq::plan_gemv(gt->fmt, 2 * gt->O, gt->I, S, d.cus, g_cfg.waves_per_cu);
+        paired = gp.ok;
+    }
+    if (paired) {
         wq::GemvArgs a;
         a.w = gt->d_w;
         a.scales = gt->d_scales;
@@ -726,8 +776,8 @@ int run_swiglu(const wq_tensor *gt, const wq_tensor *ut, const float *x, int S, 
         a.rows_per_team = gp.rows_per_team;
         return hip_status(wq::launch_gemv(gp, a, st));
     }
-    size_t planes = 0;
-    if (choose_path(gt->fmt, gt->O, gt->I, S, d.cus, &gp) == 2)
+    size_t planes = 0;  // the path run_matmul will take for gate and up (same shape and x)
+    if (choose_path(gt->fmt, gt->O, gt->I, S, d.cus, &gp, gt->gs > 0, ((uintptr_t)x & 15) == 0) == 2)
         planes = wq::plan_tiled(gt->fmt, gt->O, gt->I, S, g_cfg.tiled_mode, g_cfg.tiled_shape, gt->gs).ws_bytes;
     const size_t off = (size_t)wq::round_up((long)planes, 256);
     uint16_t *ws = nullptr;
@@ -759,8 +809,8 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
     DeviceGuard guard(g->device);
     const int bucket = wq::gemv_smax_bucket(smax);
     const int bi = bucket == 1 ? 0 : bucket == 2 ? 1 : bucket == 4 ? 2 : bucket == 8 ? 3 : -1;
-    const bool one_launch = !g->has_gs && g_cfg.force_path != 2 && smax <= gemv_limit(g->fmt) && bi >= 0 &&
-                            g->buckets[bi].plan.ok;
+    const bool one_launch = !g->has_gs && g_cfg.force_path != 2 && g_cfg.force_path != 3 &&
+                            smax <= group_gemv_limit(g->fmt) && bi >= 0 && g->buckets[bi].plan.ok;
     if (!one_launch) {
         for (int i = 0; i < g->G; ++i) {
             if (S[i] == 0) continue;
@@ -902,9 +952,15 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
         return WQ_OK;
     }
     wq::GemvPlan gp;
-    if (choose_path(fmt, O, I, S, cus, &gp) == 1) {
+    wq::SkinnyPlan sp;
+    const int path = choose_path(fmt, O, I, S, cus, &gp, false, true, &sp);
+    if (path == 1) {
         snprintf(buf, buflen, "gemv fmt=%d smax=%d lw=%d kmax=%d k=%d team=%d d=%d rows_per_team=%d grid=%d block=%d",
                  fmt, gp.smax, gp.lw, gp.kmax, gp.k, gp.team, gp.d, gp.rows_per_team, gp.grid, gp.block);
+    } else if (path == 3) {
+        snprintf(buf, buflen,
+                 "skinny fmt=%d m=%d nb=%d waves=%d ring=%d chunks=%d chunks_per_wave=%d grid=%d block=%d workspace=0",
+                 fmt, sp.m, sp.nb, sp.waves, sp.ring, sp.nchunks, sp.chunks_per_wave, sp.grid, 64 * sp.waves);
     } else {
         const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S, g_cfg.tiled_mode, g_cfg.tiled_shape);
         snprintf(buf, buflen,

@@ -277,6 +277,34 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs =
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Few activation rows (S <= 16) on the matrix cores: one launch, no
+// workspace (skinny_kernels.hip). Needs x 16-byte aligned and I % 4 == 0.
+
+struct SkinnyArgs {
+    const uint8_t *w;
+    const float *scales;
+    const float *x;
+    float *y;
+    long stride;
+    int nfull;
+    int O, I, S;
+    int chunks_per_wave;  // 128-position chunks each wave streams (a multiple of the ring)
+};
+
+struct SkinnyPlan {
+    bool ok = false;
+    int m = 0;       // stacked operand fragments: 1 (S <= 5), 2 (S <= 10), 3 (S <= 16)
+    int nb = 0;      // 16-row output blocks per block
+    int waves = 0;   // waves per block, each streaming its own chunks of the rows
+    int ring = 0;    // chunks of loads in flight per wave
+    int grid = 0;
+    int nchunks = 0;          // chunks per row (even)
+    int chunks_per_wave = 0;
+};
+SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus);
+hipError_t launch_skinny(int fmt, const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Stream-read calibration: `waves` waves (a multiple of 4) each read one
 // contiguous chunk of the buffer with `loads` 1 KiB loads in flight; out
 // receives 64 words per wave.
