@@ -150,16 +150,19 @@ def test_skinny_plan_invariants(fmt, O, I, S):
     stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
     fields = stride * {wq.WQ_I8: 1, wq.WQ_I4: 2, wq.WQ_I2: 4}[fmt]
     assert p["chunks"] * 128 >= fields and p["chunks"] % 2 == 0
-    assert p["waves"] * p["chunks_per_wave"] >= p["chunks"] and p["chunks_per_wave"] % p["ring"] == 0
+    assert p["waves"] * p["chunks_per_wave"] >= p["chunks"] and p["chunks_per_wave"] % 2 == 0
+    assert p["ring"] in (2, 4, 6)
     assert p["block"] == 64 * p["waves"] <= 1024 and p["workspace"] == 0
-    assert p["waves"] == 8 or p["m"] == 1  # 16-wave blocks only with one fragment (registers)
+    assert p["waves"] == 8 or p["m"] <= 2  # 16-wave blocks only with at most two fragments (registers)
 
 
 def test_skinny_plan_fills_the_chip_for_the_small_s_workloads():
     for fmt, O, I in ((wq.WQ_I4, 12288, 6144), (wq.WQ_I2, 16384, 8192)):
         for S in (2, 4, 8, 16):
             kind, p = _plan(fmt, O, I, S)
-            assert kind == "skinny" and int(p["grid"]) == 256 and int(p["waves"]) == 8, p
+            assert kind == "skinny" and int(p["grid"]) >= 256 and int(p["waves"]) == 8, p
+            if S <= 8:  # one block per CU
+                assert int(p["grid"]) == 256, p
 
 
 @pytest.mark.parametrize("fmt,O,I,S", [(wq.WQ_I8, 6144, 6144, 512), (wq.WQ_I4, 100, 200, 17),

@@ -56,6 +56,7 @@ struct Config {
     int waves_per_cu = 0;  // 0: per kernel shape (GEMV) / 8 (grouped launches)
     int tiled_mode = wq::kTiledBF16X3;  // quantized weights: exact bf16 split of x
     int tiled_shape = 0;                // 0: by size; else bm * 1000000 + bn * 1000 + bk
+    int skinny_ring = 0;                // 0: default; else chunks of loads in flight (2, 4, 6)
 };
 
 DeviceCtx g_dev[WQ_MAX_DEVICES];
@@ -89,6 +90,7 @@ void read_env(Config &c) {
         int bm = 0, bn = 0, bk = 0;
         if (sscanf(v, "%dx%dx%d", &bm, &bn, &bk) == 3) c.tiled_shape = bm * 1000000 + bn * 1000 + bk;
     }
+    if (const char *v = getenv("WQ_SKINNY_RING")) c.skinny_ring = atoi(v);
     if (const char *v = getenv("WQ_WAVES_PER_CU")) {
         int n = atoi(v);
         if (n >= 1 && n <= 32) c.waves_per_cu = n;
@@ -167,7 +169,7 @@ int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool sp
                 wq::SkinnyPlan *sp = nullptr) {
     auto skinny_ok = [&]() {
         if (split || !x_vec) return false;
-        const wq::SkinnyPlan p = wq::plan_skinny(fmt, O, I, S, cus);
+        const wq::SkinnyPlan p = wq::plan_skinny(fmt, O, I, S, cus, g_cfg.skinny_ring);
         if (sp) *sp = p;
         return p.ok;
     };
@@ -241,6 +243,7 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
         a.I = t->I;
         a.S = S;
         a.chunks_per_wave = skp.chunks_per_wave;
+        a.nchunks = skp.nchunks;
         return hip_status(wq::launch_skinny(t->fmt, skp, a, st));
     }
     if (path == 1) {
@@ -959,8 +962,9 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
                  fmt, gp.smax, gp.lw, gp.kmax, gp.k, gp.team, gp.d, gp.rows_per_team, gp.grid, gp.block);
     } else if (path == 3) {
         snprintf(buf, buflen,
-                 "skinny fmt=%d m=%d nb=%d waves=%d ring=%d chunks=%d chunks_per_wave=%d grid=%d block=%d workspace=0",
-                 fmt, sp.m, sp.nb, sp.waves, sp.ring, sp.nchunks, sp.chunks_per_wave, sp.grid, 64 * sp.waves);
+                 "skinny fmt=%d m=%d rpl=%d nb=%d waves=%d ring=%d chunks=%d chunks_per_wave=%d grid=%d block=%d "
+                 "workspace=0",
+                 fmt, sp.m, sp.rpl, sp.nb, sp.waves, sp.ring, sp.nchunks, sp.chunks_per_wave, sp.grid, 64 * sp.waves);
     } else {
         const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S, g_cfg.tiled_mode, g_cfg.tiled_shape);
         snprintf(buf, buflen,

@@ -27,13 +27,24 @@
 //    positions, and a lane's 16-byte load of one row holds, for its group
 //    of 8 positions per k-step, the codes of several consecutive k-steps;
 //    the activations are paired with the same positions.
-//  * A block of WAVES waves owns 16 * NB output rows and splits the row's
-//    128-position chunks between its waves; each wave streams its own
-//    chunks with the weight and activation loads of R chunks in flight,
-//    splits its activations into a wave-private LDS buffer laid out as MFMA
-//    operands (all 64 lanes split; no block barrier per step), and the
-//    waves' partial tiles are added through LDS at the end in fixed order
-//    (deterministic; no split-K kernel and no second launch).
+//  * A block of WAVES waves owns 16 * NB output rows and deals the rows'
+//    128-position chunks to its waves in pairs, in turn (neighbouring pairs
+//    go to different waves, so the block reads each row front to back);
+//    each wave streams its pairs with the weight and activation loads of R
+//    chunks in flight, splits its activations into a wave-private LDS
+//    buffer laid out as MFMA operands (all 64 lanes split; no block barrier
+//    per step), and the waves' partial tiles are added through LDS at the
+//    end in fixed order (deterministic; no split-K kernel and no second
+//    launch).
+//  * The operand buffer is swizzled so that both its writers (16 lanes: four
+//    stacked rows x four k-groups) and its MFMA readers (16 lanes: sixteen
+//    rows of one k-group) touch 16 distinct 16-byte bank groups, and any 8
+//    consecutive lanes 8 distinct ones (free of bank conflicts with 32 or 64
+//    banks); chunks alternate between two buffers where LDS allows, so the
+//    split of one chunk need not wait for the MFMA reads of the one before.
+#include <algorithm>
+#include <type_traits>
+
 #include "wq_internal.h"
 
 namespace wq {
@@ -58,17 +69,17 @@ template <> struct SkF<WQ_I2> { static constexpr int EPB = 4; static constexpr i
 // consecutive positions follow). int8 / int4: a lane group covers 32
 // positions of a chunk (one 32-byte / 16-byte run of its row); int2: one
 // 16-byte load of a lane group covers 64 positions, 32 of each of two chunks.
-template <int FMT> __device__ __forceinline__ long chunk_pos(long c, int g, int j) {
-    if constexpr (FMT == WQ_I2) return 256L * (c >> 1) + 64 * g + 32 * (c & 1) + 8 * j;
-    return (long)kChunk * c + 32 * g + 8 * j;
+template <int FMT> __device__ __forceinline__ int chunk_pos(int c, int g, int j) {
+    if constexpr (FMT == WQ_I2) return 256 * (c >> 1) + 64 * g + 32 * (c & 1) + 8 * j;
+    return kChunk * c + 32 * g + 8 * j;
 }
 
 // Byte offset in the row of 16-byte weight load u (0 .. LOADS2-1) of the
 // chunk pair starting at chunk c2 (even), for lane group g.
-template <int FMT> __device__ __forceinline__ long load_byte(long c2, int g, int u) {
-    if constexpr (FMT == WQ_I8) return 128L * (c2 + (u >> 1)) + 32 * g + 16 * (u & 1);
-    if constexpr (FMT == WQ_I4) return 64L * (c2 + u) + 16 * g;
-    return 64L * (c2 >> 1) + 16 * g;
+template <int FMT> __device__ __forceinline__ int load_byte(int c2, int g, int u) {
+    if constexpr (FMT == WQ_I8) return 128 * (c2 + (u >> 1)) + 32 * g + 16 * (u & 1);
+    if constexpr (FMT == WQ_I4) return 64 * (c2 + u) + 16 * g;
+    return 64 * (c2 >> 1) + 16 * g;
 }
 
 __device__ __forceinline__ uint32_t pack_hi(uint32_t lo_bits, uint32_t hi_bits) {
@@ -127,21 +138,45 @@ __device__ __forceinline__ void b_frag_i2(uint32_t w, u32x4 &lo, u32x4 &hi) {
     hi.w = pack_hi(sbyte_f32(m2, 3), sbyte_f32(m3, 3));
 }
 
-template <int M> struct SkBucket {
-    static constexpr int SMAX = M == 1 ? 5 : M == 2 ? 10 : 16;  // activation rows of the bucket
-    static constexpr int RPL = (16 * SMAX + 63) / 64;           // 8-position runs per lane per chunk
-};
+// Chunks per permuted 1 KiB block of a row (a chunk never straddles one).
+template <int FMT> constexpr int kChunksPerBlock = FMT == WQ_I8 ? 8 : FMT == WQ_I4 ? 16 : 32;
 
+// Element index of field position chunk_pos(c, g, j) + 4 q inside the
+// permuted blocks (device layout: field n of 16-byte granule lambda of a
+// block holds element 256 (n / 4) + 4 lambda + n % 4), split into a part
+// that depends on the chunk only (wave-uniform) and one that depends on
+// the lane's (g, j, q) only.
+template <int FMT> __device__ __forceinline__ int elem_chunk_part(int c) {
+    if constexpr (FMT == WQ_I4) return ((c >> 4) << 11) + ((c & 15) << 4);
+    if constexpr (FMT == WQ_I2) return ((c >> 5) << 12) + (((c >> 1) & 15) << 4) + ((c & 1) << 11);
+    return ((c >> 3) << 10) + ((c & 7) << 5);
+}
+template <int FMT> __device__ __forceinline__ int elem_lane_part(int g, int j, int q) {
+    if constexpr (FMT == WQ_I4 || FMT == WQ_I2) return (g << 2) + ((2 * j + q) << 8);
+    return (g << 3) + ((j >> 1) << 2) + ((2 * (j & 1) + q) << 8);
+}
+
+// 16-byte slot of stacked row rho, k-step j and k-group g in an operand
+// buffer (1 KiB per fragment of 16 rows and k-step; the MFMA's lane li + 16 g
+// reads row li of k-group g): inside its k-group the row is rotated by
+// S j + 4 g (see the bank-conflict note at the top).
+__device__ __forceinline__ int opnd_slot(int rho, int j, int g, int S) {
+    return ((rho >> 4) * 4 + j) * 64 + 16 * g + (((rho & 15) + S * j + 4 * g) & 15);
+}
+
+// M: stacked operand fragments (3 S <= 16 M); RPL: 8-position activation
+// runs per lane per chunk (16 S runs per chunk, so RPL = ceil(S / 4));
 // NB: 16-row output blocks per wave (and block); WAVES: waves per block,
-// each streaming its own chunks; R: chunks of loads in flight (even).
-template <int FMT, int M, int NB, int WAVES, int R>
+// each streaming its own chunks; R: chunks of loads in flight (even);
+// NBUF: operand buffers per wave (1 or 2).
+template <int FMT, int M, int RPL, int NB, int WAVES, int R, int NBUF>
 __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     static_assert(R % 2 == 0, "the load ring advances by chunk pairs");
-    constexpr int RPL = SkBucket<M>::RPL;
+    static_assert(NBUF == 1 || NBUF == 2, "one or two operand buffers");
     constexpr int L2 = SkF<FMT>::LOADS2;
-    constexpr int ABUF = M * 4 * 1024;                // bytes of one wave's operand buffer
+    constexpr int ABUF = M * 4 * 1024;                // bytes of one operand buffer
     constexpr int RED = WAVES * NB * M * 1024;        // bytes of the partial tiles
-    constexpr int LDS = WAVES * ABUF > RED ? WAVES * ABUF : RED;
+    constexpr int LDS = WAVES * NBUF * ABUF > RED ? WAVES * NBUF * ABUF : RED;
     __shared__ __align__(16) uint8_t lds[LDS];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -149,57 +184,86 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     const int li = lane & 15, g = lane >> 4;
     const int S = a.S, O = a.O, I = a.I;
     const int o0 = blockIdx.x * (16 * NB);
-    const long stride = a.stride;
-    const long c_begin = (long)wave * a.chunks_per_wave;
-    const int npairs = a.chunks_per_wave / 2;
+    const int stride = (int)a.stride;
+    // chunk pairs are dealt to the waves in turn (pair k of this wave is
+    // pair wave + WAVES k of the row), so at any time the block's waves read
+    // neighbouring pieces of its rows; pairs past the row are skipped and
+    // their loads re-read the row's last pair (cache hits, never used)
+    const int np_row = a.nchunks / 2;
+    const int npairs = a.chunks_per_wave / 2;  // pairs per wave
+    const int c_full = a.nfull * kChunksPerBlock<FMT>;  // chunks inside the permuted blocks
+    auto pair_c2 = [&](int k) { return 2 * min(wave + WAVES * k, np_row - 1); };
+    auto pair_live = [&](int k) { return wave + WAVES * k < np_row; };
 
-    // the rows this lane reads (clamped: rows past O are read, never stored)
-    const uint8_t *rowp[NB];
+    // 32-bit byte offsets from the tensor's base (O * stride < 2^31): the
+    // rows this lane reads (clamped: rows past O are read, never stored)
+    uint32_t roff[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) rowp[b] = a.w + (long)min(o0 + 16 * b + li, O - 1) * stride;
+    for (int b = 0; b < NB; ++b) roff[b] = (uint32_t)min(o0 + 16 * b + li, O - 1) * (uint32_t)stride;
+    const uint32_t lane_w = (FMT == WQ_I8 ? 32u : 16u) * (uint32_t)g;  // lane group's bytes in a chunk
+    const uint32_t last16 = (uint32_t)stride - 16u;
 
-    // operand buffer: rows >= 3S stay zero for the whole call
-    uint8_t *abuf = lds + wave * ABUF;
+    // operand buffers: rows >= 3S stay zero for the whole call
+    u32x4 *abuf = reinterpret_cast<u32x4 *>(lds + wave * NBUF * ABUF);
 #pragma unroll
-    for (int i = 0; i < M * 4; ++i) reinterpret_cast<u32x4 *>(abuf)[i * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NBUF * M * 4; ++i) abuf[i * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+    // the MFMA read slots of this lane, per k-step (fragment m adds 256 m)
+    int rd_slot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rd_slot[j] = opnd_slot(li, j, g, S);
+
+    // run index t = r % 4 + 4 (r / 16) of run r = lane + 64 i, k-group
+    // (r / 4) % 4: sixteen lanes hold four runs of four k-groups; run t is
+    // activation row t % S of k-step t / S (runs t >= 4 S are loaded and
+    // never stored)
+    int run_g[RPL], run_j[RPL], run_slot[RPL][3];
+    uint32_t run_x[RPL][2];   // activation offset (floats) of the run inside the permuted blocks, less the chunk part
+    uint32_t run_xn[RPL][2];  // the same in natural order (past the blocks), less the chunk's first position
+    bool run_live[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int t = (lane & 3) + 4 * (lane >> 4) + 16 * i;
+        const int rs = t % S;
+        run_g[i] = (lane >> 2) & 3;
+        run_j[i] = min(t / S, 3);
+        run_live[i] = t < 4 * S;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) run_slot[i][p] = opnd_slot(p * S + rs, run_j[i], run_g[i], S);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            run_x[i][q] = (uint32_t)(rs * I + elem_lane_part<FMT>(run_g[i], run_j[i], q));
+            run_xn[i][q] = (uint32_t)(rs * I + (int)(chunk_pos<FMT>(0, run_g[i], run_j[i]) + 4 * q));
+        }
+    }
 
     // ---- loads of one chunk pair: weights (NB x L2 16-byte loads) and the
     // activation runs of both chunks (2 x RPL runs of two 16-byte loads).
     // Every load is issued unconditionally (addresses clamped inside the
     // row / the activations), so the compiler's wait counts stay exact.
-    const long last16 = stride - 16;
-    auto load_w = [&](u32x4 (&wv)[L2][NB], long c2) {
+    auto load_w = [&](u32x4 (&wv)[L2][NB], int c2) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < L2; ++u) {
-            const long off = min(load_byte<FMT>(c2, g, u), last16);
+            const uint32_t off = min((uint32_t)load_byte<FMT>(c2, 0, u) + lane_w, last16);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) wv[u][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rowp[b] + off));
+            for (int b = 0; b < NB; ++b)
+                wv[u][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.w + (roff[b] + off)));
         }
     };
-    // run r = lane + 64 i of a chunk: g fastest (four lanes read 64
-    // contiguous bytes of an activation row), then the row s, then the
-    // k-step j (runs r >= 16 S are loaded, clamped, and never stored)
-    int run_s[RPL], run_g[RPL], run_j[RPL];
+    const uint32_t xlast = (uint32_t)(S * I - 4);
+    auto load_x = [&](f32x4 (&xv)[2][RPL][2], int c2) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const int r = lane + 64 * i;
-        run_g[i] = r & 3;
-        run_s[i] = (r >> 2) % S;
-        run_j[i] = min((r >> 2) / S, 3);
-    }
-    auto load_x = [&](f32x4 (&xv)[2][RPL][2], long c2) {
+        for (int h = 0; h < 2; ++h) {
+            const int c = c2 + h;
+            const bool full = c < c_full;  // wave-uniform
+            const uint32_t cp = full ? (uint32_t)elem_chunk_part<FMT>(c) : (uint32_t)chunk_pos<FMT>(c, 0, 0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                const long P = chunk_pos<FMT>(c2 + h, run_g[i], run_j[i]);
-                const float *xs = a.x + (long)run_s[i] * I;
+            for (int i = 0; i < RPL; ++i)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const long e = elem_of_pos4(FMT, P + 4 * q, a.nfull);
-                    xv[h][i][q] = *reinterpret_cast<const f32x4 *>(xs + min(e, (long)I - 4));
+                    const uint32_t e = min(cp + (full ? run_x[i][q] : run_xn[i][q]), xlast);
+                    xv[h][i][q] = *reinterpret_cast<const f32x4 *>(a.x + e);
                 }
-            }
+        }
     };
 
     f32x4 acc[NB][M];
@@ -213,27 +277,37 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     f32x4 xring[RP][2][RPL][2];
 #pragma unroll
     for (int p = 0; p < RP; ++p) {
-        load_x(xring[p], c_begin + 2 * p);
-        load_w(wring[p], c_begin + 2 * p);
+        load_x(xring[p], pair_c2(p));
+        load_w(wring[p], pair_c2(p));
     }
 
-    // ---- one chunk: split its activations into the operand buffer, then
-    // 4 k-steps x NB o-blocks x M stacked fragments of MFMAs
-    auto do_chunk = [&](const f32x4 (&xv)[RPL][2], const u32x4 (&wv)[L2][NB], long c, int h) {
+    // ---- one chunk: split its activations into an operand buffer, then
+    // 4 k-steps x NB o-blocks x M stacked fragments of MFMAs. Inside the
+    // permuted blocks (FULL) every run lies inside the row (I % 4 == 0 and
+    // the blocks hold exactly the first elements); past them (natural
+    // order) a run lies inside or outside [0, I) and is masked. The same
+    // wave writes and reads each buffer: its LDS operations complete in
+    // order, and the buffer's accesses may alias, so the compiler keeps them
+    // in program order.
+    auto do_chunk = [&](auto full_c, const f32x4 (&xv)[RPL][2], const u32x4 (&wv)[L2][NB], int c,
+                        int h) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_c)::value;
+        u32x4 *buf = abuf + (NBUF == 2 ? h : 0) * (ABUF / 16);
+        const int cpos = chunk_pos<FMT>(c, 0, 0);
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            const int r = lane + 64 * i;
-            const int rs = run_s[i], rg = run_g[i], rj = run_j[i];
-            const long P = chunk_pos<FMT>(c, rg, rj);
             float v[8];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const long e = elem_of_pos4(FMT, P + 4 * q, a.nfull);
-                const bool in = e < I;  // a run lies inside or outside the row (I % 4 == 0)
-                v[4 * q + 0] = in ? xv[i][q].x : 0.0f;
-                v[4 * q + 1] = in ? xv[i][q].y : 0.0f;
-                v[4 * q + 2] = in ? xv[i][q].z : 0.0f;
-                v[4 * q + 3] = in ? xv[i][q].w : 0.0f;
+                f32x4 t = xv[i][q];
+                if constexpr (!FULL) {
+                    const bool in = cpos + chunk_pos<FMT>(0, run_g[i], run_j[i]) + 4 * q < I;
+                    t = in ? t : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+                v[4 * q + 0] = t.x;
+                v[4 * q + 1] = t.y;
+                v[4 * q + 2] = t.z;
+                v[4 * q + 3] = t.w;
             }
             uint32_t pl[3][8];
 #pragma unroll
@@ -245,26 +319,18 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
                 pl[1][e] = mb;
                 pl[2][e] = __float_as_uint(r1 - __uint_as_float(mb));  // exact, <= 8 significant bits
             }
-            if (r < 16 * S) {
+            if (run_live[i]) {
 #pragma unroll
-                for (int p = 0; p < 3; ++p) {
-                    const int rho = p * S + rs;
-                    const int slot = ((rho >> 4) * 4 + rj) * 64 + (rho & 15) + 16 * rg;
-                    reinterpret_cast<u32x4 *>(abuf)[slot] =
-                        u32x4{pack_hi(pl[p][0], pl[p][1]), pack_hi(pl[p][2], pl[p][3]), pack_hi(pl[p][4], pl[p][5]),
-                              pack_hi(pl[p][6], pl[p][7])};
-                }
+                for (int p = 0; p < 3; ++p)
+                    buf[run_slot[i][p]] = u32x4{pack_hi(pl[p][0], pl[p][1]), pack_hi(pl[p][2], pl[p][3]),
+                                                pack_hi(pl[p][4], pl[p][5]), pack_hi(pl[p][6], pl[p][7])};
             }
         }
-        // the same wave reads the buffer back: LDS operations of one wave
-        // complete in order; keep the compiler from moving reads above writes
-        asm volatile("" ::: "memory");
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             bf16x8 av[M];
 #pragma unroll
-            for (int m = 0; m < M; ++m)
-                av[m] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4 *>(abuf)[(m * 4 + j) * 64 + lane]);
+            for (int m = 0; m < M; ++m) av[m] = __builtin_bit_cast(bf16x8, buf[m * 256 + rd_slot[j]]);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 u32x4 bw;
@@ -288,30 +354,41 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
                     acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, acc[b][m], 0, 0, 0);
             }
         }
-        asm volatile("" ::: "memory");  // the next chunk's writes stay after these reads
+    };
+    auto chunk = [&](const f32x4 (&xv)[RPL][2], const u32x4 (&wv)[L2][NB], int c, int h)
+        __attribute__((always_inline)) {
+        if (c < c_full) do_chunk(std::true_type{}, xv, wv, c, h);  // wave-uniform branch
+        else do_chunk(std::false_type{}, xv, wv, c, h);
     };
 
-    int pp = 0;
-    for (; pp + RP < npairs; pp += RP) {
+    // (the pair checks are wave-uniform: skipping work changes no load count)
+    int kk = 0;
+    for (; kk + RP < npairs; kk += RP) {
 #pragma unroll
         for (int p = 0; p < RP; ++p) {
-            const long c2 = c_begin + 2 * (pp + p);
-            do_chunk(xring[p][0], wring[p], c2, 0);
-            do_chunk(xring[p][1], wring[p], c2 + 1, 1);
-            // refill this slot with the chunk pair R chunks ahead
-            load_x(xring[p], c2 + R);
-            load_w(wring[p], c2 + R);
+            const int k = kk + p;
+            if (pair_live(k)) {
+                const int c2 = 2 * (wave + WAVES * k);
+                chunk(xring[p][0], wring[p], c2, 0);
+                chunk(xring[p][1], wring[p], c2 + 1, 1);
+            }
+            // refill this slot with the wave's pair RP pairs ahead
+            load_x(xring[p], pair_c2(k + RP));
+            load_w(wring[p], pair_c2(k + RP));
         }
     }
 #pragma unroll
-    for (int p = 0; p < RP; ++p) {  // the last pairs: nothing left to load
-        const long c2 = c_begin + 2 * (pp + p);
-        do_chunk(xring[p][0], wring[p], c2, 0);
-        do_chunk(xring[p][1], wring[p], c2 + 1, 1);
+    for (int p = 0; p < RP; ++p) {  // the last round: nothing left to load
+        const int k = kk + p;
+        if (k < npairs && pair_live(k)) {
+            const int c2 = 2 * (wave + WAVES * k);
+            chunk(xring[p][0], wring[p], c2, 0);
+            chunk(xring[p][1], wring[p], c2 + 1, 1);
+        }
     }
 
     // ---- add the waves' partial tiles (and the three planes) in fixed order
-    __syncthreads();  // every wave is done with its operand buffer
+    __syncthreads();  // every wave is done with its operand buffers
     float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -336,60 +413,113 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     }
 }
 
-template <int FMT, int M>
-hipError_t launch_m(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st) {
+} // namespace
+
+// Deepest ring (chunks of loads in flight per wave) whose kernel keeps every
+// value in registers (no spills at two waves per SIMD), from the compiled
+// register counts: the ring holds a chunk pair's weights (LOADS2 x NB
+// 16-byte loads) and activation runs (2 x RPL x 32 bytes); 0: not compiled.
+constexpr int skinny_max_ring(int fmt, int m, int rpl, int nb) {
+    // [format][(m, rpl) = (1,1) (1,2) (2,2) (2,3) (3,3) (3,4)][nb - 1]
+    constexpr signed char kRing[3][6][4] = {
+        {{6, 6, 6, 4}, {6, 6, 4, 2}, {6, 4, 2, 2}, {4, 2, 2, 2}, {4, 2, 2, 0}, {4, 2, 0, 0}},   // int8
+        {{6, 6, 6, 6}, {6, 6, 6, 4}, {6, 6, 4, 4}, {6, 4, 2, 2}, {6, 4, 2, 0}, {4, 2, 2, 0}},   // int4
+        {{6, 6, 6, 6}, {6, 6, 6, 6}, {6, 6, 6, 4}, {6, 4, 4, 2}, {6, 4, 2, 0}, {4, 2, 2, 0}}};  // int2
+    const int f = fmt == WQ_I8 ? 0 : fmt == WQ_I4 ? 1 : fmt == WQ_I2 ? 2 : -1;
+    const int mr = m * 10 + rpl;
+    const int k = mr == 11 ? 0 : mr == 12 ? 1 : mr == 22 ? 2 : mr == 23 ? 3 : mr == 33 ? 4 : mr == 34 ? 5 : -1;
+    return f < 0 || k < 0 || nb < 1 || nb > 4 ? 0 : kRing[f][k][nb - 1];
+}
+
+// LDS of a block: the waves' operand buffers (nbuf each), reused for the
+// partial tiles.
+constexpr int skinny_lds_bytes(int m, int nb, int waves, int nbuf) {
+    return waves * nbuf * m * 4096 > waves * nb * m * 1024 ? waves * nbuf * m * 4096 : waves * nb * m * 1024;
+}
+// 16 waves of one 16-row block (for few output rows) keep every value in
+// registers at four waves per SIMD (from the compiled register counts).
+constexpr bool skinny_wide_ok(int fmt, int m, int rpl) {
+    return (m == 1 && rpl == 1) || (m == 2 && rpl == 2) || (m == 1 && rpl == 2 && fmt != WQ_I8) ||
+           (m == 2 && rpl == 3 && fmt == WQ_I2);
+}
+// Two operand buffers per wave where they fit in the CU's 160 KiB of LDS.
+constexpr int skinny_nbuf(int m, int nb, int waves) {
+    return skinny_lds_bytes(m, nb, waves, 2) <= 160 * 1024 ? 2 : 1;
+}
+
+namespace {
+
+template <int FMT, int M, int RPL>
+hipError_t launch_mr(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st) {
     const dim3 grid(p.grid), block(64 * p.waves);
-#define WQ_SK(NB_, W_, R_)                                                                      \
-    if (p.nb == NB_ && p.waves == W_ && p.ring == R_) {                                         \
-        hipLaunchKernelGGL((skinny_kernel<FMT, M, NB_, W_, R_>), grid, block, 0, st, a);       \
-        return hipGetLastError();                                                               \
+#define WQ_SK(NB_, W_, R_)                                                                           \
+    if (p.nb == NB_ && p.waves == W_ && p.ring == R_) {                                              \
+        hipLaunchKernelGGL((skinny_kernel<FMT, M, RPL, NB_, W_, R_, skinny_nbuf(M, NB_, W_)>), grid, \
+                           block, 0, st, a);                                                         \
+        return hipGetLastError();                                                                    \
     }
-    // (16-wave blocks leave 128 registers per lane: one fragment only)
-    if constexpr (M == 1) WQ_SK(1, 16, 2)
-    WQ_SK(1, 8, 2) WQ_SK(2, 8, 2) WQ_SK(3, 8, 2)
-    if constexpr (!(FMT == WQ_I8 && M == 3)) WQ_SK(4, 8, 2)  // (int8, three fragments: 4 blocks spill)
+#define WQ_SKR(NB_, R_) \
+    if constexpr (skinny_max_ring(FMT, M, RPL, NB_) >= R_) WQ_SK(NB_, 8, R_)
+    WQ_SKR(1, 2) WQ_SKR(2, 2) WQ_SKR(3, 2) WQ_SKR(4, 2)
+    WQ_SKR(1, 4) WQ_SKR(2, 4) WQ_SKR(3, 4) WQ_SKR(4, 4)
+    WQ_SKR(1, 6) WQ_SKR(2, 6) WQ_SKR(3, 6) WQ_SKR(4, 6)
+#define WQ_SKW(NB_, W_) \
+    if constexpr (skinny_wide_ok(FMT, M, RPL)) WQ_SK(NB_, W_, 2)
+    WQ_SKW(1, 16)
+#undef WQ_SKW
+#undef WQ_SKR
 #undef WQ_SK
     return hipErrorInvalidValue;
 }
 
 template <int FMT>
 hipError_t launch_f(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st) {
-    if (p.m == 1) return launch_m<FMT, 1>(p, a, st);
-    if (p.m == 2) return launch_m<FMT, 2>(p, a, st);
-    return launch_m<FMT, 3>(p, a, st);
+    switch (p.m * 10 + p.rpl) {
+    case 11: return launch_mr<FMT, 1, 1>(p, a, st);
+    case 12: return launch_mr<FMT, 1, 2>(p, a, st);
+    case 22: return launch_mr<FMT, 2, 2>(p, a, st);
+    case 23: return launch_mr<FMT, 2, 3>(p, a, st);
+    case 33: return launch_mr<FMT, 3, 3>(p, a, st);
+    case 34: return launch_mr<FMT, 3, 4>(p, a, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 } // namespace
 
-SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus) {
+SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring) {
     SkinnyPlan p;
     if ((fmt != WQ_I8 && fmt != WQ_I4 && fmt != WQ_I2) || O <= 0 || I < 4 || I % 4 != 0 || S < 1 || S > 16)
         return p;
     p.m = S <= 5 ? 1 : S <= 10 ? 2 : 3;
+    p.rpl = (S + 3) / 4;
     const long stride = round_up(row_bytes(fmt, I), kRowAlign);
     const long npos = stride * elems_per_byte(fmt);
     long nchunks = (npos + kChunk - 1) / kChunk;
     nchunks = round_up(nchunks, 2);
-    // output blocks: as many rows per block as still gives every CU a block
-    const int nbmax = (fmt == WQ_I8 && p.m == 3) ? 3 : 4;
+    // output blocks: as many rows per block (of the compiled ones) as still
+    // gives every CU a block
     p.nb = 0;
-    for (int nb = nbmax; nb >= 1; --nb)
-        if ((O + 16 * nb - 1) / (16 * nb) >= cus) {
+    for (int nb = 4; nb >= 1; --nb)
+        if (skinny_max_ring(fmt, p.m, p.rpl, nb) > 0 && (O + 16 * nb - 1) / (16 * nb) >= cus) {
             p.nb = nb;
             break;
         }
+    p.waves = 8;
     if (p.nb == 0) {  // few output rows: more waves per block share each row's chunks
         p.nb = 1;
-        p.waves = p.m == 1 ? 16 : 8;
-    } else {
-        p.waves = 8;
+        if (skinny_wide_ok(fmt, p.m, p.rpl)) p.waves = 16;
     }
-    p.ring = 2;
+    // two chunks of loads in flight (the fastest measured), or a deeper
+    // spill-free ring when asked for
+    const int deepest = skinny_max_ring(fmt, p.m, p.rpl, p.nb);
+    p.ring = (p.waves == 8 && (ring == 4 || ring == 6)) ? std::min(ring, deepest) : 2;
     p.grid = (O + 16 * p.nb - 1) / (16 * p.nb);
     const long per_wave = (nchunks + p.waves - 1) / p.waves;
-    p.chunks_per_wave = (int)round_up(per_wave, p.ring);
+    p.chunks_per_wave = (int)round_up(per_wave, 2);
     p.nchunks = (int)nchunks;
-    p.ok = (long)p.chunks_per_wave * p.waves < (1L << 30);
+    // 32-bit offsets inside the kernel
+    p.ok = (long)O * stride < (1L << 31) && (long)S * I < (1L << 29) && nchunks * kChunk < (1L << 30);
     return p;
 }
 

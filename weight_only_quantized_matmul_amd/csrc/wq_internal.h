@@ -288,12 +288,14 @@ struct SkinnyArgs {
     long stride;
     int nfull;
     int O, I, S;
-    int chunks_per_wave;  // 128-position chunks each wave streams (a multiple of the ring)
+    int chunks_per_wave;  // 128-position chunks each wave streams (even)
+    int nchunks;          // chunks per row (even): chunks past it hold no field positions
 };
 
 struct SkinnyPlan {
     bool ok = false;
     int m = 0;       // stacked operand fragments: 1 (S <= 5), 2 (S <= 10), 3 (S <= 16)
+    int rpl = 0;     // activation runs per lane per chunk: ceil(S / 4)
     int nb = 0;      // 16-row output blocks per block
     int waves = 0;   // waves per block, each streaming its own chunks of the rows
     int ring = 0;    // chunks of loads in flight per wave
@@ -301,7 +303,9 @@ struct SkinnyPlan {
     int nchunks = 0;          // chunks per row (even)
     int chunks_per_wave = 0;
 };
-SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus);
+// ring: 4 or 6 asks for that many chunks of loads in flight per wave (capped
+// at the deepest spill-free ring; 8-wave blocks only), else 2
+SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring);
 hipError_t launch_skinny(int fmt, const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
