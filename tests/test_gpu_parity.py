@@ -250,6 +250,23 @@ def test_forced_paths_agree(path, fmt, O, I, S):
         gu.reinit_with_env(WQ_FORCE_PATH=None)
 
 
+# the few-rows matrix-core kernel by default (quantized, 2 <= S <= 16, I % 4 == 0):
+# every (fragments, runs per lane) shape, ragged O and row tails past the permuted
+# blocks, few-row plans (one 16-row block, 16 waves), and the int4 S = 8 workload size
+SKINNY_CASES = [
+    (I4, 1000, 4100, 3), (I2, 777, 8196, 5), (I8, 515, 2052, 7), (I4, 2049, 1028, 9),
+    (I2, 40, 4100, 12), (I8, 4097, 516, 14), (I4, 33, 12292, 6), (I2, 18, 260, 16),
+    (I4, 17, 8, 2), (I8, 9000, 1028, 4), (I4, 12288, 6144, 8),
+]
+
+
+@pytest.mark.parametrize("fmt,O,I,S", SKINNY_CASES)
+def test_skinny_default_ragged(fmt, O, I, S):
+    assert wq.wq_describe_plan(fmt, O, I, S).startswith("skinny")
+    p = synth.ragged(fmt, O, I, S, seed=4242 + O + I + S)
+    check_problem(p, "skinny")
+
+
 @pytest.mark.parametrize("S", [8, 9, 16])
 def test_gemv_tiled_crossover(S):
     p = synth.ragged(I4, 257, 1111, S, seed=31337 + S)
