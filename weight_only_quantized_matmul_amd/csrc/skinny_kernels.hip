@@ -36,11 +36,10 @@
 //    per step), and the waves' partial tiles are added through LDS at the
 //    end in fixed order (deterministic; no split-K kernel and no second
 //    launch).
-//  * The operand buffer is swizzled so that both its writers (16 lanes: four
-//    stacked rows x four k-groups) and its MFMA readers (16 lanes: sixteen
-//    rows of one k-group) touch 16 distinct 16-byte bank groups, and any 8
-//    consecutive lanes 8 distinct ones (free of bank conflicts with 32 or 64
-//    banks); chunks alternate between two buffers where LDS allows, so the
+//  * The operand buffer is swizzled so that any 8 consecutive lanes touch 8
+//    distinct 16-byte bank groups, both when they write it (two stacked rows
+//    x four k-groups) and when the MFMA reads it (eight rows of one
+//    k-group); chunks alternate between two buffers where LDS allows, so the
 //    split of one chunk need not wait for the MFMA reads of the one before.
 #include <algorithm>
 #include <type_traits>
@@ -159,9 +158,9 @@ template <int FMT> __device__ __forceinline__ int elem_lane_part(int g, int j, i
 // 16-byte slot of stacked row rho, k-step j and k-group g in an operand
 // buffer (1 KiB per fragment of 16 rows and k-step; the MFMA's lane li + 16 g
 // reads row li of k-group g): inside its k-group the row is rotated by
-// S j + 4 g (see the bank-conflict note at the top).
+// S j + 2 g (see the bank-conflict note at the top).
 __device__ __forceinline__ int opnd_slot(int rho, int j, int g, int S) {
-    return ((rho >> 4) * 4 + j) * 64 + 16 * g + (((rho & 15) + S * j + 4 * g) & 15);
+    return ((rho >> 4) * 4 + j) * 64 + 16 * g + (((rho & 15) + S * j + 2 * g) & 15);
 }
 
 // M: stacked operand fragments (3 S <= 16 M); RPL: 8-position activation
@@ -212,19 +211,18 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) rd_slot[j] = opnd_slot(li, j, g, S);
 
-    // run index t = r % 4 + 4 (r / 16) of run r = lane + 64 i, k-group
-    // (r / 4) % 4: sixteen lanes hold four runs of four k-groups; run t is
-    // activation row t % S of k-step t / S (runs t >= 4 S are loaded and
-    // never stored)
+    // run r = lane + 64 i: k-group r % 4 (four lanes read 64 contiguous
+    // bytes of an activation row), run index t = r / 4, which is activation
+    // row t % S of k-step t / S (runs t >= 4 S are loaded and never stored)
     int run_g[RPL], run_j[RPL], run_slot[RPL][3];
     uint32_t run_x[RPL][2];   // activation offset (floats) of the run inside the permuted blocks, less the chunk part
     uint32_t run_xn[RPL][2];  // the same in natural order (past the blocks), less the chunk's first position
     bool run_live[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-        const int t = (lane & 3) + 4 * (lane >> 4) + 16 * i;
+        const int t = (lane >> 2) + 16 * i;
         const int rs = t % S;
-        run_g[i] = (lane >> 2) & 3;
+        run_g[i] = lane & 3;
         run_j[i] = min(t / S, 3);
         run_live[i] = t < 4 * S;
 #pragma unroll
