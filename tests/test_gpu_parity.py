@@ -421,9 +421,10 @@ def test_team_rows_over_several_chunks(fmt, O, I, S):
 
 
 # ---------------------------------------------------------------------------------------
-# S = 1 int4 / int2: codes enter the FMAs as f16 subnormals (code * 2^-24) and
-# the sums are scaled back by 2^24; activations spanning 1e-35 .. 1e35 stay
-# within the bound (tiny products underflow far below its 1e-30 term)
+# S = 1 int4 / int2: codes enter the FMAs as exact f16 halves 2^k * q, and the
+# activations meeting them are pre-divided by 2^k; activations spanning
+# 1e-35 .. 1e35 stay within the bound (tiny products underflow far below its
+# 1e-30 term)
 
 
 @pytest.mark.parametrize("fmt,O,I", [(I4, 300, 6144), (I2, 260, 8192), (I4, 64, 1000)])
