@@ -48,7 +48,7 @@ extern "C" {
 #endif
 
 #define WQ_MAX_DEVICES 16   /* size of the static device table */
-#define WQ_GEMV_MAX_S 8     /* largest S the register GEMV serves (by default 4 for int4 and int2, which are faster on the tiled path above that) */
+#define WQ_GEMV_MAX_S 8     /* largest S the register GEMV serves (by default f32 only; quantized formats take it at S = 1 and the matrix-core paths above) */
 
 enum wq_fmt { WQ_F32 = 0, WQ_I8 = 1, WQ_I4 = 2, WQ_I2 = 3 };
 
@@ -74,8 +74,10 @@ typedef struct wq_group wq_group;   /* opaque set of tensors run in one launch *
  * Rejects duplicates, negative or out-of-range ordinals and ndev >
  * WQ_MAX_DEVICES (WQ_E_INVAL); no GPU or a non-gfx950 GPU gives WQ_E_NODEV.
  * Calling it again is allowed: already-open devices are kept, and the
- * environment knobs are read again (WQ_FORCE_PATH=gemv|tiled|auto,
+ * environment knobs are read again (WQ_FORCE_PATH=gemv|tiled|skinny|auto,
  * WQ_GEMV_MAX_S, WQ_MEM_LIMIT_BYTES, WQ_FAULT=upload|launch,
+ * WQ_SKINNY_RING=4|6 (chunks of loads in flight per wave of the few-rows
+ * kernel, capped at its spill-free depth; default 2), WQ_WAVES_PER_CU,
  * WQ_TILED_MODE=bf16x3|fp32, WQ_TILED_SHAPE=BMxBNxBK (a compiled tile shape:
  * 128x96x64, 128x96x128 or 64x64x64 in bf16x3 mode, 128x96x32 or 64x64x32 in
  * fp32 mode),
@@ -148,8 +150,11 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
  * synchronisation. x_dev: device [S, I] floats, y_dev: device [S, O] floats,
  * both on the tensor's device and 4-byte aligned. The call returns once the
  * work is queued; y_dev is valid after the stream reaches it.
- * S <= the GEMV limit: one kernel launch, no workspace. Larger S with a
- * quantized format (tiled path, bf16x3 mode): two launches that use the
+ * Quantized formats at S = 1, f32 at S <= 8: the register GEMV, one kernel
+ * launch, no workspace. Quantized 2 <= S <= 16 with I % 4 == 0 and x_dev
+ * 16-byte aligned: the few-rows matrix-core kernel, one launch, no
+ * workspace. Larger S (or rows the few-rows kernel cannot read in 16-byte
+ * runs) with a quantized format (tiled path, bf16x3 mode): two launches that use the
  * device's workspace (3 * round_up(S, 128) * round_up(fields per row, 128)
  * bf16 values, 16-row padding for S <= 16; when K is split across blocks,
  * a third launch adds ksplit * S * O fp32 partials kept after them;
@@ -199,7 +204,8 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
  * Run every tensor of a plain group (a gated group gives WQ_E_INVAL):
  * y_dev[g] = matmul(ts[g], x_dev[g], S[g]).
  * x_dev, S, y_dev: host arrays of G entries (device pointers inside);
- * S[g] == 0 skips tensor g. When every S[g] <= the GEMV limit and every row
+ * S[g] == 0 skips tensor g. When every S[g] <= the grouped GEMV limit
+ * (4 for int4 and int2, 8 for int8 and f32) and every row
  * fits one wave of the register GEMV, up to 64 tensors run as ONE launch on
  * hip_stream whatever their shapes (e.g. the gate, up and down projections
  * of 8 experts: 24 tensors with 3 KiB and 1 KiB rows), the work cut into
@@ -233,10 +239,10 @@ int wq_grouped_free(wq_group *group);
  * wq_swiglu_matmul_dev: h_dev[e] = h_e, an fp32 [S[e], O_e] device buffer,
  * for x_dev[e] fp32 [S[e], I_e] (host arrays of E device pointers; S[e] == 0
  * skips expert e). Stream-ordered on hip_stream. With every S[e] within the
- * GEMV limit, one scale per row and rows that fit one wave, all experts run
+ * grouped GEMV limit, one scale per row and rows that fit one wave, all experts run
  * in one launch that reads each gate row and up row once and writes h
  * directly (g and u never reach memory); otherwise each expert runs as its
- * own paired launch, or (S above the GEMV limit, or group-wise scales) as
+ * own paired launch, or (S above that limit, or group-wise scales) as
  * gate -> h_dev[e], up -> the device workspace, then an activation kernel.
  * The last form may grow the workspace (refused with WQ_E_UNSUPPORTED while
  * the stream is being captured; warm up first).
@@ -267,7 +273,8 @@ const char *wq_strerror(int code);
  * Introspection for tests and tools: the kernel path wq_matmul_dev would take
  * for (fmt, O, I, S) on this build, written as a NUL-terminated string into
  * buf (e.g. "gemv fmt=2 smax=1 lw=16 kmax=4 k=3 team=1 d=4 rows_per_team=12 grid=256 block=256",
- * or "tiled fmt=3 mode=bf16x3 bm=16 bn=32 bk=64 tiles_s=1 tiles_o=512 ksplit=4 grid=2048 block=64 workspace=...").
+ * "skinny fmt=2 m=2 rpl=2 nb=3 waves=8 ring=2 chunks=48 chunks_per_wave=6 grid=256 block=512 workspace=0",
+ * or "tiled fmt=1 mode=bf16x3 bm=128 bn=96 bk=64 tiles_s=4 tiles_o=64 ksplit=1 grid=256 block=512 workspace=...").
  * Host-only: needs no device. Returns WQ_OK or WQ_E_INVAL.
  */
 int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen);
