@@ -155,15 +155,22 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
  * 16-byte aligned: the few-rows matrix-core kernel, one launch, no
  * workspace. Larger S (or rows the few-rows kernel cannot read in 16-byte
  * runs) with a quantized format (tiled path, bf16x3 mode): two launches that use the
- * device's workspace (3 * round_up(S, 128) * round_up(fields per row, 128)
+ * stream's workspace (3 * round_up(S, 128) * round_up(fields per row, 128)
  * bf16 values, 16-row padding for S <= 16; when K is split across blocks,
  * a third launch adds ksplit * S * O fp32 partials kept after them;
- * wq_describe_plan prints the size). The workspace grows on
- * demand: growth waits for the device to go idle and allocates; a call being
- * captured into a HIP graph never grows it and returns WQ_E_UNSUPPORTED
- * instead, so run the largest S once before capturing. The workspace is
- * shared by every call on the device: tiled calls on different streams must
- * not overlap in time.
+ * wq_describe_plan prints the size). Each stream has a workspace of its
+ * own, so tiled calls on different streams may overlap; it grows on demand,
+ * which waits for the device to go idle and allocates. Up to 8 streams per
+ * device hold one; the first tiled call on a ninth stream takes over the
+ * least recently used stream's workspace (also waiting for the device). The
+ * key is the stream handle: a destroyed stream's workspace passes to a new
+ * stream that gets the same handle, so let a stream's queued calls finish
+ * before destroying it. A call being captured into a HIP graph never waits
+ * or allocates: it uses its stream's workspace if that is large enough,
+ * else the largest workspace on the device that is (the graph then shares
+ * that stream's buffer: do not replay it while that stream runs tiled
+ * calls), else it returns WQ_E_UNSUPPORTED; so run the largest S once,
+ * eagerly, before capturing.
  */
 int wq_matmul_dev(const wq_tensor *t, const float *x_dev, int S, float *y_dev, void *hip_stream);
 
@@ -211,7 +218,7 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
  * of 8 experts: 24 tensors with 3 KiB and 1 KiB rows), the work cut into
  * pieces of equal weight bytes when the group is created; more tensors take
  * one launch per 64. Otherwise one wq_matmul_dev per tensor, still
- * stream-ordered (the tiled ones share the device workspace, in stream
+ * stream-ordered (the tiled ones share the stream's workspace, in stream
  * order).
  */
 int wq_grouped_matmul_dev(wq_group *group, const float *const *x_dev, const int *S,
@@ -243,9 +250,9 @@ int wq_grouped_free(wq_group *group);
  * in one launch that reads each gate row and up row once and writes h
  * directly (g and u never reach memory); otherwise each expert runs as its
  * own paired launch, or (S above that limit, or group-wise scales) as
- * gate -> h_dev[e], up -> the device workspace, then an activation kernel.
- * The last form may grow the workspace (refused with WQ_E_UNSUPPORTED while
- * the stream is being captured; warm up first).
+ * gate -> h_dev[e], up -> the stream's workspace, then an activation kernel.
+ * The last form may grow the workspace (not while the stream is being
+ * captured: see wq_matmul_dev; warm up first).
  *
  * Accuracy: g and u meet the matmul contract; h is silu and the product
  * evaluated in fp32 on those values (a few ulps, no further cancellation).

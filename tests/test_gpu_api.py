@@ -264,6 +264,80 @@ def test_capture_refuses_workspace_growth():
         wq.wq_tensor_free(t)
 
 
+def _tiled_case(seed):
+    """An int8 tensor on the tiled path and two activation sets of different S (both tiled)."""
+    p = synth.ragged(I8, 1536, 4096, 256, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    x2 = rng.standard_normal((200, p.I)).astype(np.float32)
+    for S in (p.S, x2.shape[0]):
+        assert wq.wq_describe_plan(I8, p.O, p.I, S).startswith("tiled"), S
+    return p, x2
+
+
+def test_tiled_calls_on_concurrent_streams():
+    """Each stream has its own tiled workspace: calls queued on two streams with no ordering
+    between them (different S, so different plane sizes) all equal their eager results."""
+    p, x2h = _tiled_case(31)
+    t = gu.upload(p)
+    try:
+        x1 = torch.from_numpy(p.x).cuda()
+        x2 = torch.from_numpy(x2h).cuda()
+        r1 = torch.empty((p.S, p.O), device="cuda")
+        r2 = torch.empty((x2h.shape[0], p.O), device="cuda")
+        gu.banner("concurrent streams: eager references")
+        wq.wq_matmul_dev(t, x1, r1)
+        wq.wq_matmul_dev(t, x2, r2)
+        torch.cuda.synchronize()
+        rows = np.arange(0, p.O, 29)
+        for r, xh in ((r1, p.x), (r2, x2h)):
+            y_ref, A = oracle.matmul_rows(I8, p.w, p.scales, xh, rows)
+            gu.assert_within_bound(r.cpu().numpy()[:, rows], y_ref, A, "eager")
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        n = 12
+        o1 = [torch.full_like(r1, float("nan")) for _ in range(n)]
+        o2 = [torch.full_like(r2, float("nan")) for _ in range(n)]
+        torch.cuda.synchronize()
+        gu.banner("concurrent streams: %d calls on each of two streams" % n)
+        for i in range(n):
+            wq.wq_matmul_dev(t, x1, o1[i], stream=s1)
+            wq.wq_matmul_dev(t, x2, o2[i], stream=s2)
+        torch.cuda.synchronize()
+        for i in range(n):
+            assert torch.equal(o1[i], r1), "stream 1, call %d" % i
+            assert torch.equal(o2[i], r2), "stream 2, call %d" % i
+    finally:
+        wq.wq_tensor_free(t)
+
+
+def test_more_streams_than_workspaces():
+    """Ten streams in turn, three rounds: from the ninth stream on, a stream takes over the least
+    recently used stream's workspace; every result still equals the eager one."""
+    p, x2h = _tiled_case(33)
+    t = gu.upload(p)
+    try:
+        xs = [torch.from_numpy(p.x).cuda(), torch.from_numpy(x2h).cuda()]
+        refs = [torch.empty((x.shape[0], p.O), device="cuda") for x in xs]
+        gu.banner("ten streams: eager references")
+        for x, r in zip(xs, refs):
+            wq.wq_matmul_dev(t, x, r)
+        torch.cuda.synchronize()
+        streams = [torch.cuda.Stream() for _ in range(10)]
+        assert len({s.cuda_stream for s in streams}) == 10
+        outs = []
+        gu.banner("ten streams: three rounds")
+        for rnd in range(3):
+            for k, s in enumerate(streams):
+                j = (k + rnd) % 2
+                o = torch.full_like(refs[j], float("nan"))
+                wq.wq_matmul_dev(t, xs[j], o, stream=s)
+                outs.append((j, o))
+        torch.cuda.synchronize()
+        for i, (j, o) in enumerate(outs):
+            assert torch.equal(o, refs[j]), "call %d" % i
+    finally:
+        wq.wq_tensor_free(t)
+
+
 @pytest.mark.parametrize("mode,shape", [("bf16x3", "128x96x64"), ("bf16x3", "128x96x128"), ("bf16x3", "64x64x64"),
                                         ("bf16x3", "16x128x64"),
                                         ("fp32", "128x96x32"), ("fp32", "64x64x32")])

@@ -41,8 +41,20 @@ struct DeviceCtx {
     size_t x_cap = 0;  // bytes
     float *d_y = nullptr;
     size_t y_cap = 0;  // bytes
-    uint16_t *d_ws = nullptr;  // tiled bf16x3 activation planes, shared by every call on the device
-    size_t ws_cap = 0;         // bytes
+    // Tiled workspaces (activation planes, split-K partials, the gated
+    // intermediate), one per stream that ran such a call, so calls on
+    // different streams may overlap. At most kStreamWorkspaces per device;
+    // a new stream beyond that takes over the least recently used one.
+    struct StreamWs {
+        hipStream_t st = nullptr;
+        bool live = false;
+        uint16_t *p = nullptr;
+        size_t cap = 0;  // bytes
+        unsigned long long last = 0;
+    };
+    static constexpr int kStreamWorkspaces = 8;
+    StreamWs ws[kStreamWorkspaces];
+    unsigned long long ws_clock = 0;
     size_t lib_bytes = 0;      // device bytes held by tensors, groups and the workspace
     std::recursive_mutex mu;
 };
@@ -191,39 +203,73 @@ int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool sp
     return 2;
 }
 
-// The device workspace, grown to at least `bytes`. Growth waits for all
-// queued work (the old buffer may still be read) and is refused while `st`
-// is being captured into a graph.
+// The workspace of stream `st`, grown to at least `bytes`. Only calls on
+// `st` use it, and they run in stream order, so it is reused without any
+// wait. Growing it, or handing a new stream the slot of the least recently
+// used one (every slot taken), waits for the device to go idle (the old
+// buffer may still be read). A call being captured into a graph never
+// waits or allocates: it takes its stream's workspace if that is large
+// enough, else the largest one that is (the graph then shares that
+// stream's buffer), else it is refused.
 int ensure_workspace(DeviceCtx &d, size_t bytes, hipStream_t st, uint16_t **out) {
     std::lock_guard<std::recursive_mutex> lk(d.mu);
-    if (bytes > d.ws_cap) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return WQ_E_HIP;
+    }
+    DeviceCtx::StreamWs *e = nullptr;
+    for (DeviceCtx::StreamWs &c : d.ws)
+        if (c.live && c.st == st) e = &c;
+    if (cs != hipStreamCaptureStatusNone) {
+        if (e == nullptr || e->cap < bytes) {
+            e = nullptr;
+            for (DeviceCtx::StreamWs &c : d.ws)
+                if (c.live && c.cap >= bytes && (e == nullptr || c.cap > e->cap)) e = &c;
+        }
+        if (e == nullptr) return WQ_E_UNSUPPORTED;
+        *out = e->p;
+        return WQ_OK;
+    }
+    const bool adopt = e == nullptr;
+    if (adopt) {
+        for (DeviceCtx::StreamWs &c : d.ws)
+            if (!c.live && e == nullptr) e = &c;
+        if (e == nullptr) {
+            e = &d.ws[0];
+            for (DeviceCtx::StreamWs &c : d.ws)
+                if (c.last < e->last) e = &c;
+        }
+    }
+    // a taken-over slot may still be read by its previous stream's calls
+    if (bytes > e->cap || (adopt && e->live)) {
+        if (hipDeviceSynchronize() != hipSuccess) {
             (void)hipGetLastError();
             return WQ_E_HIP;
         }
-        if (cs != hipStreamCaptureStatusNone) return WQ_E_UNSUPPORTED;
-        if (d.d_ws) {
-            if (hipDeviceSynchronize() != hipSuccess) {
-                (void)hipGetLastError();
-                return WQ_E_HIP;
-            }
-            dev_free(d, d.d_ws, d.ws_cap);
-            d.d_ws = nullptr;
-            d.ws_cap = 0;
-        }
-        const size_t cap = (size_t)wq::round_up((long)bytes, 2L << 20);
-        int rc = dev_alloc(d, (void **)&d.d_ws, cap);
-        if (rc != WQ_OK) return rc;
-        d.ws_cap = cap;
     }
-    *out = d.d_ws;
+    if (bytes > e->cap) {
+        dev_free(d, e->p, e->cap);
+        e->p = nullptr;
+        e->cap = 0;
+        const size_t cap = (size_t)wq::round_up((long)bytes, 2L << 20);
+        int rc = dev_alloc(d, (void **)&e->p, cap);
+        if (rc != WQ_OK) {
+            e->live = false;
+            return rc;
+        }
+        e->cap = cap;
+    }
+    e->st = st;
+    e->live = true;
+    e->last = ++d.ws_clock;
+    *out = e->p;
     return WQ_OK;
 }
 
 // fixed_ws != nullptr: the workspace is that buffer of fixed_cap bytes (the
 // no-allocation entry point); a call needing more returns WQ_E_UNSUPPORTED
-// before any launch. Otherwise the device workspace, grown on demand.
+// before any launch. Otherwise the stream's workspace, grown on demand.
 int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t st, uint16_t *fixed_ws = nullptr,
                size_t fixed_cap = 0) {
     DeviceCtx &d = g_dev[t->device];
@@ -747,7 +793,7 @@ int create_group(wq_tensor *const *ts, wq_tensor *const *ts2, int G, wq_group **
 // One expert's gated front half: h[S, O] = silu(gate . x) * (up . x).
 // S within the grouped GEMV limit and one scale per row: one paired-row
 // launch (both dot products of an output from one read of x). Otherwise
-// gate -> h and up -> u (in the device workspace, after the tiled planes
+// gate -> h and up -> u (in the stream's workspace, after the tiled planes
 // when the matmuls take the tiled path) as two ordinary matmuls, then the
 // in-place activation kernel.
 int run_swiglu(const wq_tensor *gt, const wq_tensor *ut, const float *x, int S, float *h, hipStream_t st) {
