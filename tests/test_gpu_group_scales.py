@@ -34,14 +34,14 @@ def upload_gs(fmt, O, I, gs, w, sc):
     return wq.wq_tensor_upload_gs(None, gu.DEV, fmt, O, I, gs, w, sc)
 
 
-def check(fmt, O, I, S, gs, seed, rows=None, what="gs"):
+def check(fmt, O, I, S, gs, seed, rows=None, what="gs", x_offset=0):
     p = synth.ragged(fmt, O, I, S, seed=seed)
     sc = gscales(seed + 1, O, I, gs)
     t = upload_gs(fmt, O, I, gs, p.w, sc)
     try:
-        gu.banner("%s fmt=%d O=%d I=%d S=%d gs=%d plan=%s" % (what, fmt, O, I, S, gs,
-                                                             wq.wq_describe_plan(fmt, O, I, S)))
-        y = gu.run_dev(t, p.x)
+        gu.banner("%s fmt=%d O=%d I=%d S=%d gs=%d x_offset=%d plan=%s" % (what, fmt, O, I, S, gs, x_offset,
+                                                                         wq.wq_describe_plan(fmt, O, I, S)))
+        y = gu.run_dev(t, p.x, x_offset=x_offset)
     finally:
         wq.wq_tensor_free(t)
     if rows is None:
@@ -61,9 +61,20 @@ def test_group_scales_parity(fmt, gs, S):
 
 
 @pytest.mark.parametrize("fmt,O,I,S,gs", [(I4, 129, 64, 1, 64), (I2, 70, 4100, 2, 1024), (I8, 33, 5000, 9, 64),
-                                         (I4, 1000, 3000, 4, 4096), (I2, 17, 130, 40, 128)])
+                                         (I4, 1000, 3000, 4, 4096), (I2, 17, 130, 40, 128),
+                                         # S = 1 rows of 2, 3 and 4 load slots per lane, and a team of
+                                         # several waves per row (int8 20000 bytes, int2 9000 elements)
+                                         (I8, 77, 2500, 1, 64), (I4, 91, 7000, 1, 128), (I4, 60, 8192, 1, 256),
+                                         (I8, 50, 20000, 1, 128), (I2, 45, 9000, 1, 64)])
 def test_group_scales_ragged(fmt, O, I, S, gs):
     check(fmt, O, I, S, gs, seed=8500 + O + I + S, what="gs-ragged")
+
+
+@pytest.mark.parametrize("fmt,O,I,gs", [(I4, 70, 6144, 128), (I4, 33, 8192, 64), (I8, 40, 3000, 128),
+                                       (I2, 50, 8192, 256)])
+def test_group_scales_misaligned_activations(fmt, O, I, gs):
+    """S = 1 with x one float past a 16-byte boundary: the GEMV reads it element by element."""
+    check(fmt, O, I, 1, gs, seed=8550 + O + I, what="gs-misaligned", x_offset=1)
 
 
 def test_group_scales_dense_decode_shape():

@@ -730,7 +730,7 @@ GemvShape gemv_shape(int fmt, int smax) {
     return GemvShape{0, 0, 0, 0, 0};
 }
 
-GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool split) {
+GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu) {
     GemvPlan p;
     p.fmt = fmt;
     p.smax = gemv_smax_bucket(S);
@@ -740,22 +740,20 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool
     p.lw = sh.lw;
     p.kmax = sh.kmax;
     const long stride = round_up(row_bytes(fmt, I), kRowAlign);
-    // Slots per lane: up to kmax, a team of waves sharing a longer row; with
-    // split, one slot per lane (fewer activations staged per wave).
-    const long slots = (split && (stride + 64L * sh.lw - 1) / (64L * sh.lw) <= kMaxTeam) ? 1 : sh.kmax;
-    const long per_wave = 64L * sh.lw * slots;
+    // Slots per lane: up to kmax, a team of waves sharing a longer row.
+    // Group-scaled tensors take the same shape (measured against one-slot
+    // teams at 8 waves per CU, µs: int4 12288 x 6144 gs = 128 11.0 vs 12.7,
+    // int8 6144 x 6144 8.8 vs 9.3, int2 16384 x 8192 15.5 both).
+    const long per_wave = 64L * sh.lw * sh.kmax;
     const long team = (stride + per_wave - 1) / per_wave;
     if (team > kMaxTeam) return p;  // row too long for the register GEMV
     p.team = (int)team;
     p.k = (int)((stride + 64L * p.lw * p.team - 1) / (64L * p.lw * p.team));
-    // split (group-scaled tensors) keeps the grouped launch's ring depth and
-    // 8 waves per CU (measured: 11.3 us vs 12.1 for int4 gs=128); the
-    // launch compiles the same depth for them
-    p.d = ring_depth(sh.kmax, split ? sh.d : sh.dg, p.k);
+    p.d = ring_depth(sh.kmax, sh.dg, p.k);
     p.teams_per_block = (p.team == 1) ? 4 : 1;
     p.block = 64 * p.team * p.teams_per_block;
     // teams: enough waves to keep HBM busy, rows per team a multiple of the ring depth
-    const int wpc = waves_per_cu > 0 ? waves_per_cu : split ? 8 : sh.wg;
+    const int wpc = waves_per_cu > 0 ? waves_per_cu : sh.wg;
     const long want_teams = std::max(1L, (long)cus * wpc / p.team);
     long teams = std::min(want_teams, ((long)O + p.d - 1) / p.d);
     long rpt = ((long)O + teams - 1) / teams;
@@ -767,14 +765,13 @@ GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool
     return p;
 }
 
-// D: ring depth of group-scaled tensors (planned as split teams), DG: of
-// the others (the plan's ring depth is the same one, see plan_gemv).
-template <int F, int SM, int LW, int KM, int D, int DG>
+// DG: the ring depth of the single-tensor GEMV (the plan's, see plan_gemv).
+template <int F, int SM, int LW, int KM, int DG>
 hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStream_t st) {
     // exact slot count: 1..KM; 16-byte activation loads when x allows (xv)
 #define WQ_GO(KS, GS_, PAIR_)                                                                                   \
     do {                                                                                                        \
-        constexpr int RD = ring_depth(KM, GS_ ? D : DG, KS);                                                    \
+        constexpr int RD = ring_depth(KM, DG, KS);                                                              \
         if (xv)                                                                                                 \
             hipLaunchKernelGGL((gemv_kernel<F, SM, LW, KS, RD, true, GS_, PAIR_>), dim3(p.grid), dim3(p.block), \
                                0, st, a);                                                                       \
@@ -805,7 +802,7 @@ hipError_t launch_gemv_k(const GemvPlan &p, const GemvArgs &a, bool xv, hipStrea
 hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st) {
     const bool xv = (a.I % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
 #define WQ_LAUNCH_CASE(F, SM, LW, KM, D, DG, WG) \
-    if (p.fmt == F && p.smax == SM) return launch_gemv_k<F, SM, LW, KM, D, DG>(p, a, xv, st);
+    if (p.fmt == F && p.smax == SM) return launch_gemv_k<F, SM, LW, KM, DG>(p, a, xv, st);
     WQ_SHAPES(WQ_LAUNCH_CASE)
 #undef WQ_LAUNCH_CASE
     return hipErrorInvalidValue;

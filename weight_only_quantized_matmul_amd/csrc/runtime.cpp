@@ -174,30 +174,28 @@ int group_gemv_limit(int fmt) {
 // Which path a call takes: 1 (register GEMV), 2 (tiled), 3 (matrix-core
 // kernel for few rows). x_vec: x is 16-byte aligned (the few-rows kernel
 // reads it in 16-byte runs and also needs I % 4 == 0).
-// Group-scaled tensors split each row over a team of one-slot waves (their
-// natural-order rows stage activations less efficiently; measured faster)
-// and never take the few-rows kernel.
-int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool split = false, bool x_vec = true,
+// Group-scaled tensors (gs) never take the few-rows kernel.
+int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool gs = false, bool x_vec = true,
                 wq::SkinnyPlan *sp = nullptr) {
     auto skinny_ok = [&]() {
-        if (split || !x_vec) return false;
+        if (gs || !x_vec) return false;
         const wq::SkinnyPlan p = wq::plan_skinny(fmt, O, I, S, cus, g_cfg.skinny_ring);
         if (sp) *sp = p;
         return p.ok;
     };
     if (g_cfg.force_path == 3 && skinny_ok()) return 3;
     if (g_cfg.force_path != 2 && g_cfg.force_path != 3 && S <= gemv_limit(fmt)) {
-        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu);
         if (gp->ok) return 1;
     }
     if (g_cfg.force_path == 1) {
-        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu);
         if (gp->ok) return 1;
     }
     if (g_cfg.force_path == 0 && skinny_ok()) return 3;
     // x misaligned or I % 4 != 0: the register GEMV keeps its grouped range
     if (g_cfg.force_path == 0 && S <= group_gemv_limit(fmt)) {
-        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu, split);
+        *gp = wq::plan_gemv(fmt, O, I, S, cus, g_cfg.waves_per_cu);
         if (gp->ok) return 1;
     }
     return 2;

@@ -177,10 +177,9 @@ __host__ __device__ constexpr int ring_depth(int kmax, int d, int ks) {
 }
 int gemv_smax_bucket(int S); // 1,2,4,8 or 0 if S > 8
 
-// split: one load slot per lane, the row shared by as many waves as that
-// needs (when at most kMaxTeam); else up to the shape's slots per lane.
+// Up to the shape's slots per lane, a team of waves sharing a longer row.
 // waves_per_cu <= 0: the shape's default.
-GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu, bool split = false);
+GemvPlan plan_gemv(int fmt, int O, int I, int S, int cus, int waves_per_cu);
 hipError_t launch_gemv(const GemvPlan &p, const GemvArgs &a, hipStream_t st);  // a.gs, a.w2 select the variant
 
 // h[j] = silu(h[j]) * u[j], j < n (gated feed-forward after separate gate and up matmuls)
