@@ -151,9 +151,11 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
  * both on the tensor's device and 4-byte aligned. The call returns once the
  * work is queued; y_dev is valid after the stream reaches it.
  * Quantized formats at S = 1, f32 at S <= 8: the register GEMV, one kernel
- * launch, no workspace. Quantized 2 <= S <= 16 with I % 4 == 0 and x_dev
+ * launch, no workspace. Quantized 2 <= S <= 32 with I % 4 == 0 and x_dev
  * 16-byte aligned: the few-rows matrix-core kernel, one launch, no
- * workspace. Larger S (or rows the few-rows kernel cannot read in 16-byte
+ * workspace (above S = 16 with four waves per block, one block per CU; for
+ * S > 20 only where at most one block per CU covers all O rows, else the
+ * tiled path). Larger S (or rows the few-rows kernel cannot read in 16-byte
  * runs) with a quantized format (tiled path, bf16x3 mode): two launches that use the
  * stream's workspace (3 * round_up(S, 128) * round_up(fields per row, 128)
  * bf16 values, 16-row padding for S <= 16; when K is split across blocks,

@@ -137,15 +137,20 @@ def test_headline_plan_shape():
     (wq.WQ_I4, 12288, 6144, 2), (wq.WQ_I4, 12288, 6144, 8), (wq.WQ_I2, 16384, 8192, 4), (wq.WQ_I2, 16384, 8192, 8),
     (wq.WQ_I2, 16384, 8192, 16), (wq.WQ_I8, 6144, 6144, 8), (wq.WQ_I8, 6144, 6144, 16), (wq.WQ_I4, 2048, 6144, 4),
     (wq.WQ_I4, 256, 512, 3), (wq.WQ_I2, 3, 8, 2), (wq.WQ_I8, 100, 4, 11),
+    (wq.WQ_I4, 12288, 6144, 17), (wq.WQ_I4, 12288, 6144, 24), (wq.WQ_I4, 12288, 6144, 32),
+    (wq.WQ_I2, 16384, 8192, 20), (wq.WQ_I8, 6144, 6144, 25), (wq.WQ_I4, 100, 300, 31), (wq.WQ_I2, 5000, 1000, 22),
 ])
 def test_skinny_plan_invariants(fmt, O, I, S):
-    """2 <= S <= 16 on quantized rows read in 16-byte runs: the matrix-core few-rows kernel.
+    """2 <= S <= 32 on quantized rows read in 16-byte runs: the matrix-core few-rows kernel.
     Every output row is owned by a block, every 128-position chunk of a row by a wave,
-    and the stacked activation parts (3 S rows) fit the plan's MFMA fragments."""
+    the stacked activation parts (3 S rows) fit the plan's MFMA fragments and every
+    lane's activation runs cover the 4 S runs of a chunk."""
     kind, p = _plan(fmt, O, I, S)
     assert kind == "skinny", (kind, p)
     p = {k: int(v) for k, v in p.items()}
-    assert p["m"] == (1 if S <= 5 else 2 if S <= 10 else 3) and 3 * S <= 16 * p["m"]
+    m_want = 1 if S <= 5 else 2 if S <= 10 else 3 if S <= 16 else 4 if S <= 20 else 5 if S <= 24 else 6
+    assert p["m"] == m_want and 3 * S <= 16 * p["m"]
+    assert 16 * p["rpl"] >= 4 * S and (S > 16 or p["rpl"] == -(-S // 4))
     assert p["grid"] * 16 * p["nb"] >= O and (p["grid"] - 1) * 16 * p["nb"] < O
     stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
     fields = stride * {wq.WQ_I8: 1, wq.WQ_I4: 2, wq.WQ_I2: 4}[fmt]
@@ -153,7 +158,22 @@ def test_skinny_plan_invariants(fmt, O, I, S):
     assert p["waves"] * p["chunks_per_wave"] >= p["chunks"] and p["chunks_per_wave"] % 2 == 0
     assert p["ring"] in (2, 4, 6)
     assert p["block"] == 64 * p["waves"] <= 1024 and p["workspace"] == 0
-    assert p["waves"] == 8 or p["m"] <= 2  # 16-wave blocks only with at most two fragments (registers)
+    if S <= 16:  # 16-wave blocks only with at most two fragments (registers)
+        assert p["waves"] == 8 or p["m"] <= 2
+    else:  # four waves: their operand buffers fit in LDS; one wave per SIMD holds the tiles
+        assert p["waves"] == 4 and p["ring"] == 2 and 1 <= p["nb"] <= (3 if p["m"] == 6 else 4)
+        # the fewest output blocks that keep one block per CU (m = 4 may take a second round)
+        assert p["grid"] <= 256 or (p["m"] == 4 and p["nb"] == 4)
+        assert p["nb"] == 1 or -(-(-(-O // 16)) // (p["nb"] - 1)) > 256
+
+
+@pytest.mark.parametrize("fmt,O,I,S,kind", [(wq.WQ_I2, 16384, 8192, 24, "skinny"), (wq.WQ_I2, 16384, 8192, 32, "tiled"),
+                                            (wq.WQ_I4, 60000, 2048, 20, "skinny"), (wq.WQ_I4, 60000, 2048, 21, "tiled"),
+                                            (wq.WQ_I8, 6144, 6144, 32, "skinny")])
+def test_wide_few_rows_kernel_or_tiled(fmt, O, I, S, kind):
+    """Above S = 16 the few-rows kernel runs one 4-wave block per CU; where no compiled block
+    size keeps the grid to one round (m >= 5: 3 or 4 output blocks), the tiled kernel takes it."""
+    assert _plan(fmt, O, I, S)[0] == kind
 
 
 def test_skinny_plan_fills_the_chip_for_the_small_s_workloads():
@@ -165,7 +185,7 @@ def test_skinny_plan_fills_the_chip_for_the_small_s_workloads():
                 assert int(p["grid"]) == 256, p
 
 
-@pytest.mark.parametrize("fmt,O,I,S", [(wq.WQ_I8, 6144, 6144, 512), (wq.WQ_I4, 100, 200, 17),
+@pytest.mark.parametrize("fmt,O,I,S", [(wq.WQ_I8, 6144, 6144, 512), (wq.WQ_I4, 100, 200, 33),
                                        (wq.WQ_F32, 64, 300000, 8)])
 def test_tiled_plan(fmt, O, I, S):
     kind, p = _plan(fmt, O, I, S)
@@ -274,12 +294,13 @@ def test_init_without_gpu_reports_nodev():
 
 
 @pytest.mark.parametrize("fmt,S,kind", [(wq.WQ_I4, 1, "gemv"), (wq.WQ_I4, 2, "skinny"), (wq.WQ_I4, 16, "skinny"),
-                                        (wq.WQ_I4, 17, "tiled"), (wq.WQ_I2, 1, "gemv"), (wq.WQ_I2, 4, "skinny"),
-                                        (wq.WQ_I8, 1, "gemv"), (wq.WQ_I8, 8, "skinny"), (wq.WQ_F32, 8, "gemv"),
-                                        (wq.WQ_F32, 9, "tiled")])
+                                        (wq.WQ_I4, 17, "skinny"), (wq.WQ_I4, 32, "skinny"), (wq.WQ_I4, 33, "tiled"),
+                                        (wq.WQ_I2, 1, "gemv"), (wq.WQ_I2, 4, "skinny"), (wq.WQ_I2, 32, "skinny"),
+                                        (wq.WQ_I8, 1, "gemv"), (wq.WQ_I8, 8, "skinny"), (wq.WQ_I8, 33, "tiled"),
+                                        (wq.WQ_F32, 8, "gemv"), (wq.WQ_F32, 9, "tiled")])
 def test_default_path_per_format_and_s(fmt, S, kind):
     """Quantized formats: the register GEMV for one activation row, the matrix-core
-    few-rows kernel for 2..16, the tiled kernel above; f32 weights keep the GEMV up to
+    few-rows kernel for 2..32, the tiled kernel above; f32 weights keep the GEMV up to
     S = 8."""
     assert _plan(fmt, 4096, 2048, S)[0] == kind
 

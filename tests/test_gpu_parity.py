@@ -250,13 +250,17 @@ def test_forced_paths_agree(path, fmt, O, I, S):
         gu.reinit_with_env(WQ_FORCE_PATH=None)
 
 
-# the few-rows matrix-core kernel by default (quantized, 2 <= S <= 16, I % 4 == 0):
+# the few-rows matrix-core kernel by default (quantized, 2 <= S <= 32, I % 4 == 0):
 # every (fragments, runs per lane) shape, ragged O and row tails past the permuted
-# blocks, few-row plans (one 16-row block, 16 waves), and the int4 S = 8 workload size
+# blocks, few-row plans (one 16-row block, 16 waves), the 4-wave blocks above S = 16
+# with 1, 2 and 3 output blocks each, and the int4 S = 8 and S = 32 workload sizes
 SKINNY_CASES = [
     (I4, 1000, 4100, 3), (I2, 777, 8196, 5), (I8, 515, 2052, 7), (I4, 2049, 1028, 9),
     (I2, 40, 4100, 12), (I8, 4097, 516, 14), (I4, 33, 12292, 6), (I2, 18, 260, 16),
     (I4, 17, 8, 2), (I8, 9000, 1028, 4), (I4, 12288, 6144, 8),
+    (I4, 1000, 4100, 17), (I2, 777, 8196, 21), (I8, 515, 2052, 24), (I4, 9000, 1028, 26),
+    (I2, 40, 4100, 29), (I8, 12280, 516, 32), (I4, 33, 260, 20), (I2, 13000, 2052, 18),
+    (I8, 8200, 1000, 23), (I4, 12288, 6144, 32),
 ]
 
 

@@ -276,8 +276,9 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs =
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// Few activation rows (S <= 16) on the matrix cores: one launch, no
-// workspace (skinny_kernels.hip). Needs x 16-byte aligned and I % 4 == 0.
+// Few activation rows (S <= 32) on the matrix cores: one launch, no
+// workspace (skinny_kernel.h, skinny_kernels.hip, skinny_wide_*.hip). Needs x
+// 16-byte aligned and I % 4 == 0.
 
 struct SkinnyArgs {
     const uint8_t *w;
@@ -291,10 +292,12 @@ struct SkinnyArgs {
     int nchunks;          // chunks per row (even): chunks past it hold no field positions
 };
 
+constexpr int kSkinnyMaxS = 32;  // activation rows the few-rows kernel takes at most
+
 struct SkinnyPlan {
     bool ok = false;
-    int m = 0;       // stacked operand fragments: 1 (S <= 5), 2 (S <= 10), 3 (S <= 16)
-    int rpl = 0;     // activation runs per lane per chunk: ceil(S / 4)
+    int m = 0;       // stacked operand fragments: 1 (S <= 5), 2 (S <= 10), 3 (S <= 16), 4..6 (S <= 32)
+    int rpl = 0;     // activation runs per lane per chunk: ceil(S / 4) (5, 6 or 8 above S = 16)
     int nb = 0;      // 16-row output blocks per block
     int waves = 0;   // waves per block, each streaming its own chunks of the rows
     int ring = 0;    // chunks of loads in flight per wave
