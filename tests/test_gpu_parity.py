@@ -260,7 +260,7 @@ SKINNY_CASES = [
     (I4, 17, 8, 2), (I8, 9000, 1028, 4), (I4, 12288, 6144, 8),
     (I4, 1000, 4100, 17), (I2, 777, 8196, 21), (I8, 515, 2052, 24), (I4, 9000, 1028, 26),
     (I2, 40, 4100, 29), (I8, 12280, 516, 32), (I4, 33, 260, 20), (I2, 13000, 2052, 18),
-    (I8, 8200, 1000, 23), (I4, 12288, 6144, 32),
+    (I8, 8200, 1000, 23), (I4, 12288, 6144, 32), (I8, 1, 4, 32), (I2, 5, 8, 17), (I4, 16, 4, 25),
 ]
 
 
