@@ -874,28 +874,11 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
 
 } // namespace
 
-TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) {
-    TiledPlan p;
-    // the bf16 split needs exact integer codes (quantized formats); f32 weights
-    // stay fp32; group-scaled tensors always take the bf16x3 kernel
-    p.mode = (fmt != WQ_F32 && (mode == kTiledBF16X3 || gs > 0)) ? kTiledBF16X3 : kTiledF32;
-    // plane sizes are kept in int: rows near the int limit take the fp32 mode
-    if ((long)S > INT_MAX - kTiledSAlign || (long)I > INT_MAX / 2 - 4 * kTiledKAlign) p.mode = kTiledF32;
-    // big tiles (128 x 96, 4 x 3 fragments per wave) when there are enough of them
-    const long big = (long)((S + 127) / 128) * ((O + 95) / 96);
-    const bool use_big = S >= 128 && big >= 128;
-    Shape sh;
-    if (p.mode == kTiledBF16X3) {
-        // S <= 16: 16 x 128 tiles of eight waves side by side along o,
-        // sharing the activation fragments (tiled_x3o_kernel)
-        sh = use_big ? kX3Shapes[0] : S <= 16 ? kX3Shapes[3] : kX3Shapes[2];
-        for (const Shape &c : kX3Shapes)
-            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign)) sh = c;
-    } else {
-        sh = use_big ? kF32Shapes[0] : kF32Shapes[1];
-        for (const Shape &c : kF32Shapes)
-            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk) sh = c;
-    }
+namespace {
+
+// The rest of a plan for one tile shape: tile counts, block size, the
+// bf16x3 planes and split K.
+TiledPlan plan_shape(TiledPlan p, const Shape &sh, int fmt, int O, int I, int S, int gs) {
     p.bm = sh.bm;
     p.bn = sh.bn;
     p.bk = sh.bk;
@@ -931,6 +914,49 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         }
     }
     return p;
+}
+
+// Share of the last round of resident waves that a plan fills (1: its
+// waves make whole rounds of kTiledSplitWaves).
+double round_fill(const TiledPlan &p) {
+    const long waves = (long)p.grid * (p.block / 64);
+    const long rounds = (waves + kTiledSplitWaves - 1) / kTiledSplitWaves;
+    return (double)waves / (double)(rounds * kTiledSplitWaves);
+}
+
+} // namespace
+
+TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) {
+    TiledPlan p;
+    // the bf16 split needs exact integer codes (quantized formats); f32 weights
+    // stay fp32; group-scaled tensors always take the bf16x3 kernel
+    p.mode = (fmt != WQ_F32 && (mode == kTiledBF16X3 || gs > 0)) ? kTiledBF16X3 : kTiledF32;
+    // plane sizes are kept in int: rows near the int limit take the fp32 mode
+    if ((long)S > INT_MAX - kTiledSAlign || (long)I > INT_MAX / 2 - 4 * kTiledKAlign) p.mode = kTiledF32;
+    if (p.mode == kTiledBF16X3) {
+        for (const Shape &c : kX3Shapes)
+            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign))
+                return plan_shape(p, c, fmt, O, I, S, gs);
+        // S <= 16: 16 x 128 tiles of eight waves side by side along o,
+        // sharing the activation fragments (tiled_x3o_kernel); 17..64: 64 x 64
+        // tiles (at S = 40 and 64 4-10 % faster than 128 x 96). Above, the
+        // 128 x 96 tiles of eight waves (one block per CU) unless their grid,
+        // split K included, fills its last round of blocks worse than the
+        // 64 x 64 tiles' (us: int4 12288 x 6144 at S = 96 65.8 on 128 x 96
+        // vs 80.2, int8 6144 x 6144 at S = 128 44.8 vs 62.9; int2 16384 x 8192
+        // at S = 96 139.6 on 342 big blocks vs 115.7 on 512 small ones).
+        if (S <= 16) return plan_shape(p, kX3Shapes[3], fmt, O, I, S, gs);
+        const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
+        if (S <= 64) return small;
+        const TiledPlan large = plan_shape(p, kX3Shapes[0], fmt, O, I, S, gs);
+        return round_fill(large) >= round_fill(small) ? large : small;
+    }
+    // fp32: big tiles (128 x 96, 4 x 3 fragments per wave) when there are enough of them
+    const long big = (long)((S + 127) / 128) * ((O + 95) / 96);
+    Shape sh = (S >= 128 && big >= 128) ? kF32Shapes[0] : kF32Shapes[1];
+    for (const Shape &c : kF32Shapes)
+        if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk) sh = c;
+    return plan_shape(p, sh, fmt, O, I, S, gs);
 }
 
 hipError_t launch_tiled(int fmt, const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
