@@ -298,11 +298,10 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen);
  * flight.
  * out_dev (device, 4-byte aligned) receives 64 * waves words (an
  * exclusive-or of the words read, so the loads cannot be dropped).
- * Stream-ordered on hip_stream, no host synchronisation. The survey's
- * measurement protocol asks for such a kernel beside the GEMV timings
- * (colibri docs "CUDA backend (Linux)" print no kernel-level rates, so
- * the ceiling is measured, not quoted). Errors: WQ_E_INVAL for a bad
- * argument, WQ_E_HIP.
+ * Stream-ordered on hip_stream, no host synchronisation. It gives the GEMV
+ * timings a measured ceiling to be read against (colibri docs "CUDA backend
+ * (Linux)" print no kernel-level rates, so the ceiling is measured, not
+ * quoted). Errors: WQ_E_INVAL for a bad argument, WQ_E_HIP.
  */
 int wq_stream_read_dev(const void *buf_dev, size_t bytes, int waves, int loads_in_flight, unsigned *out_dev,
                        void *hip_stream);
