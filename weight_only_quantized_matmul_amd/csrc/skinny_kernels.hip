@@ -106,8 +106,9 @@ SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring) {
         // one block per CU (a second round of blocks costs more than bigger
         // blocks: int2 16384 x 8192 at S = 20, 37.6 us with 4 output blocks,
         // 57.0 with 2, 62.8 with 3); where no compiled size does, m >= 5
-        // leaves it to the tiled kernel (as fast or faster there: S = 24
-        // 65.0 vs 66.6 us, S = 32 81.2 vs 68.1 us).
+        // leaves it to the tiled kernel (within 3 % at S = 24: 66.6 vs
+        // 65.0 us on two rounds of 4-wave blocks; faster at S = 32: 68.1 vs
+        // 81.2 us).
         p.m = S <= 20 ? 4 : S <= 24 ? 5 : 6;
         p.rpl = S <= 20 ? 5 : S <= 24 ? 6 : 8;
         const int nbmax = p.m == 6 ? 3 : 4;
