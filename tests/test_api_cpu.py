@@ -211,7 +211,7 @@ def test_tiled_plan(fmt, O, I, S):
 
 
 @pytest.mark.parametrize("fmt,O,I,S,ks", [(wq.WQ_I4, 12288, 6144, 8, 6), (wq.WQ_I2, 16384, 8192, 12, 4),
-                                          (wq.WQ_I4, 12288, 6144, 32, 3),
+                                          (wq.WQ_I4, 12288, 6144, 32, 8), (wq.WQ_I2, 16384, 8192, 40, 2),
                                           (wq.WQ_I8, 6144, 6144, 512, 1), (wq.WQ_I4, 100, 200, 9, 1)])
 def test_tiled_split_k_plan(fmt, O, I, S, ks):
     """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves
@@ -222,6 +222,8 @@ def test_tiled_split_k_plan(fmt, O, I, S, ks):
     assert kind == "tiled" and int(p["ksplit"]) == ks, p
     if S <= 16 and fmt != wq.WQ_F32:  # 16 x 128 tiles of eight waves side by side along o
         assert (p["bm"], p["bn"], p["block"]) == ("16", "128", "512"), p
+    elif S <= 64:  # 64 x 192 tiles unless their blocks overflow a round of resident waves (int2 16384 rows)
+        assert (p["bm"], p["bn"], p["block"]) == (("64", "64", "256") if O == 16384 else ("64", "192", "256")), p
 
 
 def test_prefill_plan_uses_large_tiles():

@@ -339,7 +339,7 @@ def test_more_streams_than_workspaces():
 
 
 @pytest.mark.parametrize("mode,shape", [("bf16x3", "128x96x64"), ("bf16x3", "128x96x128"), ("bf16x3", "64x64x64"),
-                                        ("bf16x3", "16x128x64"),
+                                        ("bf16x3", "16x128x64"), ("bf16x3", "64x192x64"),
                                         ("fp32", "128x96x32"), ("fp32", "64x64x32")])
 @pytest.mark.parametrize("fmt,O,I,S", [(I8, 200, 700, 150), (I4, 97, 2100, 20), (I2, 130, 4500, 70)])
 def test_forced_tile_shapes(mode, shape, fmt, O, I, S):

@@ -848,7 +848,7 @@ hipError_t launch_x3o(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
 struct Shape {
     int bm, bn, bk;
 };
-constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 128}, {64, 64, 64}, {16, 128, 64}};
+constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 128}, {64, 64, 64}, {16, 128, 64}, {64, 192, 64}};
 constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
 
 template <int FMT>
@@ -857,6 +857,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
         if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: 64-position K steps
             if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true>(p, a, st);
             if (p.bm == 16) return launch_x3o<FMT, 8, 1, true>(p, a, st);
+            if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, true>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true>(p, a, st);
         }
         if (p.mode == kTiledBF16X3) {
@@ -865,6 +866,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
                 return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch>(p, a, st);
             }
             if (p.bm == 16) return launch_x3o<FMT, 8, 1>(p, a, st);
+            if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch>(p, a, st);
         }
     }
@@ -885,7 +887,7 @@ TiledPlan plan_shape(TiledPlan p, const Shape &sh, int fmt, int O, int I, int S,
     p.tiles_s = (S + p.bm - 1) / p.bm;
     p.tiles_o = (O + p.bn - 1) / p.bn;
     p.grid = p.tiles_s * p.tiles_o;
-    p.block = (p.mode == kTiledBF16X3 && (p.bm == 128 || p.bm == 16)) ? 512 : 256;
+    p.block = (p.mode == kTiledBF16X3 && (p.bm == 128 || p.bm == 16)) ? 512 : 256;  // 64-row tiles: four waves
     if (p.mode == kTiledBF16X3) {
         const long stride = round_up(row_bytes(fmt, I), kRowAlign);
         const long npos = stride * elems_per_byte(fmt);
@@ -938,17 +940,20 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
             if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign))
                 return plan_shape(p, c, fmt, O, I, S, gs);
         // S <= 16: 16 x 128 tiles of eight waves side by side along o,
-        // sharing the activation fragments (tiled_x3o_kernel); 17..64: 64 x 64
-        // tiles (at S = 40 and 64 4-10 % faster than 128 x 96). Above, the
-        // 128 x 96 tiles of eight waves (one block per CU) unless their grid,
-        // split K included, fills its last round of blocks worse than the
-        // 64 x 64 tiles' (us: int4 12288 x 6144 at S = 96 65.8 on 128 x 96
-        // vs 80.2, int8 6144 x 6144 at S = 128 44.8 vs 62.9; int2 16384 x 8192
-        // at S = 96 139.6 on 342 big blocks vs 115.7 on 512 small ones).
+        // sharing the activation fragments (tiled_x3o_kernel). 17..64: 64 x
+        // 192 tiles of four waves (each 16 x 192: a third of the activation
+        // reads of 64 x 64 tiles) unless their grid, split K included, fills
+        // its last round of resident waves worse than the 64 x 64 tiles' (us:
+        // int4 12288 x 6144 at S = 33 / 64 47.2 / 53.3 vs 55.1 / 59.4, int8
+        // 6144 x 6144 35.7 / 38.3 vs 39.1 / 41.1; int2 16384 x 8192 at S = 40
+        // 82.2 on 516 blocks vs 69.8 on 512). Above, the 128 x 96 tiles of
+        // eight waves (one block per CU; 64 x 192 measured 5-10 % slower
+        // there) on the same test against the 64 x 64 tiles (int4 at S = 96
+        // 65.8 vs 80.2, int8 at S = 128 44.8 vs 62.9; int2 at S = 96 139.6 on
+        // 342 big blocks vs 115.7 on 512 small ones).
         if (S <= 16) return plan_shape(p, kX3Shapes[3], fmt, O, I, S, gs);
         const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
-        if (S <= 64) return small;
-        const TiledPlan large = plan_shape(p, kX3Shapes[0], fmt, O, I, S, gs);
+        const TiledPlan large = plan_shape(p, S <= 64 ? kX3Shapes[4] : kX3Shapes[0], fmt, O, I, S, gs);
         return round_fill(large) >= round_fill(small) ? large : small;
     }
     // fp32: big tiles (128 x 96, 4 x 3 fragments per wave) when there are enough of them
