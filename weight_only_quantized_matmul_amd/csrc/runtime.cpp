@@ -712,12 +712,9 @@ int create_group(wq_tensor *const *ts, wq_tensor *const *ts2, int G, wq_group **
         bk.plan.kmax = sh.kmax;
         bk.plan.d = sh.d;
         const long per_wave = 64L * sh.lw * sh.kmax;
-        long total = 0;
         bool fits = true;
-        for (const auto &gd : g->h_desc) {
+        for (const auto &gd : g->h_desc)
             if (gd.stride > per_wave) fits = false;
-            total += (long)vrows * gd.O * gd.stride;
-        }
         if (!fits) continue;
         // One launch per chunk of <= kGroupMaxPerLaunch problems, whatever
         // their row lengths: the chunk's weight bytes are cut into about
