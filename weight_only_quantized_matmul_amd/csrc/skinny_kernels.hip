@@ -82,18 +82,28 @@ SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring) {
     if (S <= 16) {
         p.m = S <= 5 ? 1 : S <= 10 ? 2 : 3;
         p.rpl = (S + 3) / 4;
-        // output blocks: as many rows per block (of the compiled ones) as
-        // still gives every CU a block
-        p.nb = 0;
-        for (int nb = 4; nb >= 1; --nb)
-            if (skinny_max_ring(fmt, p.m, p.rpl, nb) > 0 && (O + 16 * nb - 1) / (16 * nb) >= cus) {
-                p.nb = nb;
-                break;
-            }
+        // Output blocks per block (of the compiled ones): the fewest rounds
+        // of one block per CU, weighed against bigger blocks (each block also
+        // loads and splits all of x, about one output block's worth): cost =
+        // rounds * (1 + nb). A second round costs more than idle CUs: int8
+        // 6144 x 6144 at S = 8, 16.3 us on 192 blocks of 32 rows against 20.5
+        // on 384 of 16; int4 6144 x 6144 13.2 against 18.3.
+        const long row_blocks = ((long)O + 15) / 16;
+        p.nb = 1;
         p.waves = 8;
-        if (p.nb == 0) {  // few output rows: more waves per block share each row's chunks
-            p.nb = 1;
+        if (row_blocks < cus) {  // few output rows: more waves per block share each row's chunks
             if (skinny_wide_ok(fmt, p.m, p.rpl)) p.waves = 16;
+        } else {
+            long best = -1;
+            for (int nb = 1; nb <= 4; ++nb) {
+                if (skinny_max_ring(fmt, p.m, p.rpl, nb) == 0) continue;
+                const long blocks = (row_blocks + nb - 1) / nb;
+                const long cost = (blocks + cus - 1) / cus * (1 + nb);
+                if (best < 0 || cost < best) {
+                    best = cost;
+                    p.nb = nb;
+                }
+            }
         }
         // two chunks of loads in flight (the fastest measured), or a deeper
         // spill-free ring when asked for
