@@ -943,18 +943,21 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         // sharing the activation fragments (tiled_x3o_kernel). 17..64: 64 x
         // 192 tiles of four waves (each 16 x 192: a third of the activation
         // reads of 64 x 64 tiles) unless their grid, split K included, fills
-        // its last round of resident waves worse than the 64 x 64 tiles' (us:
+        // its last round of resident waves clearly worse (by more than 0.2)
+        // than the 64 x 64 tiles' (us:
         // int4 12288 x 6144 at S = 33 / 64 47.2 / 53.3 vs 55.1 / 59.4, int8
         // 6144 x 6144 35.7 / 38.3 vs 39.1 / 41.1; int2 16384 x 8192 at S = 40
         // 82.2 on 516 blocks vs 69.8 on 512). Above, the 128 x 96 tiles of
         // eight waves (one block per CU; 64 x 192 measured 5-10 % slower
         // there) on the same test against the 64 x 64 tiles (int4 at S = 96
         // 65.8 vs 80.2, int8 at S = 128 44.8 vs 62.9; int2 at S = 96 139.6 on
-        // 342 big blocks vs 115.7 on 512 small ones).
+        // 342 big blocks vs 115.7 on 512 small ones; int4 14336 x 4096 at
+        // S = 512 207.5 on 600 big blocks, fill 0.78, vs 255 on 1792 small
+        // ones, fill 0.88).
         if (S <= 16) return plan_shape(p, kX3Shapes[3], fmt, O, I, S, gs);
         const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
         const TiledPlan large = plan_shape(p, S <= 64 ? kX3Shapes[4] : kX3Shapes[0], fmt, O, I, S, gs);
-        return round_fill(large) >= round_fill(small) ? large : small;
+        return round_fill(large) + 0.2 >= round_fill(small) ? large : small;
     }
     // fp32: big tiles (128 x 96, 4 x 3 fragments per wave) when there are enough of them
     const long big = (long)((S + 127) / 128) * ((O + 95) / 96);
