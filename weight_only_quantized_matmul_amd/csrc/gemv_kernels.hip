@@ -680,7 +680,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedArgs a) {
 // waves per CU (their expert rows are few per wave).
 #define WQ_SHAPES(X)                                                   \
     X(WQ_F32, 1, 16, 4, 2, 2, 8) X(WQ_F32, 2, 16, 4, 2, 2, 8)          \
-    X(WQ_F32, 4, 16, 4, 2, 2, 8) X(WQ_F32, 8, 16, 2, 2, 2, 8)          \
+    X(WQ_F32, 4, 16, 4, 2, 2, 8) X(WQ_F32, 8, 16, 4, 2, 2, 8)          \
     X(WQ_I8, 1, 16, 4, 2, 2, 8) X(WQ_I8, 2, 16, 2, 2, 2, 8)            \
     X(WQ_I8, 4, 16, 1, 4, 4, 8) X(WQ_I8, 8, 8, 1, 4, 4, 8)             \
     X(WQ_I4, 1, 16, 4, 2, 4, 4) X(WQ_I4, 2, 16, 1, 2, 2, 8)            \
