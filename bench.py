@@ -71,10 +71,14 @@ def parse():
 COUNTER_SUMMARY = {"dense_gemv": "profiles/gemv_int4_dense_gemv_hbm_counters.txt"}
 
 
+# sources the counted kernel is compiled from (the register GEMV)
+COUNTED_SOURCES = ("gemv_kernels.hip", "wq_internal.h")
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemv_kernels.hip", "tiled_kernels.hip", "wq_internal.h"):
+    for f in COUNTED_SOURCES:
         with open(os.path.join(ROOT, "weight_only_quantized_matmul_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -89,7 +93,7 @@ def traffic_from_counters(workload):
     sha, traffic = None, None
     with open(os.path.join(ROOT, path)) as f:
         for line in f:
-            if line.startswith("kernel source sha256[:16]:"):
+            if line.startswith("kernel source sha256[:16]"):
                 sha = line.rsplit(":", 1)[1].strip()
             elif line.startswith("traffic_bytes_per_launch:"):
                 traffic = int(line.split(":", 1)[1])

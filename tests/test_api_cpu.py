@@ -195,8 +195,8 @@ def test_tiled_plan(fmt, O, I, S):
     assert int(p["grid"]) == int(p["tiles_s"]) * int(p["tiles_o"]) * ks
     # plane rows hold every tile row the kernel reads: bm divides the 128-row padding
     assert 128 % int(p["bm"]) == 0 and 128 % int(p["bk"]) == 0
-    if fmt == wq.WQ_F32:
-        assert p["mode"] == "fp32" and p["workspace"] == "0" and ks == 1
+    if fmt == wq.WQ_F32:  # no planes; split K keeps fp32 partials per chunk
+        assert p["mode"] == "fp32" and int(p["workspace"]) == (0 if ks == 1 else ks * S * O * 4)
     else:
         # three bf16 planes of round_up(S, 128) rows (16 for the 16-row tile) by round_up(fields per row, 128)
         stride = -(-wq.wq_row_bytes(fmt, I) // 16) * 16
@@ -212,7 +212,10 @@ def test_tiled_plan(fmt, O, I, S):
 
 @pytest.mark.parametrize("fmt,O,I,S,ks", [(wq.WQ_I4, 12288, 6144, 8, 6), (wq.WQ_I2, 16384, 8192, 12, 4),
                                           (wq.WQ_I4, 12288, 6144, 32, 8), (wq.WQ_I2, 16384, 8192, 40, 2),
-                                          (wq.WQ_I8, 6144, 6144, 512, 1), (wq.WQ_I4, 100, 200, 9, 1)])
+                                          (wq.WQ_I8, 6144, 6144, 512, 1), (wq.WQ_I4, 100, 200, 9, 1),
+                                          (wq.WQ_F32, 12288, 6144, 9, 3), (wq.WQ_F32, 64, 300000, 8, 512),
+                                          (wq.WQ_F32, 4096, 4096, 200, 2), (wq.WQ_F32, 4096, 4096, 512, 3),
+                                          (wq.WQ_F32, 16384, 4096, 512, 1)])
 def test_tiled_split_k_plan(fmt, O, I, S, ks):
     """Few tiles split K into chunks of >= 4 steps until the grid holds 2048 waves
     (S <= 16 takes the tiled path only when forced, or for rows it cannot read in
@@ -220,7 +223,10 @@ def test_tiled_split_k_plan(fmt, O, I, S, ks):
     with forced(WQ_FORCE_PATH="tiled"):
         kind, p = _plan(fmt, O, I, S)
     assert kind == "tiled" and int(p["ksplit"]) == ks, p
-    if S <= 16 and fmt != wq.WQ_F32:  # 16 x 128 tiles of eight waves side by side along o
+    if fmt == wq.WQ_F32:  # fp32 mode: 128 x 96 tiles from 128 rows when there are >= 128 of them
+        big = S >= 128 and -(-S // 128) * -(-O // 96) >= 128
+        assert (p["bm"], p["bn"], p["block"]) == (("128", "96", "256") if big else ("64", "64", "256")), p
+    elif S <= 16:  # 16 x 128 tiles of eight waves side by side along o
         assert (p["bm"], p["bn"], p["block"]) == ("16", "128", "512"), p
     elif S <= 64:  # 64 x 192 tiles unless their blocks overflow a round of resident waves (int2 16384 rows)
         assert (p["bm"], p["bn"], p["block"]) == (("64", "64", "256") if O == 16384 else ("64", "192", "256")), p

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void tiled_f32_kernel(TiledArgs a) {
     extern __shared__ __attribute__((aligned(16))) float ldsf[];
 
     int s0, o0;
-    tile_origin(a, BM, BN, s0, o0);
+    const int kc = tile_origin(a, BM, BN, s0, o0);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -182,6 +182,8 @@ __global__ __launch_bounds__(256) void tiled_f32_kernel(TiledArgs a) {
     // elements inside 1 KiB blocks; positions past I may hold real elements)
     const long npos = (FMT == WQ_F32) ? (long)a.I : (long)(a.stride) * (FMT == WQ_I8 ? 1 : FMT == WQ_I4 ? 2 : 4);
     const int nk = (int)((npos + BK32 - 1) / BK32);
+    // this block's K steps [kb, ke) (all of them without split K)
+    const int kb = (int)((long)kc * nk / a.ksplit), ke = (int)((long)(kc + 1) * nk / a.ksplit);
 
     // staging: unit u covers tile row u / 4, positions 8 * (u % 4) .. +8 of the K step
     float xv[C::XU][8], wv[C::WU][8];
@@ -230,12 +232,12 @@ __global__ __launch_bounds__(256) void tiled_f32_kernel(TiledArgs a) {
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    fetch(0);
+    fetch((long)kb * BK32);
     stash(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) fetch((long)(kt + 1) * BK32);
+    for (int kt = kb; kt < ke; ++kt) {
+        const int buf = (kt - kb) & 1;
+        if (kt + 1 < ke) fetch((long)(kt + 1) * BK32);
         const float *As = ldsf + buf * C::STAGE_FLOATS;
         const float *Bs = As + C::A_FLOATS;
 #pragma unroll
@@ -255,10 +257,27 @@ __global__ __launch_bounds__(256) void tiled_f32_kernel(TiledArgs a) {
                     for (int n = 0; n < WN; ++n)
                         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m][j], bv[n][j], acc[m][n], 0, 0, 0);
         }
-        if (kt + 1 < nk) stash(buf ^ 1);
+        if (kt + 1 < ke) stash(buf ^ 1);
         __syncthreads();
     }
-    store_tile<WM, WN>(a, acc, s0, o0, wm, wn, g, li);
+    if (a.ksplit == 1) {
+        store_tile<WM, WN>(a, acc, s0, o0, wm, wn, g, li);
+        return;
+    }
+    // split K: this chunk's unscaled sums; splitk_sum_kernel adds the chunks
+    const long pstride = (long)a.S * a.O;
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+        const int o = o0 + wn * 16 * WN + n * 16 + li;
+        if (o >= a.O) continue;
+#pragma unroll
+        for (int m = 0; m < WM; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = s0 + wm * 16 * WM + m * 16 + 4 * g + r;
+                if (s < a.S) a.part[kc * pstride + (long)s * a.O + o] = acc[m][n][r];
+            }
+    }
 }
 
 // ===========================================================================
@@ -795,6 +814,11 @@ hipError_t launch_f32(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     static const hipError_t lim = raise_lds_limit(&tiled_f32_kernel<FMT, WM, WN>, C::LDS_BYTES);
     if (lim != hipSuccess) return lim;
     hipLaunchKernelGGL((tiled_f32_kernel<FMT, WM, WN>), dim3(p.grid), dim3(256), C::LDS_BYTES, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.ksplit == 1) return e;
+    const long n = (long)a.S * a.O;
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)std::min<long>((n + 255) / 256, 4096)), dim3(256), 0, st,
+                       a.part, a.ksplit, n, a.O, a.scales, a.y);
     return hipGetLastError();
 }
 
@@ -888,6 +912,23 @@ TiledPlan plan_shape(TiledPlan p, const Shape &sh, int fmt, int O, int I, int S,
     p.tiles_o = (O + p.bn - 1) / p.bn;
     p.grid = p.tiles_s * p.tiles_o;
     p.block = (p.mode == kTiledBF16X3 && (p.bm == 128 || p.bm == 16)) ? 512 : 256;  // 64-row tiles: four waves
+    if (p.mode == kTiledF32) {
+        // fp32 mode: no planes; split K as below when the tiles leave the
+        // chip short of waves (f32 12288 x 6144 at S = 9: 192 tiles)
+        const long npos = fmt == WQ_F32 ? (long)I : round_up(row_bytes(fmt, I), kRowAlign) * elems_per_byte(fmt);
+        const int nk = (int)((npos + BK32 - 1) / BK32);
+        const int waves = p.grid * (p.block / 64);
+        if (gs == 0 && waves < kTiledSplitWaves && nk >= 2 * kTiledMinChunk) {
+            int ks = (kTiledSplitWaves + waves - 1) / waves;
+            ks = std::min(ks, nk / kTiledMinChunk);
+            if (ks > 1 && (long)ks * S * O <= (long)INT_MAX) {
+                p.ksplit = ks;
+                p.grid *= ks;
+                p.part_off = 0;
+                p.ws_bytes = (size_t)ks * S * O * sizeof(float);
+            }
+        }
+    }
     if (p.mode == kTiledBF16X3) {
         const long stride = round_up(row_bytes(fmt, I), kRowAlign);
         const long npos = stride * elems_per_byte(fmt);
