@@ -34,8 +34,10 @@
 //    activations meeting a field scaled by 2^k are pre-divided by 2^k
 //    (exact). A row whose codes all decode to zero therefore gives exactly
 //    0.
-//  * Lanes are reduced with DPP (quad_perm, row_shr, row_bcast) instead of an
-//    LDS tree; teams of several waves add their wave totals through LDS in a
+//  * Lanes are reduced four rows at a time with gfx950's lane-half and
+//    lane-quarter swaps (v_permlane32_swap, v_permlane16_swap) and DPP
+//    (quad_perm, row_shr) instead of an LDS tree; teams of several waves add
+//    their wave totals through LDS in a
 //    fixed order, so results are deterministic. Row scales are read with
 //    scalar loads (the row index is wave-uniform), which do not wait on the
 //    weight stream.
@@ -227,23 +229,57 @@ __device__ __forceinline__ float dpp_move(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
 }
 
-// Sums of N values over the 64 lanes; each total lands in lane 63. The N
-// butterflies advance together, one step at a time, so independent DPP adds
-// sit back to back (one butterfly alone needs wait states between its
-// dependent steps).
-template <int N> __device__ __forceinline__ void wave_sums_lane63(float (&v)[N]) {
+// Sums of N values over the 64 lanes, up to four values per register:
+// v_permlane32_swap exchanges the upper lane half of value a with the lower
+// half of value b, so one add leaves a's half sums in lanes 0..31 and b's in
+// 32..63; v_permlane16_swap does the same for 16-lane quarters of two such
+// registers, and four DPP steps finish each 16-lane row. Every value is
+// summed in the same order whatever N and whatever its place in a register
+// (a missing partner is a zero), so launches with different ring depths give
+// identical sums. One or two values take a register each (independent
+// chains, and their totals share a lane); four or more share registers.
+// Total i ends in lane sum_lane<N>(i) of v[i]. About 10 VALU instructions per
+// four values, against 32 for four separate butterflies.
+template <int N> __host__ __device__ constexpr int sum_lane(int i) {
+    return N <= 2 ? 15 : (i & 3) == 0 ? 15 : (i & 3) == 1 ? 47 : (i & 3) == 2 ? 31 : 63;
+}
+
+__device__ __forceinline__ float swap32_add(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);  // lanes 0..31: a, 32..63: b
+}
+
+__device__ __forceinline__ float swap16_add(float a, float b) {
+    // a, b from swap32_add: 16-lane rows of the sum hold a.lo, b.lo, a.hi, b.hi
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int N> __device__ __forceinline__ void wave_sums_rows(float (&v)[N]) {
+    constexpr int P = N <= 2 ? 1 : 4;  // values per register
+    constexpr int G = (N + P - 1) / P;
+    // value in place p (0..3) of register g, or -1
+    auto slot = [](int g, int p) { return P == 1 ? (p == 0 ? g : -1) : (g * 4 + p < N ? g * 4 + p : -1); };
+    float q[2 * G], r[G];
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_move<0xB1>(v[i]);        // quad_perm [1,0,3,2]
+    for (int j = 0; j < 2 * G; ++j) {
+        const int a = slot(j / 2, 2 * (j % 2)), b = slot(j / 2, 2 * (j % 2) + 1);
+        q[j] = (a < 0 && b < 0) ? 0.0f : swap32_add(a < 0 ? 0.0f : v[a], b < 0 ? 0.0f : v[b]);
+    }
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x4E>(v[i]);        // quad_perm [2,3,0,1]
+    for (int g = 0; g < G; ++g) r[g] = swap16_add(q[2 * g], q[2 * g + 1]);
+    // rows of r[g]: places 0, 2, 1, 3; the registers' steps interleave so
+    // independent DPP adds sit back to back
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x114>(v[i]);       // row_shr:4
+    for (int g = 0; g < G; ++g) r[g] += dpp_move<0xB1>(r[g]);   // quad_perm [1,0,3,2]
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x118>(v[i]);       // row_shr:8
+    for (int g = 0; g < G; ++g) r[g] += dpp_move<0x4E>(r[g]);   // quad_perm [2,3,0,1]
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x142, 0xA>(v[i]);  // row_bcast:15 into rows 1 and 3
+    for (int g = 0; g < G; ++g) r[g] += dpp_move<0x114>(r[g]);  // row_shr:4
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] += dpp_move<0x143, 0xC>(v[i]);  // row_bcast:31 into rows 2 and 3
+    for (int g = 0; g < G; ++g) r[g] += dpp_move<0x118>(r[g]);  // row_shr:8: lane 15 of each row
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = r[i / P];
 }
 
 // One team processes rows [row_begin, row_begin + rpt) (rows >= O are not
@@ -471,7 +507,37 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
         }
     };
 
-    // Finish D rows starting at row0: part[d][s] holds this wave's totals.
+    // The wave totals of part[d][s]: paired rows reduce the gate (even d)
+    // and up (odd d) values separately, so both totals of an output sit in
+    // the same lane.
+    constexpr int NS = PAIR ? D / 2 * SMAX : D * SMAX;
+    auto tot_lane = [&](int d, int s) { return sum_lane<NS>(PAIR ? (d >> 1) * SMAX + s : d * SMAX + s); };
+    auto reduce = [&](float (&part)[D][SMAX]) {
+        if constexpr (PAIR) {
+            float gv[NS], uv[NS];
+#pragma unroll
+            for (int d = 0; d < D; d += 2)
+#pragma unroll
+                for (int s = 0; s < SMAX; ++s) {
+                    gv[(d >> 1) * SMAX + s] = part[d][s];
+                    uv[(d >> 1) * SMAX + s] = part[d + 1][s];
+                }
+            wave_sums_rows(gv);
+            wave_sums_rows(uv);
+#pragma unroll
+            for (int d = 0; d < D; d += 2)
+#pragma unroll
+                for (int s = 0; s < SMAX; ++s) {
+                    part[d][s] = gv[(d >> 1) * SMAX + s];
+                    part[d + 1][s] = uv[(d >> 1) * SMAX + s];
+                }
+        } else {
+            wave_sums_rows(reinterpret_cast<float(&)[D * SMAX]>(part));
+        }
+    };
+
+    // Finish D rows starting at row0: lane tot_lane(d, s) of part[d][s]
+    // holds this wave's total.
     int pb = 0;
     const int Oy = PAIR ? O / 2 : O;  // output rows (row stride of y)
     int cpos = 0;  // rows of the open chunk (team > 1, not PAIR)
@@ -485,21 +551,21 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                         const int oc = min(o, Oy - 1);
                         const float sg = GS ? 1.0f : uniform_ld(scales + oc);
                         const float su = GS ? 1.0f : uniform_ld(scales2 + oc);
-                        if (lane == 63 && row0 + d <= row_last) {
+                        if (row0 + d <= row_last) {
 #pragma unroll
                             for (int s = 0; s < SMAX; ++s)
-                                if (s < S) y[(long)s * Oy + o] = gated(sg * part[d][s], su * part[d + 1][s]);
+                                if (lane == tot_lane(d, s) && s < S)
+                                    y[(long)s * Oy + o] = gated(sg * part[d][s], su * part[d + 1][s]);
                         }
                     }
                 }
             } else {
                 float *rbuf = red + pb * (kMaxTeam * D * SMAX);
-                if (lane == 63) {
 #pragma unroll
-                    for (int d = 0; d < D; ++d)
+                for (int d = 0; d < D; ++d)
 #pragma unroll
-                        for (int s = 0; s < SMAX; ++s) rbuf[(wave_in_team * D + d) * SMAX + s] = part[d][s];
-                }
+                    for (int s = 0; s < SMAX; ++s)
+                        if (lane == tot_lane(d, s)) rbuf[(wave_in_team * D + d) * SMAX + s] = part[d][s];
                 float sg[D / 2], su[D / 2];
 #pragma unroll
                 for (int j = 0; j < D / 2; ++j) {
@@ -535,10 +601,10 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 if (d < nvalid) {
                     const int row = row0 + d;
                     const float sc = GS ? 1.0f : uniform_ld(scales + min(row, O - 1));
-                    if (lane == 63 && row <= row_last) {
+                    if (row <= row_last) {
 #pragma unroll
                         for (int s = 0; s < SMAX; ++s)
-                            if (s < S) y[(long)s * O + row] = sc * part[d][s];
+                            if (lane == tot_lane(d, s) && s < S) y[(long)s * O + row] = sc * part[d][s];
                     }
                 }
             }
@@ -550,13 +616,11 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             // n + 1 also tells that wave 0 has read chunk n.
             float *cbuf = red + pb * (kTeamChunk * kMaxTeam * SMAX);
             float *sbuf = red + 2 * (kTeamChunk * kMaxTeam * SMAX) + pb * kTeamChunk;
-            if (lane == 63) {
 #pragma unroll
-                for (int d = 0; d < D; ++d)
+            for (int d = 0; d < D; ++d)
 #pragma unroll
-                    for (int s = 0; s < SMAX; ++s)
-                        cbuf[((cpos + d) * kMaxTeam + wave_in_team) * SMAX + s] = part[d][s];
-            }
+                for (int s = 0; s < SMAX; ++s)
+                    if (lane == tot_lane(d, s)) cbuf[((cpos + d) * kMaxTeam + wave_in_team) * SMAX + s] = part[d][s];
             if (wave_in_team == 0) {
 #pragma unroll
                 for (int d = 0; d < D; ++d) {
@@ -596,7 +660,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
             // wave then has no weight load in flight between ring passes
             __builtin_amdgcn_sched_barrier(0);
         }
-        wave_sums_lane63(reinterpret_cast<float(&)[D * SMAX]>(part));
+        reduce(part);
         finish(row_begin + i, part, D, false);
     }
     {
@@ -610,7 +674,7 @@ __device__ __forceinline__ void team_rows(const uint8_t *__restrict__ w, long st
                 for (int s = 0; s < SMAX; ++s) part[d][s] = 0.0f;
             }
         }
-        wave_sums_lane63(reinterpret_cast<float(&)[D * SMAX]>(part));
+        reduce(part);
         finish(row_begin + i, part, rpt - i, true);
     }
 }
