@@ -288,6 +288,10 @@ const char *wq_strerror(int code);
  */
 int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen);
 
+/* The same for a tensor uploaded with wq_tensor_upload_gs(..., gs, ...)
+ * (gs = 0: as wq_describe_plan). WQ_E_INVAL also for gs < 0. */
+int wq_describe_plan_gs(int fmt, int O, int I, int S, int gs, char *buf, size_t buflen);
+
 /*
  * Measurement helper (not part of the matmul): the practical HBM read
  * ceiling. Reads `bytes` (a multiple of 16) from the device buffer buf_dev

@@ -238,8 +238,35 @@ def test_prefill_plan_uses_large_tiles():
     assert int(p["grid"]) == 256
 
 
+def _plan_gs(fmt, O, I, S, gs):
+    s = wq.wq_describe_plan_gs(fmt, O, I, S, gs)
+    kind, rest = s.split(" ", 1)
+    return kind, dict(kv.split("=") for kv in rest.split())
+
+
+@pytest.mark.parametrize("fmt,O,I,S,gs,kind", [
+    (wq.WQ_I4, 12288, 6144, 2, 128, "skinny"), (wq.WQ_I4, 12288, 6144, 8, 128, "skinny"),
+    (wq.WQ_I4, 12288, 6144, 12, 128, "skinny"), (wq.WQ_I2, 16384, 8192, 16, 256, "skinny"),
+    (wq.WQ_I4, 12288, 6144, 16, 256, "skinny"), (wq.WQ_I8, 6144, 6144, 12, 128, "skinny"),
+    (wq.WQ_I2, 16384, 8192, 8, 256, "skinny"), (wq.WQ_I4, 300, 1000, 5, 128, "skinny"),
+    # a chunk would straddle two groups: int4/int8 gs % 128, int2 gs % 256
+    (wq.WQ_I4, 12288, 6144, 8, 64, "tiled"), (wq.WQ_I2, 16384, 8192, 8, 128, "tiled"),
+    (wq.WQ_I4, 12288, 6144, 17, 128, "tiled"),  # group scales stop at S = 16 here
+    (wq.WQ_I4, 12288, 6144, 1, 128, "gemv"), (wq.WQ_I4, 12288, 6144, 8, 0, "skinny")])
+def test_group_scaled_plans(fmt, O, I, S, gs, kind):
+    k, p = _plan_gs(fmt, O, I, S, gs)
+    assert k == kind, (k, p)
+    if k == "skinny" and gs > 0:  # group-scaled tiles: two chunks in flight; 4-wave blocks for m = 3 only
+        assert p["ring"] == "2" and p["waves"] in ("8", "4"), p
+        if p["waves"] == "4":
+            assert p["m"] == "3" and int(p["nb"]) >= 3 and int(p["grid"]) <= 256, p
+    if gs == 0:
+        assert wq.wq_describe_plan(fmt, O, I, S) == wq.wq_describe_plan_gs(fmt, O, I, S, 0)
+
+
 def test_plan_rejects_bad_arguments():
     buf = ctypes.create_string_buffer(64)
+    assert wq.lib.wq_describe_plan_gs(2, 4, 4, 1, -1, buf, 64) == wq.WQ_E_INVAL
     assert wq.lib.wq_describe_plan(9, 4, 4, 1, buf, 64) == wq.WQ_E_INVAL
     assert wq.lib.wq_describe_plan(0, 0, 4, 1, buf, 64) == wq.WQ_E_INVAL
     assert wq.lib.wq_describe_plan(0, 4, 4, -1, buf, 64) == wq.WQ_E_INVAL

@@ -40,7 +40,7 @@ def check(fmt, O, I, S, gs, seed, rows=None, what="gs", x_offset=0):
     t = upload_gs(fmt, O, I, gs, p.w, sc)
     try:
         gu.banner("%s fmt=%d O=%d I=%d S=%d gs=%d x_offset=%d plan=%s" % (what, fmt, O, I, S, gs, x_offset,
-                                                                         wq.wq_describe_plan(fmt, O, I, S)))
+                                                                         wq.wq_describe_plan_gs(fmt, O, I, S, gs)))
         y = gu.run_dev(t, p.x, x_offset=x_offset)
     finally:
         wq.wq_tensor_free(t)
@@ -86,6 +86,54 @@ def test_group_scales_forced_tile_shapes(shape, fmt, O, I, S, gs):
         check(fmt, O, I, S, gs, seed=8900 + O + S, what="gs-tile-" + shape)
     finally:
         gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_SHAPE=None)
+
+
+# Few activation rows on the matrix cores with group scales: ragged o blocks
+# (O not a multiple of 16 * nb), ragged last chunk and group, every compiled
+# stack of fragments (S = 2..16) and several groups per chunk pair (gs = 128)
+# or chunks per group (gs >= 256).
+@pytest.mark.parametrize("fmt,O,I,S,gs", [(I4, 300, 1000, 2, 128), (I4, 517, 3000, 5, 384), (I4, 70, 2048, 6, 128),
+                                         (I4, 1000, 6144, 11, 256), (I4, 45, 1100, 16, 128),
+                                         (I8, 300, 1000, 4, 128), (I8, 257, 2500, 9, 256), (I8, 129, 640, 13, 128),
+                                         (I2, 300, 1000, 3, 256), (I2, 700, 4100, 8, 512), (I2, 60, 8192, 16, 256),
+                                         # many output rows at 11..16 rows: 4-wave blocks of 3-4 output blocks
+                                         (I8, 9000, 700, 14, 128), (I4, 10000, 1300, 16, 256),
+                                         (I2, 12000, 1032, 12, 256)])
+def test_group_scales_few_rows_kernel(fmt, O, I, S, gs):
+    assert wq.wq_describe_plan_gs(fmt, O, I, S, gs).startswith("skinny")
+    check(fmt, O, I, S, gs, seed=8700 + O + I + S + gs, what="gs-skinny")
+
+
+@pytest.mark.parametrize("S", [2, 8, 16])
+def test_group_scales_few_rows_decode_shape(S):
+    """int4 12288 x 6144, gs = 128, the batched-decode shapes, on sampled rows."""
+    assert wq.wq_describe_plan_gs(I4, 12288, 6144, S, 128).startswith("skinny")
+    rows = np.arange(5, 12288, 89)
+    check(I4, 12288, 6144, S, 128, seed=8650 + S, rows=rows, what="gs-skinny-dense")
+
+
+def test_group_scales_few_rows_bit_identical_to_forced_tiled_on_integers():
+    """Integer activations and integer group scales: every partial sum is an
+    exact integer below 2^24, so the few-rows kernel and the tiled kernel must
+    agree bit for bit (and with the oracle)."""
+    fmt, O, I, S, gs = I4, 200, 1024, 8, 128
+    p = synth.ragged(fmt, O, I, S, seed=8800)
+    p.x = synth.rng(8801).integers(-4, 5, size=(S, I)).astype(np.float32)
+    sc = synth.rng(8802).integers(1, 4, size=(O, oracle.n_groups(I, gs))).astype(np.float32)
+    t = upload_gs(fmt, O, I, gs, p.w, sc)
+    try:
+        assert wq.wq_describe_plan_gs(fmt, O, I, S, gs).startswith("skinny")
+        gu.banner("gs integers skinny")
+        y1 = gu.run_dev(t, p.x)
+        gu.reinit_with_env(WQ_FORCE_PATH="tiled")
+        gu.banner("gs integers tiled")
+        y2 = gu.run_dev(t, p.x)
+    finally:
+        gu.reinit_with_env(WQ_FORCE_PATH=None)
+        wq.wq_tensor_free(t)
+    y_ref, _ = oracle.matmul_gs(fmt, p.w, sc, gs, p.x)
+    np.testing.assert_array_equal(y1, y2)
+    np.testing.assert_array_equal(y1, y_ref.astype(np.float32))
 
 
 def test_group_scales_dense_decode_shape():

@@ -142,15 +142,14 @@ def test_near_zero_rows_swiglu(fmt, I, S, smallest):
             wq.wq_tensor_free(t)
 
 
-@pytest.mark.parametrize("fmt,I", [(I4, 6144), (I2, 8192)])
-@pytest.mark.parametrize("S", [1, 2, 24])
-def test_near_zero_rows_group_scales(fmt, I, S):
+@pytest.mark.parametrize("fmt,I,gs", [(I4, 6144, 128), (I2, 8192, 128), (I2, 8192, 256)])
+@pytest.mark.parametrize("S", [1, 2, 8, 24])
+def test_near_zero_rows_group_scales(fmt, I, gs, S):
     p = near_zero_problem(fmt, 200, I, S, seed=15000 + 10 * fmt + S, smallest=True)
-    gs = 128
     gsc = synth.rng(15001 + S).uniform(0.002, 0.05, size=(p.O, oracle.n_groups(I, gs))).astype(np.float32)
     t = wq.wq_tensor_upload_gs(None, gu.DEV, fmt, p.O, I, gs, p.w, gsc)
     try:
-        gu.banner("near-zero gs=%d fmt=%d S=%d" % (gs, fmt, S))
+        gu.banner("near-zero gs=%d fmt=%d S=%d plan=%s" % (gs, fmt, S, wq.wq_describe_plan_gs(fmt, p.O, I, S, gs)))
         y = gu.run_dev(t, p.x)
     finally:
         wq.wq_tensor_free(t)

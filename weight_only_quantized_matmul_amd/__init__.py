@@ -72,6 +72,7 @@ def _bind(lib):
         "wq_tensor_free": (ci, [vp]),
         "wq_strerror": (ctypes.c_char_p, [ci]),
         "wq_describe_plan": (ci, [ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t]),
+        "wq_describe_plan_gs": (ci, [ci, ci, ci, ci, ci, ctypes.c_char_p, ctypes.c_size_t]),
         "wq_stream_read_dev": (ci, [vp, ctypes.c_size_t, ci, ci, vp, vp]),
         "wq_matmul_dev_noalloc": (ci, [vp, vp, ci, vp, vp]),
         "wq_noalloc_scratch_bytes": (ctypes.c_size_t, []),
@@ -355,6 +356,12 @@ def wq_tensor_free(t: Tensor) -> None:
 def wq_describe_plan(fmt: int, O: int, I: int, S: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib.wq_describe_plan(int(fmt), int(O), int(I), int(S), buf, 256), "wq_describe_plan")
+    return buf.value.decode()
+
+
+def wq_describe_plan_gs(fmt: int, O: int, I: int, S: int, gs: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib.wq_describe_plan_gs(int(fmt), int(O), int(I), int(S), int(gs), buf, 256), "wq_describe_plan_gs")
     return buf.value.decode()
 
 

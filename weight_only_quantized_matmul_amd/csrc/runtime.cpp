@@ -175,11 +175,11 @@ int group_gemv_limit(int fmt) {
 // kernel for few rows). x_vec: x is 16-byte aligned (the few-rows kernel
 // reads it in 16-byte runs and also needs I % 4 == 0).
 // Group-scaled tensors (gs) never take the few-rows kernel.
-int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, bool gs = false, bool x_vec = true,
+int choose_path(int fmt, int O, int I, int S, int cus, wq::GemvPlan *gp, int gs = 0, bool x_vec = true,
                 wq::SkinnyPlan *sp = nullptr) {
     auto skinny_ok = [&]() {
-        if (gs || !x_vec) return false;
-        const wq::SkinnyPlan p = wq::plan_skinny(fmt, O, I, S, cus, g_cfg.skinny_ring);
+        if (!x_vec) return false;
+        const wq::SkinnyPlan p = wq::plan_skinny(fmt, O, I, S, cus, g_cfg.skinny_ring, gs);
         if (sp) *sp = p;
         return p.ok;
     };
@@ -274,7 +274,7 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
     wq::GemvPlan gp;
     wq::SkinnyPlan skp;
     const bool x_vec = ((uintptr_t)x & 15) == 0;
-    const int path = choose_path(t->fmt, t->O, t->I, S, d.cus, &gp, t->gs > 0, x_vec, &skp);
+    const int path = choose_path(t->fmt, t->O, t->I, S, d.cus, &gp, t->gs, x_vec, &skp);
     if (path == 3) {
         wq::SkinnyArgs a;
         a.w = t->d_w;
@@ -288,6 +288,9 @@ int run_matmul(const wq_tensor *t, const float *x, int S, float *y, hipStream_t 
         a.S = S;
         a.chunks_per_wave = skp.chunks_per_wave;
         a.nchunks = skp.nchunks;
+        a.gscales_t = t->d_scales_t;
+        a.gs = t->gs;
+        a.ng = t->ng;
         return hip_status(wq::launch_skinny(t->fmt, skp, a, st));
     }
     if (path == 1) {
@@ -821,7 +824,7 @@ int run_swiglu(const wq_tensor *gt, const wq_tensor *ut, const float *x, int S, 
         return hip_status(wq::launch_gemv(gp, a, st));
     }
     size_t planes = 0;  // the path run_matmul will take for gate and up (same shape and x)
-    if (choose_path(gt->fmt, gt->O, gt->I, S, d.cus, &gp, gt->gs > 0, ((uintptr_t)x & 15) == 0) == 2)
+    if (choose_path(gt->fmt, gt->O, gt->I, S, d.cus, &gp, gt->gs, ((uintptr_t)x & 15) == 0) == 2)
         planes = wq::plan_tiled(gt->fmt, gt->O, gt->I, S, g_cfg.tiled_mode, g_cfg.tiled_shape, gt->gs).ws_bytes;
     const size_t off = (size_t)wq::round_up((long)planes, 256);
     uint16_t *ws = nullptr;
@@ -989,7 +992,11 @@ int wq_stream_read_dev(const void *buf_dev, size_t bytes, int waves, int loads_i
 }
 
 int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
-    if (!valid_fmt(fmt) || O <= 0 || I <= 0 || S < 0 || buf == nullptr || buflen == 0) return WQ_E_INVAL;
+    return wq_describe_plan_gs(fmt, O, I, S, 0, buf, buflen);
+}
+
+int wq_describe_plan_gs(int fmt, int O, int I, int S, int gs, char *buf, size_t buflen) {
+    if (!valid_fmt(fmt) || O <= 0 || I <= 0 || S < 0 || gs < 0 || buf == nullptr || buflen == 0) return WQ_E_INVAL;
     const int cus = device_open(0) ? g_dev[0].cus : kDefaultCUs;
     if (S == 0) {
         snprintf(buf, buflen, "none");
@@ -997,7 +1004,7 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
     }
     wq::GemvPlan gp;
     wq::SkinnyPlan sp;
-    const int path = choose_path(fmt, O, I, S, cus, &gp, false, true, &sp);
+    const int path = choose_path(fmt, O, I, S, cus, &gp, gs, true, &sp);
     if (path == 1) {
         snprintf(buf, buflen, "gemv fmt=%d smax=%d lw=%d kmax=%d k=%d team=%d d=%d rows_per_team=%d grid=%d block=%d",
                  fmt, gp.smax, gp.lw, gp.kmax, gp.k, gp.team, gp.d, gp.rows_per_team, gp.grid, gp.block);
@@ -1007,7 +1014,7 @@ int wq_describe_plan(int fmt, int O, int I, int S, char *buf, size_t buflen) {
                  "workspace=0",
                  fmt, sp.m, sp.rpl, sp.nb, sp.waves, sp.ring, sp.nchunks, sp.chunks_per_wave, sp.grid, 64 * sp.waves);
     } else {
-        const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S, g_cfg.tiled_mode, g_cfg.tiled_shape);
+        const wq::TiledPlan tp = wq::plan_tiled(fmt, O, I, S, g_cfg.tiled_mode, g_cfg.tiled_shape, gs);
         snprintf(buf, buflen,
                  "tiled fmt=%d mode=%s bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d ksplit=%d grid=%d block=%d "
                  "workspace=%zu",

@@ -39,6 +39,12 @@
 //    per step), and the waves' partial tiles are added through LDS at the
 //    end in fixed order (deterministic; no split-K kernel and no second
 //    launch).
+//  * Group-wise scales (GS): a chunk's positions lie in one group when the
+//    group size is a multiple of the positions a chunk spans (128; int2 256),
+//    so each chunk's MFMAs go to fresh accumulators that are then added to
+//    the running tile times the group scale of their column (the output
+//    row), read from the group-major copy of the scales with the chunk's
+//    loads.
 //  * The operand buffer is swizzled so that any 8 consecutive lanes touch 8
 //    distinct 16-byte bank groups, both when they write it (two stacked rows
 //    x four k-groups) and when the MFMA reads it (eight rows of one
@@ -167,12 +173,17 @@ __device__ __forceinline__ int opnd_slot(int rho, int j, int g, int S) {
     return ((rho >> 4) * 4 + j) * 64 + 16 * g + (((rho & 15) + S * j + 2 * g) & 15);
 }
 
+// Group of the field positions of chunk c (all in one group, see GS above).
+template <int FMT> __device__ __forceinline__ int chunk_group(int c, int gs, int ng) {
+    return min(chunk_pos<FMT>(c, 0, 0) / gs, ng - 1);
+}
+
 // M: stacked operand fragments (3 S <= 16 M); RPL: 8-position activation
 // runs per lane per chunk (16 S runs per chunk, so RPL = ceil(S / 4));
 // NB: 16-row output blocks per wave (and block); WAVES: waves per block,
 // each streaming its own chunks; R: chunks of loads in flight (even);
-// NBUF: operand buffers per wave (1 or 2).
-template <int FMT, int M, int RPL, int NB, int WAVES, int R, int NBUF>
+// NBUF: operand buffers per wave (1 or 2); GS: group-wise scales.
+template <int FMT, int M, int RPL, int NB, int WAVES, int R, int NBUF, bool GS = false>
 __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     static_assert(R % 2 == 0, "the load ring advances by chunk pairs");
     static_assert(NBUF == 1 || NBUF == 2, "one or two operand buffers");
@@ -251,6 +262,21 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
                 wv[u][b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.w + (roff[b] + off)));
         }
     };
+    // GS: the group scale of this lane's column (output row, clamped like
+    // the weight rows) for both chunks of a pair
+    uint32_t scol[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) scol[b] = (uint32_t)min(o0 + 16 * b + li, O - 1);
+    auto load_s = [&](float (&sv)[2][NB], int c2) __attribute__((always_inline)) {
+        if constexpr (GS) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t gbase = (uint32_t)chunk_group<FMT>(c2 + h, a.gs, a.ng) * (uint32_t)O;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) sv[h][b] = a.gscales_t[gbase + scol[b]];
+            }
+        }
+    };
     const uint32_t xlast = (uint32_t)(S * I - 4);
     auto load_x = [&](f32x4 (&xv)[2][RPL][2], int c2) __attribute__((always_inline)) {
 #pragma unroll
@@ -277,10 +303,12 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     constexpr int RP = R / 2;  // chunk pairs in flight
     u32x4 wring[RP][L2][NB];
     f32x4 xring[RP][2][RPL][2];
+    float sring[RP][2][NB];  // GS only
 #pragma unroll
     for (int p = 0; p < RP; ++p) {
         load_x(xring[p], pair_c2(p));
         load_w(wring[p], pair_c2(p));
+        load_s(sring[p], pair_c2(p));
     }
 
     // ---- one chunk: split its activations into an operand buffer, then
@@ -291,8 +319,8 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     // wave writes and reads each buffer: its LDS operations complete in
     // order, and the buffer's accesses may alias, so the compiler keeps them
     // in program order.
-    auto do_chunk = [&](auto full_c, const f32x4 (&xv)[RPL][2], const u32x4 (&wv)[L2][NB], int c,
-                        int h) __attribute__((always_inline)) {
+    auto do_chunk = [&](auto full_c, const f32x4 (&xv)[RPL][2], const u32x4 (&wv)[L2][NB],
+                        const float (&sv)[NB], int c, int h) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_c)::value;
         u32x4 *buf = abuf + (NBUF == 2 ? h : 0) * (ABUF / 16);
         const int cpos = chunk_pos<FMT>(c, 0, 0);
@@ -328,6 +356,7 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
                                                 pack_hi(pl[p][4], pl[p][5]), pack_hi(pl[p][6], pl[p][7])};
             }
         }
+        f32x4 tmp[NB][M];  // GS: this chunk's sums (one group)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             bf16x8 av[M];
@@ -352,15 +381,28 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
                 }
                 const bf16x8 bv = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
-                for (int m = 0; m < M; ++m)
-                    acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, acc[b][m], 0, 0, 0);
+                for (int m = 0; m < M; ++m) {
+                    if constexpr (GS)
+                        tmp[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av[m], bv, j == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : tmp[b][m], 0, 0, 0);
+                    else
+                        acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[m], bv, acc[b][m], 0, 0, 0);
+                }
             }
         }
+        if constexpr (GS) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[b][m][r] = __builtin_fmaf(sv[b], tmp[b][m][r], acc[b][m][r]);
+        }
     };
-    auto chunk = [&](const f32x4 (&xv)[RPL][2], const u32x4 (&wv)[L2][NB], int c, int h)
+    auto chunk = [&](const f32x4 (&xv)[RPL][2], const u32x4 (&wv)[L2][NB], const float (&sv)[NB], int c, int h)
         __attribute__((always_inline)) {
-        if (c < c_full) do_chunk(std::true_type{}, xv, wv, c, h);  // wave-uniform branch
-        else do_chunk(std::false_type{}, xv, wv, c, h);
+        if (c < c_full) do_chunk(std::true_type{}, xv, wv, sv, c, h);  // wave-uniform branch
+        else do_chunk(std::false_type{}, xv, wv, sv, c, h);
     };
 
     // (the pair checks are wave-uniform: skipping work changes no load count)
@@ -371,12 +413,13 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
             const int k = kk + p;
             if (pair_live(k)) {
                 const int c2 = 2 * (wave + WAVES * k);
-                chunk(xring[p][0], wring[p], c2, 0);
-                chunk(xring[p][1], wring[p], c2 + 1, 1);
+                chunk(xring[p][0], wring[p], sring[p][0], c2, 0);
+                chunk(xring[p][1], wring[p], sring[p][1], c2 + 1, 1);
             }
             // refill this slot with the wave's pair RP pairs ahead
             load_x(xring[p], pair_c2(k + RP));
             load_w(wring[p], pair_c2(k + RP));
+            load_s(sring[p], pair_c2(k + RP));
         }
     }
 #pragma unroll
@@ -384,8 +427,8 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
         const int k = kk + p;
         if (k < npairs && pair_live(k)) {
             const int c2 = 2 * (wave + WAVES * k);
-            chunk(xring[p][0], wring[p], c2, 0);
-            chunk(xring[p][1], wring[p], c2 + 1, 1);
+            chunk(xring[p][0], wring[p], sring[p][0], c2, 0);
+            chunk(xring[p][1], wring[p], sring[p][1], c2 + 1, 1);
         }
     }
 
@@ -411,7 +454,7 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
                 const int lc = ((rho & 15) >> 2) * 16 + col;
                 sum += red[(((w * NB + b) * M + (rho >> 4)) * 64 + lc) * 4 + (rho & 3)];
             }
-        a.y[(long)s * O + o] = a.scales[o] * (sum * SkF<FMT>::UNSCALE);
+        a.y[(long)s * O + o] = GS ? sum * SkF<FMT>::UNSCALE : a.scales[o] * (sum * SkF<FMT>::UNSCALE);
     }
 }
 

@@ -21,6 +21,20 @@ constexpr int skinny_max_ring(int fmt, int m, int rpl, int nb) {
     return f < 0 || k < 0 || nb < 1 || nb > 4 ? 0 : kRing[f][k][nb - 1];
 }
 
+// Group-scaled tiles (fresh accumulators per chunk beside the running ones)
+// that keep every value in registers with two chunks in flight (from the
+// compiled register counts): 8-wave blocks at two waves per SIMD, and for
+// three stacked fragments (11 <= S <= 16) also 4-wave blocks at one wave per
+// SIMD, whose larger register file holds three or four output blocks.
+constexpr bool skinny_gs_ok(int fmt, int m, int rpl, int nb, int waves) {
+    if (fmt < WQ_I8 || fmt > WQ_I2 || m < 1 || m > 3 || rpl < 1 || rpl > 4 || nb < 1 || nb > 4) return false;
+    if (waves == 4) return m == 3 && nb >= 3;
+    if (waves != 8) return false;
+    if (m * nb <= 6) return true;
+    const int k = m * 100 + rpl * 10 + nb;
+    return k == 224 || k == 333 || (k == 234 && fmt != WQ_I8) || (k == 343 && fmt == WQ_I2);
+}
+
 // 16 waves of one 16-row block (for few output rows) keep every value in
 // registers at four waves per SIMD (from the compiled register counts).
 constexpr bool skinny_wide_ok(int fmt, int m, int rpl) {
@@ -32,6 +46,19 @@ namespace {
 template <int FMT, int M, int RPL>
 hipError_t launch_mr(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st) {
     const dim3 grid(p.grid), block(64 * p.waves);
+    if (a.gs > 0) {  // group-wise scales: two chunks in flight
+#define WQ_SKG(NB_, W_)                                                                                         \
+    if constexpr (skinny_gs_ok(FMT, M, RPL, NB_, W_)) {                                                         \
+        if (p.nb == NB_ && p.waves == W_ && p.ring == 2) {                                                      \
+            hipLaunchKernelGGL((skinny_kernel<FMT, M, RPL, NB_, W_, 2, skinny_nbuf(M, NB_, W_), true>), grid, \
+                               block, 0, st, a);                                                                \
+            return hipGetLastError();                                                                           \
+        }                                                                                                       \
+    }
+        WQ_SKG(1, 8) WQ_SKG(2, 8) WQ_SKG(3, 8) WQ_SKG(4, 8) WQ_SKG(3, 4) WQ_SKG(4, 4)
+#undef WQ_SKG
+        return hipErrorInvalidValue;
+    }
 #define WQ_SK(NB_, W_, R_)                                                                           \
     if (p.nb == NB_ && p.waves == W_ && p.ring == R_) {                                              \
         hipLaunchKernelGGL((skinny_kernel<FMT, M, RPL, NB_, W_, R_, skinny_nbuf(M, NB_, W_)>), grid, \
@@ -62,6 +89,7 @@ hipError_t launch_f(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st) {
     case 33: return launch_mr<FMT, 3, 3>(p, a, st);
     case 34: return launch_mr<FMT, 3, 4>(p, a, st);
     default:  // 4-wave blocks, S > 16
+        if (a.gs > 0) return hipErrorInvalidValue;
         return FMT == WQ_I8 ? launch_skinny_wide_i8(p, a, st)
              : FMT == WQ_I4 ? launch_skinny_wide_i4(p, a, st)
                             : launch_skinny_wide_i2(p, a, st);
@@ -70,10 +98,14 @@ hipError_t launch_f(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st) {
 
 } // namespace
 
-SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring) {
+SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring, int gs) {
     SkinnyPlan p;
     if ((fmt != WQ_I8 && fmt != WQ_I4 && fmt != WQ_I2) || O <= 0 || I < 4 || I % 4 != 0 || S < 1 ||
         S > kSkinnyMaxS)
+        return p;
+    // group-wise scales: a chunk's positions in one group, the 8-wave tiles
+    if (gs < 0 || (gs > 0 && (S > 16 || gs % (fmt == WQ_I2 ? 2 * kChunk : kChunk) != 0 ||
+                              (long)O * ((I + gs - 1) / gs) >= (1L << 31))))
         return p;
     const long stride = round_up(row_bytes(fmt, I), kRowAlign);
     const long npos = stride * elems_per_byte(fmt);
@@ -92,11 +124,12 @@ SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring) {
         p.nb = 1;
         p.waves = 8;
         if (row_blocks < cus) {  // few output rows: more waves per block share each row's chunks
-            if (skinny_wide_ok(fmt, p.m, p.rpl)) p.waves = 16;
+            if (skinny_wide_ok(fmt, p.m, p.rpl) && gs == 0) p.waves = 16;
         } else {
             long best = -1;
             for (int nb = 1; nb <= 4; ++nb) {
                 if (skinny_max_ring(fmt, p.m, p.rpl, nb) == 0) continue;
+                if (gs > 0 && !skinny_gs_ok(fmt, p.m, p.rpl, nb, 8)) continue;
                 const long blocks = (row_blocks + nb - 1) / nb;
                 const long cost = (blocks + cus - 1) / cus * (1 + nb);
                 if (best < 0 || cost < best) {
@@ -104,11 +137,22 @@ SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring) {
                     p.nb = nb;
                 }
             }
+            // group-scaled three-fragment tiles: when the 8-wave blocks that
+            // keep their registers take more than one round, 4-wave blocks
+            // of three or four output blocks at one wave per SIMD
+            if (gs > 0 && p.m == 3 && (row_blocks + p.nb - 1) / p.nb > cus) {
+                for (int nb = 3; nb <= 4; ++nb)
+                    if (skinny_gs_ok(fmt, p.m, p.rpl, nb, 4) && (row_blocks + nb - 1) / nb <= cus) {
+                        p.nb = nb;
+                        p.waves = 4;
+                        break;
+                    }
+            }
         }
         // two chunks of loads in flight (the fastest measured), or a deeper
         // spill-free ring when asked for
         const int deepest = skinny_max_ring(fmt, p.m, p.rpl, p.nb);
-        p.ring = (p.waves == 8 && (ring == 4 || ring == 6)) ? std::min(ring, deepest) : 2;
+        p.ring = (p.waves == 8 && gs == 0 && (ring == 4 || ring == 6)) ? std::min(ring, deepest) : 2;
     } else {
         // 17 <= S <= 32: four waves per block (their operand buffers fit in
         // LDS; one block per CU), compiled tiles (m, rpl) = (4, 5), (5, 6),

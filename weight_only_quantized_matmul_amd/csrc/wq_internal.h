@@ -290,6 +290,9 @@ struct SkinnyArgs {
     int O, I, S;
     int chunks_per_wave;  // 128-position chunks each wave streams (even)
     int nchunks;          // chunks per row (even): chunks past it hold no field positions
+    // group-wise scales (gs > 0): ng x O, group-major; scales is then unused
+    const float *gscales_t = nullptr;
+    int gs = 0, ng = 1;
 };
 
 constexpr int kSkinnyMaxS = 32;  // activation rows the few-rows kernel takes at most
@@ -307,7 +310,9 @@ struct SkinnyPlan {
 };
 // ring: 4 or 6 asks for that many chunks of loads in flight per wave (capped
 // at the deepest spill-free ring; 8-wave blocks only), else 2
-SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring);
+// gs > 0: group-wise scales (S <= 16 and gs a multiple of the positions one
+// chunk spans: 128 for int8/int4, 256 for int2; otherwise not ok).
+SkinnyPlan plan_skinny(int fmt, int O, int I, int S, int cus, int ring, int gs = 0);
 hipError_t launch_skinny(int fmt, const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
