@@ -122,7 +122,9 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
  *   scales: host pointer to O * ng floats, row-major (required).
  *   gs:     group size, a positive multiple of 64 (WQ_E_UNSUPPORTED otherwise;
  *           each 16-byte weight slot and each 64-column tiled step then lies
- *           inside one group).
+ *           inside one group). 2 <= S <= 16 runs on the few-rows matrix-core
+ *           kernel when gs is a multiple of 128 (int8, int4) or 256 (int2),
+ *           else on the tiled path (wq_describe_plan_gs tells which).
  * Formats int8/int4/int2 only (WQ_E_INVAL for WQ_F32 or gs <= 0). Otherwise
  * as wq_tensor_upload; a re-upload also checks gs (WQ_E_MISMATCH). The
  * tensor then works with every matmul call; groups containing such tensors
