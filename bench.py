@@ -54,9 +54,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dense_gemv",
-                    choices=["dense_gemv", "moe_decode", "moe_ffn", "moe_ffn_pipeline", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
+                    choices=["dense_gemv", "moe_decode", "moe_decode_s8", "moe_ffn", "moe_ffn_pipeline", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
                              "int2_gemv_s2", "int2_gemv_s16", "dense_gemv_s2", "dense_gemv_s4", "dense_gemv_s8",
-                             "dense_gemv_s16", "dense_gemv_gs128", "prefill_gs128",
+                             "dense_gemv_s16", "dense_gemv_gs128", "dense_gemv_s8_gs128", "prefill_gs128",
                              "prefill"])
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -104,10 +104,14 @@ def problems_for(name):
     import synth
     if name == "dense_gemv":
         return [synth.dense_gemv(S=1)], "dense_gemv: int4 W[12288,6144] (codes U{0..15}), scales U[0.002,0.05], x N(0,1), S=1"
-    if name.startswith("dense_gemv_s"):
+    if name.startswith("dense_gemv_s") and name[len("dense_gemv_s"):].isdigit():
         S = int(name[len("dense_gemv_s"):])
         return [synth.dense_gemv(S=S)], ("dense_gemv: int4 W[12288,6144] (codes U{0..15}), scales U[0.002,0.05], "
                                          "x N(0,1), S=%d" % S)
+    if name.startswith("moe_decode_s") and name[len("moe_decode_s"):].isdigit():
+        S = int(name[len("moe_decode_s"):])
+        return synth.moe_decode(S=S), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
+                                       "S=%d per expert, all 24 matmuls in one grouped call" % S)
     if name == "moe_decode":
         return synth.moe_decode(), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
                                     "S=1 per expert, all 24 matmuls in one grouped launch")
@@ -124,6 +128,11 @@ def problems_for(name):
         p.gs, p.gscales = 128, synth.group_scales(p, 128, 0.002, 0.05)
         return [p], ("dense_gemv_gs128: int4 W[12288,6144] (codes U{0..15}), one scale per row and group of 128 "
                      "columns U[0.002,0.05], x N(0,1), S=1")
+    if name == "dense_gemv_s8_gs128":
+        p = synth.dense_gemv(S=8)
+        p.gs, p.gscales = 128, synth.group_scales(p, 128, 0.002, 0.05)
+        return [p], ("dense_gemv_s8_gs128: int4 W[12288,6144] (codes U{0..15}), one scale per row and group of 128 "
+                     "columns U[0.002,0.05], x N(0,1), S=8")
     if name == "prefill_gs128":
         p = synth.prefill(S=512)
         p.gs, p.gscales = 128, synth.group_scales(p, 128, 0.001, 0.01)
@@ -159,7 +168,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
-    grouped = args.workload == "moe_decode"
+    grouped = args.workload == "moe_decode" or args.workload.startswith("moe_decode_s")
     ffn = args.workload in ("moe_ffn", "moe_ffn_pipeline")
     weight_bytes = sum(p.weight_bytes for p in probs)
 
@@ -261,7 +270,7 @@ def main():
         step_per_launch = per_launch
         per_launch = e0.elapsed_time(e1) / 1e3 / K
 
-    plans = [wq.wq_describe_plan(p.fmt, p.O, p.I, p.S) for p in probs]
+    plans = [wq.wq_describe_plan_gs(p.fmt, p.O, p.I, p.S, getattr(p, "gs", 0)) for p in probs]
     tiled = all(pl.startswith("tiled") for pl in plans)
     bf16x3 = tiled and all("mode=bf16x3" in pl for pl in plans)
     if compute_bound or tiled:

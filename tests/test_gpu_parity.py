@@ -176,6 +176,98 @@ def test_grouped_mixed_S_and_skips():
             wq.wq_tensor_free(t)
 
 
+@pytest.mark.parametrize("S", [5, 8, 16])
+def test_grouped_few_rows_one_launch(S):
+    """Several tokens per expert (above the grouped GEMV's rows): all 24
+    matmuls of the 8-expert step in one launch of the few-rows kernel."""
+    probs = synth.moe_decode(S=S)
+    ts = [gu.upload(p) for p in probs]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x).cuda() for p in probs]
+        bufs, ys = zip(*[gu.guarded_output(p.S, p.O) for p in probs])
+        gu.banner("grouped few rows S=%d: launch count" % S)
+        assert gu.count_kernel_launches(lambda: wq.wq_grouped_matmul_dev(g, xs, list(ys))) == 1
+        for b in bufs:
+            b.fill_(int(np.int32(gu.CANARY.view(np.int32))))
+        gu.banner("grouped few rows S=%d" % S)
+        wq.wq_grouped_matmul_dev(g, xs, list(ys))
+        torch.cuda.synchronize()
+        for p, b, y in zip(probs, bufs, ys):
+            gu.check_canaries(b, p.S, p.O)
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, p.name)
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
+@pytest.mark.parametrize("fmt", [I8, I4, I2])
+def test_grouped_few_rows_ragged_and_chunked(fmt):
+    """40 tensors of ragged shapes with 0..16 rows each (some skipped): the
+    few-rows kernel in launches of at most 32 active tensors."""
+    g0 = synth.rng(4400 + fmt)
+    probs, Ss = [], []
+    for i in range(40):
+        O = int(g0.integers(1, 700))
+        I = 4 * int(g0.integers(1, 900))
+        S = int(g0.choice([0, 1, 2, 5, 9, 13, 16]))
+        S = 16 if i == 3 else S  # the launch tile is the largest S
+        p = synth.ragged(fmt, O, I, max(S, 1), seed=4500 + 7 * i + fmt)
+        probs.append(p)
+        Ss.append(S)
+    ts = [gu.upload(p) for p in probs]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x[:S]).cuda() if S else None for p, S in zip(probs, Ss)]
+        outs = [gu.guarded_output(max(S, 1), p.O) for p, S in zip(probs, Ss)]
+        ys = [o[1] if S else None for o, S in zip(outs, Ss)]
+        active = sum(1 for S in Ss if S)
+        gu.banner("grouped few rows ragged fmt=%d active=%d: launch count" % (fmt, active))
+        assert gu.count_kernel_launches(lambda: wq.wq_grouped_matmul_dev(g, xs, ys)) == -(-active // 32)
+        for b, _ in outs:
+            b.fill_(int(np.int32(gu.CANARY.view(np.int32))))
+        gu.banner("grouped few rows ragged fmt=%d" % fmt)
+        wq.wq_grouped_matmul_dev(g, xs, ys)
+        torch.cuda.synchronize()
+        for p, S, (b, y) in zip(probs, Ss, outs):
+            if S == 0:
+                gu.check_canaries(b, 0, p.O)  # untouched
+                continue
+            gu.check_canaries(b, S, p.O)
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x[:S])
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, "%s S=%d" % (p.name, S))
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
+def test_grouped_few_rows_misaligned_x_falls_back():
+    """An activation buffer off a 16-byte boundary: per-tensor launches (the tiled path), same results."""
+    probs = synth.moe_decode(n_experts=2, S=8)
+    ts = [gu.upload(p) for p in probs]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = []
+        for p in probs:
+            buf = torch.zeros(p.S * p.I + 1, dtype=torch.float32, device="cuda")
+            buf[1:] = torch.from_numpy(p.x.reshape(-1)).cuda()
+            xs.append(buf[1:].view(p.S, p.I))
+        ys = [torch.empty((p.S, p.O), dtype=torch.float32, device="cuda") for p in probs]
+        gu.banner("grouped few rows misaligned")
+        wq.wq_grouped_matmul_dev(g, xs, ys)
+        torch.cuda.synchronize()
+        for p, y in zip(probs, ys):
+            y_ref, A = oracle.matmul(p.fmt, p.w, p.scales, p.x)
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, p.name)
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
 @pytest.mark.parametrize("fmt,S", [(I4, 1), (I8, 2), (I2, 1), (F32, 1)])
 def test_grouped_many_problems_mixed_row_lengths(fmt, S):
     # 70 problems (two launch chunks of at most 64) whose rows need 1..4 load

@@ -9,6 +9,7 @@
 // device, bad ordinals) are errors, not a silent CPU mode (colibri docs
 // "CUDA backend (Linux)", introduction).
 #include <algorithm>
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -16,6 +17,7 @@
 #include <mutex>
 #include <new>
 
+#include "skinny_group.h"
 #include "wq_internal.h"
 
 namespace {
@@ -858,6 +860,46 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
     const int bi = bucket == 1 ? 0 : bucket == 2 ? 1 : bucket == 4 ? 2 : bucket == 8 ? 3 : -1;
     const bool one_launch = !g->has_gs && g_cfg.force_path != 2 && g_cfg.force_path != 3 &&
                             smax <= group_gemv_limit(g->fmt) && bi >= 0 && g->buckets[bi].plan.ok;
+    if (!one_launch && !pair && !g->has_gs && g_cfg.force_path == 0) {
+        // 2..16 rows per tensor: the few-rows kernel over the whole group,
+        // one launch per kSkinnyGroupMax active tensors
+        wq::SkinnyGroupArgs a;
+        memset(&a, 0, sizeof a);
+        std::vector<wq::SkinnyGroupArgs> launches;
+        std::vector<wq::SkinnyGroupPlan> plans;
+        bool ok = true;
+        for (int i = 0; i < g->G && ok; ++i) {
+            if (S[i] == 0) continue;
+            const wq_tensor *t = g->ts[i];
+            if (((uintptr_t)x_dev[i] & 15) != 0 || t->stride >= INT_MAX) ok = false;
+            wq::SkinnyGroupDesc &e = a.t[a.n++];
+            e.w = t->d_w;
+            e.scales = t->d_scales;
+            e.x = x_dev[i];
+            e.y = y_dev[i];
+            e.stride = (int)t->stride;
+            e.nfull = t->nfull;
+            e.O = t->O;
+            e.I = t->I;
+            e.S = S[i];
+            if (a.n == wq::kSkinnyGroupMax) {
+                launches.push_back(a);
+                memset(&a, 0, sizeof a);
+            }
+        }
+        if (a.n > 0) launches.push_back(a);
+        for (size_t c = 0; c < launches.size() && ok; ++c) {
+            plans.push_back(wq::plan_skinny_group(g->fmt, launches[c].t, launches[c].n, g_dev[g->device].cus));
+            ok = plans.back().ok;
+        }
+        if (ok) {
+            for (size_t c = 0; c < launches.size(); ++c) {
+                int rc = hip_status(wq::launch_skinny_group(g->fmt, plans[c], launches[c], st));
+                if (rc != WQ_OK) return rc;
+            }
+            return WQ_OK;
+        }
+    }
     if (!one_launch) {
         for (int i = 0; i < g->G; ++i) {
             if (S[i] == 0) continue;

@@ -1,0 +1,41 @@
+// Grouped few-rows launch: the tensors of a group (one format, 2..16
+// activation rows each) in one launch of the few-rows matrix-core kernel
+// (grouped expert matmuls of a mixture-of-experts step with several tokens
+// per expert; grouped expert handling at prefill: colibri docs "CUDA
+// backend (Linux)", section "The GPU-resident pipeline").
+#pragma once
+#include "wq_internal.h"
+
+namespace wq {
+
+// One tensor of a grouped few-rows launch; blocks [block_end of the previous
+// entry, block_end) work on it (16 * nb output rows each).
+struct SkinnyGroupDesc {
+    const uint8_t *w;
+    const float *scales;
+    const float *x;
+    float *y;
+    int stride, nfull, O, I, S, nchunks, chunks_per_wave, block_end;
+};
+
+constexpr int kSkinnyGroupMax = 32;  // tensors per launch (2 KiB of kernel arguments)
+
+struct SkinnyGroupArgs {
+    int n;
+    SkinnyGroupDesc t[kSkinnyGroupMax];
+};
+
+struct SkinnyGroupPlan {
+    bool ok = false;
+    int m = 0, rpl = 0, nb = 0;  // tile for the largest S of the launch
+    int grid = 0;
+};
+
+// Plan for n tensors (S[i] >= 1) of one format on 8-wave blocks; fills each
+// descriptor's nchunks, chunks_per_wave and block_end (the caller fills the
+// pointers, shape and S). Not ok when a tensor cannot take the few-rows
+// kernel (S > 16, I % 4 != 0, 32-bit offsets).
+SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus);
+hipError_t launch_skinny_group(int fmt, const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hipStream_t st);
+
+} // namespace wq

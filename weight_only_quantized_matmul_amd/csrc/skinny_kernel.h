@@ -183,8 +183,9 @@ template <int FMT> __device__ __forceinline__ int chunk_group(int c, int gs, int
 // NB: 16-row output blocks per wave (and block); WAVES: waves per block,
 // each streaming its own chunks; R: chunks of loads in flight (even);
 // NBUF: operand buffers per wave (1 or 2); GS: group-wise scales.
-template <int FMT, int M, int RPL, int NB, int WAVES, int R, int NBUF, bool GS = false>
-__global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
+// The work of one block: output rows [16 NB blk, 16 NB (blk + 1)) of a.
+template <int FMT, int M, int RPL, int NB, int WAVES, int R, int NBUF, bool GS>
+__device__ __forceinline__ void skinny_block(const SkinnyArgs &a, int blk) {
     static_assert(R % 2 == 0, "the load ring advances by chunk pairs");
     static_assert(NBUF == 1 || NBUF == 2, "one or two operand buffers");
     constexpr int L2 = SkF<FMT>::LOADS2;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     const int lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
     const int S = a.S, O = a.O, I = a.I;
-    const int o0 = blockIdx.x * (16 * NB);
+    const int o0 = blk * (16 * NB);
     const int stride = (int)a.stride;
     // chunk pairs are dealt to the waves in turn (pair k of this wave is
     // pair wave + WAVES k of the row), so at any time the block's waves read
@@ -458,6 +459,11 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
     }
 }
 
+template <int FMT, int M, int RPL, int NB, int WAVES, int R, int NBUF, bool GS = false>
+__global__ __launch_bounds__(64 * WAVES) void skinny_kernel(SkinnyArgs a) {
+    skinny_block<FMT, M, RPL, NB, WAVES, R, NBUF, GS>(a, blockIdx.x);
+}
+
 // LDS of a block: the waves' operand buffers (nbuf each), reused for the
 // partial tiles.
 constexpr int skinny_lds_bytes(int m, int nb, int waves, int nbuf) {
@@ -497,6 +503,25 @@ hipError_t launch_wide(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st)
 }
 
 } // namespace
+
+// Deepest ring (chunks of loads in flight per wave) whose kernel keeps every
+// value in registers (no spills at two waves per SIMD), from the compiled
+// register counts: the ring holds a chunk pair's weights (LOADS2 x NB
+// 16-byte loads) and activation runs (2 x RPL x 32 bytes); 0: not compiled.
+constexpr int skinny_max_ring(int fmt, int m, int rpl, int nb) {
+    // [format][(m, rpl) = (1,1) (1,2) (2,2) (2,3) (3,3) (3,4)][nb - 1]
+    constexpr signed char kRing[3][6][4] = {
+        {{6, 6, 6, 4}, {6, 6, 4, 2}, {6, 4, 2, 2}, {4, 2, 2, 2}, {4, 2, 2, 0}, {4, 2, 0, 0}},   // int8
+        {{6, 6, 6, 6}, {6, 6, 6, 4}, {6, 6, 4, 4}, {6, 4, 2, 2}, {6, 4, 2, 0}, {4, 2, 2, 0}},   // int4
+        {{6, 6, 6, 6}, {6, 6, 6, 6}, {6, 6, 6, 4}, {6, 4, 4, 2}, {6, 4, 2, 0}, {4, 2, 2, 0}}};  // int2
+    const int f = fmt == WQ_I8 ? 0 : fmt == WQ_I4 ? 1 : fmt == WQ_I2 ? 2 : -1;
+    const int mr = m * 10 + rpl;
+    const int k = mr == 11 ? 0 : mr == 12 ? 1 : mr == 22 ? 2 : mr == 23 ? 3 : mr == 33 ? 4 : mr == 34 ? 5 : -1;
+    return f < 0 || k < 0 || nb < 1 || nb > 4 ? 0 : kRing[f][k][nb - 1];
+}
+
+// Tiles with at least the default two chunks of loads in flight.
+constexpr bool skinny_ring_ok(int fmt, int m, int rpl, int nb) { return skinny_max_ring(fmt, m, rpl, nb) >= 2; }
 
 hipError_t launch_skinny_wide_i8(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);
 hipError_t launch_skinny_wide_i4(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);

@@ -5,22 +5,6 @@
 
 namespace wq {
 
-// Deepest ring (chunks of loads in flight per wave) whose kernel keeps every
-// value in registers (no spills at two waves per SIMD), from the compiled
-// register counts: the ring holds a chunk pair's weights (LOADS2 x NB
-// 16-byte loads) and activation runs (2 x RPL x 32 bytes); 0: not compiled.
-constexpr int skinny_max_ring(int fmt, int m, int rpl, int nb) {
-    // [format][(m, rpl) = (1,1) (1,2) (2,2) (2,3) (3,3) (3,4)][nb - 1]
-    constexpr signed char kRing[3][6][4] = {
-        {{6, 6, 6, 4}, {6, 6, 4, 2}, {6, 4, 2, 2}, {4, 2, 2, 2}, {4, 2, 2, 0}, {4, 2, 0, 0}},   // int8
-        {{6, 6, 6, 6}, {6, 6, 6, 4}, {6, 6, 4, 4}, {6, 4, 2, 2}, {6, 4, 2, 0}, {4, 2, 2, 0}},   // int4
-        {{6, 6, 6, 6}, {6, 6, 6, 6}, {6, 6, 6, 4}, {6, 4, 4, 2}, {6, 4, 2, 0}, {4, 2, 2, 0}}};  // int2
-    const int f = fmt == WQ_I8 ? 0 : fmt == WQ_I4 ? 1 : fmt == WQ_I2 ? 2 : -1;
-    const int mr = m * 10 + rpl;
-    const int k = mr == 11 ? 0 : mr == 12 ? 1 : mr == 22 ? 2 : mr == 23 ? 3 : mr == 33 ? 4 : mr == 34 ? 5 : -1;
-    return f < 0 || k < 0 || nb < 1 || nb > 4 ? 0 : kRing[f][k][nb - 1];
-}
-
 // Group-scaled tiles (fresh accumulators per chunk beside the running ones)
 // that keep every value in registers with two chunks in flight (from the
 // compiled register counts): 8-wave blocks at two waves per SIMD, and for
