@@ -221,9 +221,13 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
  * hip_stream whatever their shapes (e.g. the gate, up and down projections
  * of 8 experts: 24 tensors with 3 KiB and 1 KiB rows), the work cut into
  * pieces of equal weight bytes when the group is created; more tensors take
- * one launch per 64. Otherwise one wq_matmul_dev per tensor, still
- * stream-ordered (the tiled ones share the stream's workspace, in stream
- * order).
+ * one launch per 64. Otherwise, when every S[g] <= 16, no tensor has
+ * group-wise scales, every x_dev[g] is 16-byte aligned and every I % 4 == 0,
+ * the tensors run on the few-rows matrix-core kernel, one launch per 32
+ * tensors with S[g] > 0 (blocks of 16 to 64 output rows of one tensor each;
+ * the tile is that of the largest S[g]). Otherwise one wq_matmul_dev per
+ * tensor, still stream-ordered (the tiled ones share the stream's
+ * workspace, in stream order).
  */
 int wq_grouped_matmul_dev(wq_group *group, const float *const *x_dev, const int *S,
                           float *const *y_dev, void *hip_stream);
