@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="dense_gemv",
-                    choices=["dense_gemv", "moe_decode", "moe_decode_s8", "moe_ffn", "moe_ffn_pipeline", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
+                    choices=["dense_gemv", "moe_decode", "moe_decode_s8", "moe_ffn", "moe_ffn_s8", "moe_ffn_pipeline", "int2_gemv_s1", "int2_gemv_s4", "int2_gemv_s8",
                              "int2_gemv_s2", "int2_gemv_s16", "dense_gemv_s2", "dense_gemv_s4", "dense_gemv_s8",
                              "dense_gemv_s16", "dense_gemv_gs128", "dense_gemv_s8_gs128", "prefill_gs128",
                              "prefill"])
@@ -115,6 +115,10 @@ def problems_for(name):
     if name == "moe_decode":
         return synth.moe_decode(), ("moe_decode: 8 experts x int4 {gate,up}[2048,6144] + down[6144,2048], "
                                     "S=1 per expert, all 24 matmuls in one grouped launch")
+    if name.startswith("moe_ffn_s") and name[len("moe_ffn_s"):].isdigit():
+        S = int(name[len("moe_ffn_s"):])
+        return synth.moe_decode(S=S), ("moe_ffn: 8 experts x int4 {gate,up}[2048,6144] -> h = silu(g)*u -> "
+                                       "down[6144,2048], S=%d per expert" % S)
     if name in ("moe_ffn", "moe_ffn_pipeline"):
         return synth.moe_decode(), ("moe_ffn: 8 experts x int4 {gate,up}[2048,6144] -> h = silu(g)*u -> "
                                     "down[6144,2048], S=1 per expert, fused gate/up launch + grouped down launch")
@@ -169,7 +173,7 @@ def main():
     torch.cuda.set_device(dev)
     K, W = args.steps, args.warmup
     grouped = args.workload == "moe_decode" or args.workload.startswith("moe_decode_s")
-    ffn = args.workload in ("moe_ffn", "moe_ffn_pipeline")
+    ffn = args.workload in ("moe_ffn", "moe_ffn_pipeline") or args.workload.startswith("moe_ffn_s")
     weight_bytes = sum(p.weight_bytes for p in probs)
 
     def io_bytes(p):  # weights, scales, activations in, results out

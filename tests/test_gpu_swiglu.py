@@ -195,6 +195,31 @@ def test_swiglu_moe_decode_shape_batched():
     run_chain(experts, what="moe-batched")
 
 
+@pytest.mark.parametrize("E,S,launches", [(8, 8, 2), (20, 5, 3)])
+def test_swiglu_few_rows_grouped_launches(E, S, launches):
+    """2..16 rows per expert: gate and up of up to 16 experts per few-rows
+    launch, then one activation launch per 32 experts."""
+    experts = [Expert(I4, 2048 if E == 8 else 130 + 7 * k, 6144 if E == 8 else 1000, S, seed=9800 + E + k,
+                      down_O=256) for k in range(E)]
+    ts = [e.upload() for e in experts]
+    grp = wq.wq_swiglu_create([t[0] for t in ts], [t[1] for t in ts])
+    try:
+        xs = [dev(e.x) for e in experts]
+        hs = [torch.empty((S, e.O), dtype=torch.float32, device="cuda:%d" % gu.DEV) for e in experts]
+        gu.banner("swiglu grouped few rows E=%d S=%d" % (E, S))
+        wq.wq_swiglu_matmul_dev(grp, xs, hs)  # eager first: the workspace then holds every u
+        torch.cuda.synchronize()
+        for i, e in enumerate(experts):
+            assert_h(hs[i].cpu().numpy(), e.reference(), "expert %d h" % i)
+        gu.banner("swiglu grouped few rows E=%d S=%d: launch count" % (E, S))
+        assert gu.count_kernel_launches(lambda: wq.wq_swiglu_matmul_dev(grp, xs, hs)) == launches
+    finally:
+        wq.wq_grouped_free(grp)
+        for t in ts:
+            for x in t:
+                wq.wq_tensor_free(x)
+
+
 def test_swiglu_exact_zero_rows():
     # gate codes that all decode to 0 give g = 0 exactly, so h = 0; up codes
     # that decode to 0 give u = 0 and h = 0; a zero h gives y = 0 exactly

@@ -48,6 +48,7 @@
 //    (SiLU gating: the reading taken for the gated up-projection shader that
 //    colibri "第 8 章 · 02 CUDA/Metal/Vulkan 三后端" names in its learning
 //    goals and section recap without giving its activation).
+#include "skinny_group.h"
 #include "wq_internal.h"
 
 
@@ -761,6 +762,14 @@ __global__ void relayout_kernel(const uint8_t *__restrict__ src, uint8_t *__rest
     }
 }
 
+// The same for expert blockIdx.y of a launch over several experts.
+__global__ void gated_group_kernel(GatedGroupArgs a) {
+    float *h = a.e[blockIdx.y].h;
+    const float *u = a.e[blockIdx.y].u;
+    const int n = a.e[blockIdx.y].count;
+    for (int j = blockIdx.x * 256 + threadIdx.x; j < n; j += gridDim.x * 256) h[j] = gated(h[j], u[j]);
+}
+
 // h[j] = gated(h[j], u[j]): the activation step of the gated feed-forward
 // when gate and up ran as separate matmuls (h holds g on entry).
 __global__ void gated_inplace_kernel(float *__restrict__ h, const float *__restrict__ u, long n) {
@@ -769,6 +778,13 @@ __global__ void gated_inplace_kernel(float *__restrict__ h, const float *__restr
 }
 
 } // namespace
+
+hipError_t launch_gated_group(const GatedGroupArgs &a, int max_count, hipStream_t st) {
+    if (a.n <= 0 || max_count <= 0) return hipSuccess;
+    const dim3 grid((unsigned)std::min((max_count + 255) / 256, 64), (unsigned)a.n);
+    hipLaunchKernelGGL(gated_group_kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_gated_inplace(float *h, const float *u, long n, hipStream_t st) {
     if (n <= 0) return hipSuccess;

@@ -900,6 +900,76 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
             return WQ_OK;
         }
     }
+    if (!one_launch && pair && !g->has_gs && g_cfg.force_path == 0) {
+        // 2..16 rows per expert, gated: gate -> h and up -> u (in the
+        // stream's workspace) of every expert in grouped few-rows launches,
+        // then one activation launch per kSkinnyGroupMax experts
+        std::vector<int> act;
+        bool ok = true;
+        size_t ubytes = 0;
+        std::vector<size_t> uoff(g->G, 0);
+        for (int i = 0; i < g->G; ++i) {
+            if (S[i] == 0) continue;
+            if (((uintptr_t)x_dev[i] & 15) != 0 || g->ts[i]->stride >= INT_MAX || S[i] > 16) ok = false;
+            act.push_back(i);
+            uoff[i] = ubytes;
+            ubytes += (size_t)wq::round_up((long)S[i] * g->ts[i]->O * (long)sizeof(float), 256);
+        }
+        std::vector<wq::SkinnyGroupArgs> launches;
+        std::vector<wq::SkinnyGroupPlan> plans;
+        const int per = wq::kSkinnyGroupMax / 2;  // experts per launch (two tensors each)
+        for (size_t c = 0; c < act.size() && ok; c += per) {
+            wq::SkinnyGroupArgs a;
+            memset(&a, 0, sizeof a);
+            for (size_t j = c; j < std::min(act.size(), c + per); ++j) {
+                const int i = act[j];
+                for (int h = 0; h < 2; ++h) {
+                    const wq_tensor *t = h ? g->ts2[i] : g->ts[i];
+                    wq::SkinnyGroupDesc &e = a.t[a.n++];
+                    e.w = t->d_w;
+                    e.scales = t->d_scales;
+                    e.x = x_dev[i];
+                    e.y = y_dev[i];  // up: set once the workspace is known
+                    e.stride = (int)t->stride;
+                    e.nfull = t->nfull;
+                    e.O = t->O;
+                    e.I = t->I;
+                    e.S = S[i];
+                }
+            }
+            plans.push_back(wq::plan_skinny_group(g->fmt, a.t, a.n, g_dev[g->device].cus));
+            ok = plans.back().ok;
+            launches.push_back(a);
+        }
+        if (ok && !act.empty()) {
+            uint16_t *ws = nullptr;
+            int rc = ensure_workspace(g_dev[g->device], ubytes, st, &ws);
+            if (rc != WQ_OK) return rc;
+            char *ub = reinterpret_cast<char *>(ws);
+            for (size_t c = 0; c < launches.size(); ++c) {
+                for (int k = 1; k < launches[c].n; k += 2)
+                    launches[c].t[k].y = reinterpret_cast<float *>(ub + uoff[act[c * per + k / 2]]);
+                rc = hip_status(wq::launch_skinny_group(g->fmt, plans[c], launches[c], st));
+                if (rc != WQ_OK) return rc;
+            }
+            for (size_t c = 0; c < act.size(); c += wq::kSkinnyGroupMax) {
+                wq::GatedGroupArgs ga;
+                memset(&ga, 0, sizeof ga);
+                int maxc = 0;
+                for (size_t j = c; j < std::min(act.size(), c + wq::kSkinnyGroupMax); ++j) {
+                    const int i = act[j];
+                    auto &e = ga.e[ga.n++];
+                    e.h = y_dev[i];
+                    e.u = reinterpret_cast<const float *>(ub + uoff[i]);
+                    e.count = S[i] * g->ts[i]->O;
+                    maxc = std::max(maxc, e.count);
+                }
+                rc = hip_status(wq::launch_gated_group(ga, maxc, st));
+                if (rc != WQ_OK) return rc;
+            }
+            return WQ_OK;
+        }
+    }
     if (!one_launch) {
         for (int i = 0; i < g->G; ++i) {
             if (S[i] == 0) continue;

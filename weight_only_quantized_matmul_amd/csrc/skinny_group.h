@@ -38,4 +38,17 @@ struct SkinnyGroupPlan {
 SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus);
 hipError_t launch_skinny_group(int fmt, const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hipStream_t st);
 
+// The activation step of several experts' gated feed-forward in one launch:
+// h_e[j] = silu(h_e[j]) * u_e[j] for j < count_e (h_e holds the gate
+// product on entry, u_e the up product).
+struct GatedGroupArgs {
+    int n;
+    struct {
+        float *h;
+        const float *u;
+        int count;
+    } e[kSkinnyGroupMax];
+};
+hipError_t launch_gated_group(const GatedGroupArgs &a, int max_count, hipStream_t st);
+
 } // namespace wq
