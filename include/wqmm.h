@@ -256,11 +256,15 @@ int wq_grouped_free(wq_group *group);
  * skips expert e). Stream-ordered on hip_stream. With every S[e] within the
  * grouped GEMV limit, one scale per row and rows that fit one wave, all experts run
  * in one launch that reads each gate row and up row once and writes h
- * directly (g and u never reach memory); otherwise each expert runs as its
- * own paired launch, or (S above that limit, or group-wise scales) as
- * gate -> h_dev[e], up -> the stream's workspace, then an activation kernel.
- * The last form may grow the workspace (not while the stream is being
- * captured: see wq_matmul_dev; warm up first).
+ * directly (g and u never reach memory); otherwise, with every S[e] <= 16,
+ * one scale per row, x 16-byte aligned and I % 4 == 0, the gate and up
+ * matmuls of up to 16 experts run per launch of the few-rows matrix-core
+ * kernel (gate -> h_dev[e], up -> the stream's workspace), then one
+ * activation launch per 32 experts; otherwise each expert runs as its own
+ * paired launch, or (S above the grouped GEMV limit, or group-wise scales)
+ * as gate -> h_dev[e], up -> the stream's workspace, then an activation
+ * kernel. The forms through the workspace may grow it (not while the stream
+ * is being captured: see wq_matmul_dev; warm up first).
  *
  * Accuracy: g and u meet the matmul contract; h is silu and the product
  * evaluated in fp32 on those values (a few ulps, no further cancellation).
