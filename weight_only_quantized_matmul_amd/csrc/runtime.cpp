@@ -18,6 +18,7 @@
 #include <new>
 
 #include "skinny_group.h"
+#include "staging.h"
 #include "wq_internal.h"
 
 namespace {
@@ -43,6 +44,13 @@ struct DeviceCtx {
     size_t x_cap = 0;  // bytes
     float *d_y = nullptr;
     size_t y_cap = 0;  // bytes
+    // pinned host staging of the host-pointer calls, mapped into the
+    // device's address space (dh_*: its device addresses), read and written
+    // by copy kernels on the library stream
+    float *h_x = nullptr, *dh_x = nullptr;
+    size_t hx_cap = 0;  // bytes
+    float *h_y = nullptr, *dh_y = nullptr;
+    size_t hy_cap = 0;  // bytes
     // Tiled workspaces (activation planes, split-K partials, the gated
     // intermediate), one per stream that ran such a call, so calls on
     // different streams may overlap. At most kStreamWorkspaces per device;
@@ -370,7 +378,28 @@ int ensure_scratch(DeviceCtx &d, size_t xb, size_t yb) {
         }
         d.y_cap = yb;
     }
-    return WQ_OK;
+    auto pinned = [](size_t bytes, float **h, float **dh, size_t *cap) {
+        if (bytes <= *cap) return WQ_OK;
+        if (*h) (void)hipHostFree(*h);
+        *h = *dh = nullptr;
+        *cap = 0;
+        if (hipHostMalloc((void **)h, bytes, hipHostMallocMapped) != hipSuccess) {
+            (void)hipGetLastError();
+            *h = nullptr;
+            return WQ_E_OOM;
+        }
+        if (hipHostGetDevicePointer((void **)dh, *h, 0) != hipSuccess || *dh == nullptr) {
+            (void)hipGetLastError();
+            (void)hipHostFree(*h);
+            *h = *dh = nullptr;
+            return WQ_E_HIP;
+        }
+        *cap = bytes;
+        return WQ_OK;
+    };
+    int rc = pinned(xb, &d.h_x, &d.dh_x, &d.hx_cap);
+    if (rc == WQ_OK) rc = pinned(yb, &d.h_y, &d.dh_y, &d.hy_cap);
+    return rc;
 }
 
 } // namespace
@@ -589,7 +618,11 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y) {
     const size_t yb = (size_t)S * t->O * sizeof(float);
     int rc = ensure_scratch(d, xb, yb);
     if (rc != WQ_OK) return rc;
-    hipError_t e = hipMemcpyAsync(d.d_x, x, xb, hipMemcpyHostToDevice, d.stream);
+    // x -> pinned staging -> device by a copy kernel, the matmul, y back the
+    // same way; the previous call finished before it returned, so the
+    // staging buffers are free
+    memcpy(d.h_x, x, xb);
+    hipError_t e = wq::launch_stage_copy(d.dh_x, d.d_x, xb / sizeof(float), d.stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return hip_status(e);
@@ -599,12 +632,13 @@ int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y) {
         (void)hipStreamSynchronize(d.stream);
         return rc;
     }
-    e = hipMemcpyAsync(y, d.d_y, yb, hipMemcpyDeviceToHost, d.stream);
+    e = wq::launch_stage_copy(d.d_y, d.dh_y, yb / sizeof(float), d.stream);
     if (e == hipSuccess) e = hipStreamSynchronize(d.stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return hip_status(e);
     }
+    memcpy(y, d.h_y, yb);  // y is written only on success
     return WQ_OK;
 }
 
