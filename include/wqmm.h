@@ -143,7 +143,11 @@ int wq_tensor_upload_gs(wq_tensor **t, int device, int fmt, int O, int I, int gs
 int wq_matmul(wq_tensor **t, int device, int fmt, int O, int I, const void *w,
               const float *scales, const float *x, int S, float *y);
 
-/* Synchronous matmul with an already-resident tensor; x, y host pointers. */
+/* Synchronous matmul with an already-resident tensor; x, y host pointers.
+ * x and y pass through pinned host buffers mapped into the device's address
+ * space (library-owned, grown to the largest call, held until the process
+ * ends), which kernels on the library stream copy to and from device memory;
+ * y is written only when the call succeeds. */
 int wq_matmul_t(const wq_tensor *t, const float *x, int S, float *y);
 
 /*
