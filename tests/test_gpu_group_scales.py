@@ -190,21 +190,66 @@ def test_group_scales_zero_rows_exact(fmt, zero, S):
     gu.assert_within_bound(y, y_ref, A, "gs zeros")
 
 
-def test_group_scales_in_a_group_call():
-    """Grouped calls holding group-scaled tensors run per tensor, still stream-ordered."""
-    probs = [synth.ragged(I4, 512, 2048, 1, seed=8900 + k) for k in range(3)]
+@pytest.mark.parametrize("S", [1, 2, 8, 16])
+def test_group_scales_in_a_group_call(S):
+    """Grouped calls holding group-scaled tensors: per tensor at S = 1, one
+    few-rows launch for 2..16 rows."""
+    probs = [synth.ragged(I4, 512, 2048, S, seed=8900 + k + S) for k in range(3)]
     scs = [gscales(8950 + k, 512, 2048, 128) for k in range(3)]
     ts = [upload_gs(I4, 512, 2048, 128, p.w, sc) for p, sc in zip(probs, scs)]
     g = wq.wq_grouped_create(ts)
     try:
         xs = [torch.from_numpy(p.x).cuda() for p in probs]
-        ys = [torch.empty((1, 512), device="cuda") for _ in probs]
-        gu.banner("gs grouped call")
+        ys = [torch.empty((S, 512), device="cuda") for _ in probs]
+        if S > 1:
+            wq.wq_grouped_matmul_dev(g, xs, ys)
+            torch.cuda.synchronize()
+            gu.banner("gs grouped call S=%d: launch count" % S)
+            assert gu.count_kernel_launches(lambda: wq.wq_grouped_matmul_dev(g, xs, ys)) == 1
+        gu.banner("gs grouped call S=%d" % S)
         wq.wq_grouped_matmul_dev(g, xs, ys)
         torch.cuda.synchronize()
         for p, sc, y in zip(probs, scs, ys):
             y_ref, A = oracle.matmul_gs(I4, p.w, sc, 128, p.x)
             gu.assert_within_bound(y.cpu().numpy(), y_ref, A, "gs grouped")
+    finally:
+        wq.wq_grouped_free(g)
+        for t in ts:
+            wq.wq_tensor_free(t)
+
+
+@pytest.mark.parametrize("fmt,gs", [(I8, 256), (I4, 128), (I2, 256)])
+def test_group_scales_mixed_group_few_rows(fmt, gs):
+    """A group mixing group-scaled tensors (gs) and tensors with one scale per
+    row, 2..16 rows each, some skipped: one group-scaled few-rows launch (a
+    row-scaled tensor is one group as long as its row)."""
+    g0 = synth.rng(8960 + fmt)
+    probs, scs, Ss = [], [], []
+    for k in range(7):
+        O, I = int(g0.integers(20, 600)), 4 * int(g0.integers(40, 700))
+        S = [3, 0, 16, 8, 2, 5, 11][k]
+        p = synth.ragged(fmt, O, I, max(S, 1), seed=8970 + k + fmt)
+        probs.append(p)
+        scs.append(gscales(8990 + k, O, I, gs) if k % 2 == 0 else None)
+        Ss.append(S)
+    ts = [upload_gs(fmt, p.O, p.I, gs, p.w, sc) if sc is not None else gu.upload(p) for p, sc in zip(probs, scs)]
+    g = wq.wq_grouped_create(ts)
+    try:
+        xs = [torch.from_numpy(p.x[:S]).cuda() if S else None for p, S in zip(probs, Ss)]
+        ys = [torch.empty((S, p.O), device="cuda") if S else None for p, S in zip(probs, Ss)]
+        gu.banner("gs mixed group few rows fmt=%d: launch count" % fmt)
+        assert gu.count_kernel_launches(lambda: wq.wq_grouped_matmul_dev(g, xs, ys)) == 1
+        gu.banner("gs mixed group few rows fmt=%d" % fmt)
+        wq.wq_grouped_matmul_dev(g, xs, ys)
+        torch.cuda.synchronize()
+        for p, sc, S, y in zip(probs, scs, Ss, ys):
+            if S == 0:
+                continue
+            if sc is None:
+                y_ref, A = oracle.matmul(fmt, p.w, p.scales, p.x[:S])
+            else:
+                y_ref, A = oracle.matmul_gs(fmt, p.w, sc, gs, p.x[:S])
+            gu.assert_within_bound(y.cpu().numpy(), y_ref, A, "gs mixed group")
     finally:
         wq.wq_grouped_free(g)
         for t in ts:

@@ -873,6 +873,14 @@ int run_swiglu(const wq_tensor *gt, const wq_tensor *ut, const float *x, int S, 
     return rc;
 }
 
+// The group-scale fields of a grouped few-rows descriptor: a tensor with one
+// scale per row is one group as long as the row.
+void set_group_scales(wq::SkinnyGroupDesc &e, const wq_tensor *t) {
+    e.gscales_t = t->gs > 0 ? t->d_scales_t : t->d_scales;
+    e.gs = t->gs > 0 ? t->gs : (1 << 30);
+    e.ng = t->gs > 0 ? t->ng : 1;
+}
+
 // Shared by the plain and the paired group calls (checked by the callers).
 int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const *y_dev, hipStream_t st) {
     const bool pair = !g->ts2.empty();
@@ -894,7 +902,7 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
     const int bi = bucket == 1 ? 0 : bucket == 2 ? 1 : bucket == 4 ? 2 : bucket == 8 ? 3 : -1;
     const bool one_launch = !g->has_gs && g_cfg.force_path != 2 && g_cfg.force_path != 3 &&
                             smax <= group_gemv_limit(g->fmt) && bi >= 0 && g->buckets[bi].plan.ok;
-    if (!one_launch && !pair && !g->has_gs && g_cfg.force_path == 0) {
+    if (!one_launch && !pair && g_cfg.force_path == 0) {
         // 2..16 rows per tensor: the few-rows kernel over the whole group,
         // one launch per kSkinnyGroupMax active tensors
         wq::SkinnyGroupArgs a;
@@ -916,6 +924,7 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
             e.O = t->O;
             e.I = t->I;
             e.S = S[i];
+            set_group_scales(e, t);
             if (a.n == wq::kSkinnyGroupMax) {
                 launches.push_back(a);
                 memset(&a, 0, sizeof a);
@@ -923,7 +932,8 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
         }
         if (a.n > 0) launches.push_back(a);
         for (size_t c = 0; c < launches.size() && ok; ++c) {
-            plans.push_back(wq::plan_skinny_group(g->fmt, launches[c].t, launches[c].n, g_dev[g->device].cus));
+            plans.push_back(
+                wq::plan_skinny_group(g->fmt, launches[c].t, launches[c].n, g_dev[g->device].cus, g->has_gs));
             ok = plans.back().ok;
         }
         if (ok) {
@@ -934,7 +944,7 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
             return WQ_OK;
         }
     }
-    if (!one_launch && pair && !g->has_gs && g_cfg.force_path == 0) {
+    if (!one_launch && pair && g_cfg.force_path == 0) {
         // 2..16 rows per expert, gated: gate -> h and up -> u (in the
         // stream's workspace) of every expert in grouped few-rows launches,
         // then one activation launch per kSkinnyGroupMax experts
@@ -969,9 +979,10 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
                     e.O = t->O;
                     e.I = t->I;
                     e.S = S[i];
+                    set_group_scales(e, t);
                 }
             }
-            plans.push_back(wq::plan_skinny_group(g->fmt, a.t, a.n, g_dev[g->device].cus));
+            plans.push_back(wq::plan_skinny_group(g->fmt, a.t, a.n, g_dev[g->device].cus, g->has_gs));
             ok = plans.back().ok;
             launches.push_back(a);
         }

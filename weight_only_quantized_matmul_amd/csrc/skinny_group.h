@@ -16,6 +16,11 @@ struct SkinnyGroupDesc {
     const float *x;
     float *y;
     int stride, nfull, O, I, S, nchunks, chunks_per_wave, block_end;
+    // launches with group-wise scales: ng x O group-major scales and the
+    // group size (a tensor with one scale per row: its scales, gs = 1 << 30,
+    // ng = 1)
+    const float *gscales_t;
+    int gs, ng;
 };
 
 constexpr int kSkinnyGroupMax = 32;  // tensors per launch (2 KiB of kernel arguments)
@@ -28,14 +33,16 @@ struct SkinnyGroupArgs {
 struct SkinnyGroupPlan {
     bool ok = false;
     int m = 0, rpl = 0, nb = 0;  // tile for the largest S of the launch
+    bool gs = false;             // the group-scaled kernel (per-chunk accumulators)
     int grid = 0;
 };
 
 // Plan for n tensors (S[i] >= 1) of one format on 8-wave blocks; fills each
 // descriptor's nchunks, chunks_per_wave and block_end (the caller fills the
-// pointers, shape and S). Not ok when a tensor cannot take the few-rows
-// kernel (S > 16, I % 4 != 0, 32-bit offsets).
-SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus);
+// pointers, shape, S and, with gs, the group fields). Not ok when a tensor
+// cannot take the few-rows kernel (S > 16, I % 4 != 0, 32-bit offsets, a
+// group size that is not a multiple of a chunk's span).
+SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus, bool gs = false);
 hipError_t launch_skinny_group(int fmt, const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hipStream_t st);
 
 // The activation step of several experts' gated feed-forward in one launch:

@@ -13,7 +13,7 @@ namespace wq {
 
 namespace {
 
-template <int FMT, int M, int RPL, int NB>
+template <int FMT, int M, int RPL, int NB, bool GS>
 __global__ __launch_bounds__(512) void skinny_group_kernel(SkinnyGroupArgs ga) {
     // the block's tensor (wave-uniform scan of at most kSkinnyGroupMax entries)
     const int b = blockIdx.x;
@@ -32,18 +32,28 @@ __global__ __launch_bounds__(512) void skinny_group_kernel(SkinnyGroupArgs ga) {
     a.S = d.S;
     a.chunks_per_wave = d.chunks_per_wave;
     a.nchunks = d.nchunks;
-    skinny_block<FMT, M, RPL, NB, 8, 2, skinny_nbuf(M, NB, 8), false>(a, b - (t > 0 ? ga.t[t - 1].block_end : 0));
+    a.gscales_t = d.gscales_t;
+    a.gs = d.gs;
+    a.ng = d.ng;
+    skinny_block<FMT, M, RPL, NB, 8, 2, skinny_nbuf(M, NB, 8), GS>(a, b - (t > 0 ? ga.t[t - 1].block_end : 0));
 }
 
 template <int FMT, int M, int RPL>
 hipError_t launch_group_mr(const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hipStream_t st) {
-#define WQ_SKGR(NB_)                                                                                   \
-    if constexpr (skinny_ring_ok(FMT, M, RPL, NB_)) {                                                  \
-        if (p.nb == NB_) {                                                                             \
-            hipLaunchKernelGGL((skinny_group_kernel<FMT, M, RPL, NB_>), dim3(p.grid), dim3(512), 0, st, \
-                               a);                                                                     \
-            return hipGetLastError();                                                                  \
-        }                                                                                              \
+#define WQ_SKGR(NB_)                                                                                          \
+    if constexpr (skinny_ring_ok(FMT, M, RPL, NB_)) {                                                         \
+        if (p.nb == NB_ && !p.gs) {                                                                           \
+            hipLaunchKernelGGL((skinny_group_kernel<FMT, M, RPL, NB_, false>), dim3(p.grid), dim3(512), 0, st, \
+                               a);                                                                            \
+            return hipGetLastError();                                                                         \
+        }                                                                                                     \
+    }                                                                                                         \
+    if constexpr (skinny_ring_ok(FMT, M, RPL, NB_) && skinny_gs_ok(FMT, M, RPL, NB_, 8)) {                    \
+        if (p.nb == NB_ && p.gs) {                                                                            \
+            hipLaunchKernelGGL((skinny_group_kernel<FMT, M, RPL, NB_, true>), dim3(p.grid), dim3(512), 0, st,  \
+                               a);                                                                            \
+            return hipGetLastError();                                                                         \
+        }                                                                                                     \
     }
     WQ_SKGR(1) WQ_SKGR(2) WQ_SKGR(3) WQ_SKGR(4)
 #undef WQ_SKGR
@@ -65,14 +75,18 @@ hipError_t launch_group_f(const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hi
 
 } // namespace
 
-SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus) {
+SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus, bool gs) {
     SkinnyGroupPlan p;
     if ((fmt != WQ_I8 && fmt != WQ_I4 && fmt != WQ_I2) || n < 1 || n > kSkinnyGroupMax) return p;
+    p.gs = gs;
     int smax = 0;
     for (int i = 0; i < n; ++i) {
         const SkinnyGroupDesc &d = t[i];
         if (d.S < 1 || d.S > 16 || d.O <= 0 || d.I < 4 || d.I % 4 != 0) return p;
         if ((long)d.O * d.stride >= (1L << 31) || (long)d.S * d.I >= (1L << 29)) return p;
+        if (gs && (d.gscales_t == nullptr || d.gs <= 0 || d.ng < 1 || d.gs % (fmt == WQ_I2 ? 2 * kChunk : kChunk) != 0 ||
+                   (long)d.O * d.ng >= (1L << 31)))
+            return p;
         smax = std::max(smax, d.S);
     }
     p.m = smax <= 5 ? 1 : smax <= 10 ? 2 : 3;
@@ -81,7 +95,7 @@ SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus) {
     // against bigger blocks (each loads all of its tensor's x), as for one tensor
     long best = -1;
     for (int nb = 1; nb <= 4; ++nb) {
-        if (!skinny_ring_ok(fmt, p.m, p.rpl, nb)) continue;
+        if (!skinny_ring_ok(fmt, p.m, p.rpl, nb) || (gs && !skinny_gs_ok(fmt, p.m, p.rpl, nb, 8))) continue;
         long blocks = 0;
         for (int i = 0; i < n; ++i) blocks += ((long)t[i].O + 16 * nb - 1) / (16 * nb);
         const long cost = (blocks + cus - 1) / cus * (1 + nb);

@@ -523,6 +523,20 @@ constexpr int skinny_max_ring(int fmt, int m, int rpl, int nb) {
 // Tiles with at least the default two chunks of loads in flight.
 constexpr bool skinny_ring_ok(int fmt, int m, int rpl, int nb) { return skinny_max_ring(fmt, m, rpl, nb) >= 2; }
 
+// Group-scaled tiles (fresh accumulators per chunk beside the running ones)
+// that keep every value in registers with two chunks in flight (from the
+// compiled register counts): 8-wave blocks at two waves per SIMD, and for
+// three stacked fragments (11 <= S <= 16) also 4-wave blocks at one wave per
+// SIMD, whose larger register file holds three or four output blocks.
+constexpr bool skinny_gs_ok(int fmt, int m, int rpl, int nb, int waves) {
+    if (fmt < WQ_I8 || fmt > WQ_I2 || m < 1 || m > 3 || rpl < 1 || rpl > 4 || nb < 1 || nb > 4) return false;
+    if (waves == 4) return m == 3 && nb >= 3;
+    if (waves != 8) return false;
+    if (m * nb <= 6) return true;
+    const int k = m * 100 + rpl * 10 + nb;
+    return k == 224 || k == 333 || (k == 234 && fmt != WQ_I8) || (k == 343 && fmt == WQ_I2);
+}
+
 hipError_t launch_skinny_wide_i8(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);
 hipError_t launch_skinny_wide_i4(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);
 hipError_t launch_skinny_wide_i2(const SkinnyPlan &p, const SkinnyArgs &a, hipStream_t st);
