@@ -128,7 +128,8 @@ int wq_tensor_upload(wq_tensor **t, int device, int fmt, int O, int I, const voi
  * Formats int8/int4/int2 only (WQ_E_INVAL for WQ_F32 or gs <= 0). Otherwise
  * as wq_tensor_upload; a re-upload also checks gs (WQ_E_MISMATCH). The
  * tensor then works with every matmul call; groups containing such tensors
- * run one launch per tensor.
+ * take the grouped few-rows launch (below) when its conditions hold, else
+ * one launch per tensor.
  */
 int wq_tensor_upload_gs(wq_tensor **t, int device, int fmt, int O, int I, int gs, const void *w,
                         const float *scales);
@@ -225,11 +226,14 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
  * hip_stream whatever their shapes (e.g. the gate, up and down projections
  * of 8 experts: 24 tensors with 3 KiB and 1 KiB rows), the work cut into
  * pieces of equal weight bytes when the group is created; more tensors take
- * one launch per 64. Otherwise, when every S[g] <= 16, no tensor has
- * group-wise scales, every x_dev[g] is 16-byte aligned and every I % 4 == 0,
- * the tensors run on the few-rows matrix-core kernel, one launch per 32
- * tensors with S[g] > 0 (blocks of 16 to 64 output rows of one tensor each;
- * the tile is that of the largest S[g]). Otherwise one wq_matmul_dev per
+ * one launch per 64 (none of this with group-wise scales). Otherwise, when
+ * every S[g] <= 16, every x_dev[g] is 16-byte aligned, every I % 4 == 0 and
+ * every group size is a multiple of 128 (int8, int4) or 256 (int2), the
+ * tensors run on the few-rows matrix-core kernel, one launch per 32 tensors
+ * with S[g] > 0 (blocks of 16 to 64 output rows of one tensor each; the
+ * tile is that of the largest S[g]; with any group-scaled tensor the
+ * group-scaled kernel, where a row-scaled tensor is one group as long as
+ * its row). Otherwise one wq_matmul_dev per
  * tensor, still stream-ordered (the tiled ones share the stream's
  * workspace, in stream order).
  */
@@ -260,8 +264,8 @@ int wq_grouped_free(wq_group *group);
  * skips expert e). Stream-ordered on hip_stream. With every S[e] within the
  * grouped GEMV limit, one scale per row and rows that fit one wave, all experts run
  * in one launch that reads each gate row and up row once and writes h
- * directly (g and u never reach memory); otherwise, with every S[e] <= 16,
- * one scale per row, x 16-byte aligned and I % 4 == 0, the gate and up
+ * directly (g and u never reach memory); otherwise, on the conditions of
+ * the grouped few-rows launch (see wq_grouped_matmul_dev), the gate and up
  * matmuls of up to 16 experts run per launch of the few-rows matrix-core
  * kernel (gate -> h_dev[e], up -> the stream's workspace), then one
  * activation launch per 32 experts; otherwise each expert runs as its own
