@@ -176,7 +176,7 @@ def test_grouped_mixed_S_and_skips():
             wq.wq_tensor_free(t)
 
 
-@pytest.mark.parametrize("S", [5, 8, 16])
+@pytest.mark.parametrize("S", [5, 8, 16, 20, 32])
 def test_grouped_few_rows_one_launch(S):
     """Several tokens per expert (above the grouped GEMV's rows): all 24
     matmuls of the 8-expert step in one launch of the few-rows kernel."""
@@ -213,7 +213,8 @@ def test_grouped_few_rows_ragged_and_chunked(fmt):
         O = int(g0.integers(1, 700))
         I = 4 * int(g0.integers(1, 900))
         S = int(g0.choice([0, 1, 2, 5, 9, 13, 16]))
-        S = 16 if i == 3 else S  # the launch tile is the largest S
+        S = 16 if i == 3 else S  # the launch tile is the largest S (24: four-wave blocks)
+        S = 24 if (i == 5 and fmt == I8) else S
         p = synth.ragged(fmt, O, I, max(S, 1), seed=4500 + 7 * i + fmt)
         probs.append(p)
         Ss.append(S)

@@ -195,7 +195,7 @@ def test_swiglu_moe_decode_shape_batched():
     run_chain(experts, what="moe-batched")
 
 
-@pytest.mark.parametrize("E,S,launches", [(8, 8, 2), (20, 5, 3)])
+@pytest.mark.parametrize("E,S,launches", [(8, 8, 2), (20, 5, 3), (8, 24, 2)])
 def test_swiglu_few_rows_grouped_launches(E, S, launches):
     """2..16 rows per expert: gate and up of up to 16 experts per few-rows
     launch, then one activation launch per 32 experts."""

@@ -903,8 +903,9 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
     const bool one_launch = !g->has_gs && g_cfg.force_path != 2 && g_cfg.force_path != 3 &&
                             smax <= group_gemv_limit(g->fmt) && bi >= 0 && g->buckets[bi].plan.ok;
     if (!one_launch && !pair && g_cfg.force_path == 0) {
-        // 2..16 rows per tensor: the few-rows kernel over the whole group,
-        // one launch per kSkinnyGroupMax active tensors
+        // up to 32 rows per tensor (16 with group scales): the few-rows
+        // kernel over the whole group, one launch per kSkinnyGroupMax active
+        // tensors
         wq::SkinnyGroupArgs a;
         memset(&a, 0, sizeof a);
         std::vector<wq::SkinnyGroupArgs> launches;
@@ -945,7 +946,7 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
         }
     }
     if (!one_launch && pair && g_cfg.force_path == 0) {
-        // 2..16 rows per expert, gated: gate -> h and up -> u (in the
+        // up to 32 rows per expert, gated: gate -> h and up -> u (in the
         // stream's workspace) of every expert in grouped few-rows launches,
         // then one activation launch per kSkinnyGroupMax experts
         std::vector<int> act;
@@ -954,7 +955,7 @@ int run_group(wq_group *g, const float *const *x_dev, const int *S, float *const
         std::vector<size_t> uoff(g->G, 0);
         for (int i = 0; i < g->G; ++i) {
             if (S[i] == 0) continue;
-            if (((uintptr_t)x_dev[i] & 15) != 0 || g->ts[i]->stride >= INT_MAX || S[i] > 16) ok = false;
+            if (((uintptr_t)x_dev[i] & 15) != 0 || g->ts[i]->stride >= INT_MAX || S[i] > wq::kSkinnyMaxS) ok = false;
             act.push_back(i);
             uoff[i] = ubytes;
             ubytes += (size_t)wq::round_up((long)S[i] * g->ts[i]->O * (long)sizeof(float), 256);

@@ -33,15 +33,17 @@ struct SkinnyGroupArgs {
 struct SkinnyGroupPlan {
     bool ok = false;
     int m = 0, rpl = 0, nb = 0;  // tile for the largest S of the launch
+    int waves = 8;               // 8-wave blocks up to S = 16, 4-wave blocks above
     bool gs = false;             // the group-scaled kernel (per-chunk accumulators)
     int grid = 0;
 };
 
-// Plan for n tensors (S[i] >= 1) of one format on 8-wave blocks; fills each
+// Plan for n tensors (S[i] >= 1) of one format; fills each
 // descriptor's nchunks, chunks_per_wave and block_end (the caller fills the
 // pointers, shape, S and, with gs, the group fields). Not ok when a tensor
-// cannot take the few-rows kernel (S > 16, I % 4 != 0, 32-bit offsets, a
-// group size that is not a multiple of a chunk's span).
+// cannot take the few-rows kernel (S > 32, or S > 16 with group scales,
+// I % 4 != 0, 32-bit offsets, a group size that is not a multiple of a
+// chunk's span).
 SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus, bool gs = false);
 hipError_t launch_skinny_group(int fmt, const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hipStream_t st);
 

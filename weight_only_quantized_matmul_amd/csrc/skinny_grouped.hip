@@ -13,8 +13,8 @@ namespace wq {
 
 namespace {
 
-template <int FMT, int M, int RPL, int NB, bool GS>
-__global__ __launch_bounds__(512) void skinny_group_kernel(SkinnyGroupArgs ga) {
+template <int FMT, int M, int RPL, int NB, bool GS, int WAVES = 8>
+__global__ __launch_bounds__(64 * WAVES) void skinny_group_kernel(SkinnyGroupArgs ga) {
     // the block's tensor (wave-uniform scan of at most kSkinnyGroupMax entries)
     const int b = blockIdx.x;
     int t = 0;
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(512) void skinny_group_kernel(SkinnyGroupArgs ga) {
     a.gscales_t = d.gscales_t;
     a.gs = d.gs;
     a.ng = d.ng;
-    skinny_block<FMT, M, RPL, NB, 8, 2, skinny_nbuf(M, NB, 8), GS>(a, b - (t > 0 ? ga.t[t - 1].block_end : 0));
+    skinny_block<FMT, M, RPL, NB, WAVES, 2, skinny_nbuf(M, NB, WAVES), GS>(a, b - (t > 0 ? ga.t[t - 1].block_end : 0));
 }
 
 template <int FMT, int M, int RPL>
@@ -60,9 +60,29 @@ hipError_t launch_group_mr(const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, h
     return hipErrorInvalidValue;
 }
 
+// 17 <= S <= 32: 4-wave blocks at one wave per SIMD (the tiles of the
+// single-tensor launch), one scale per row
+template <int FMT, int M, int RPL>
+hipError_t launch_group_wide(const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hipStream_t st) {
+    if (p.gs || p.waves != 4) return hipErrorInvalidValue;
+#define WQ_SKGW(NB_)                                                                                        \
+    if (p.nb == NB_) {                                                                                      \
+        hipLaunchKernelGGL((skinny_group_kernel<FMT, M, RPL, NB_, false, 4>), dim3(p.grid), dim3(256), 0, st, \
+                           a);                                                                              \
+        return hipGetLastError();                                                                           \
+    }
+    WQ_SKGW(1) WQ_SKGW(2) WQ_SKGW(3)
+    if constexpr (M <= 5) { WQ_SKGW(4) }  // (m = 6 with four blocks would spill)
+#undef WQ_SKGW
+    return hipErrorInvalidValue;
+}
+
 template <int FMT>
 hipError_t launch_group_f(const SkinnyGroupPlan &p, const SkinnyGroupArgs &a, hipStream_t st) {
     switch (p.m * 10 + p.rpl) {
+    case 45: return launch_group_wide<FMT, 4, 5>(p, a, st);
+    case 56: return launch_group_wide<FMT, 5, 6>(p, a, st);
+    case 68: return launch_group_wide<FMT, 6, 8>(p, a, st);
     case 11: return launch_group_mr<FMT, 1, 1>(p, a, st);
     case 12: return launch_group_mr<FMT, 1, 2>(p, a, st);
     case 22: return launch_group_mr<FMT, 2, 2>(p, a, st);
@@ -82,20 +102,30 @@ SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus, b
     int smax = 0;
     for (int i = 0; i < n; ++i) {
         const SkinnyGroupDesc &d = t[i];
-        if (d.S < 1 || d.S > 16 || d.O <= 0 || d.I < 4 || d.I % 4 != 0) return p;
+        if (d.S < 1 || d.S > kSkinnyMaxS || d.O <= 0 || d.I < 4 || d.I % 4 != 0) return p;
         if ((long)d.O * d.stride >= (1L << 31) || (long)d.S * d.I >= (1L << 29)) return p;
         if (gs && (d.gscales_t == nullptr || d.gs <= 0 || d.ng < 1 || d.gs % (fmt == WQ_I2 ? 2 * kChunk : kChunk) != 0 ||
                    (long)d.O * d.ng >= (1L << 31)))
             return p;
         smax = std::max(smax, d.S);
     }
-    p.m = smax <= 5 ? 1 : smax <= 10 ? 2 : 3;
-    p.rpl = (smax + 3) / 4;
+    if (smax <= 16) {
+        p.m = smax <= 5 ? 1 : smax <= 10 ? 2 : 3;
+        p.rpl = (smax + 3) / 4;
+        p.waves = 8;
+    } else {  // the single-tensor launch's 4-wave tiles
+        if (gs) return p;
+        p.m = smax <= 20 ? 4 : smax <= 24 ? 5 : 6;
+        p.rpl = smax <= 20 ? 5 : smax <= 24 ? 6 : 8;
+        p.waves = 4;
+    }
     // output blocks per block: the fewest rounds of one block per CU, weighed
     // against bigger blocks (each loads all of its tensor's x), as for one tensor
     long best = -1;
     for (int nb = 1; nb <= 4; ++nb) {
-        if (!skinny_ring_ok(fmt, p.m, p.rpl, nb) || (gs && !skinny_gs_ok(fmt, p.m, p.rpl, nb, 8))) continue;
+        if (p.waves == 8 && (!skinny_ring_ok(fmt, p.m, p.rpl, nb) || (gs && !skinny_gs_ok(fmt, p.m, p.rpl, nb, 8))))
+            continue;
+        if (p.waves == 4 && p.m == 6 && nb == 4) continue;
         long blocks = 0;
         for (int i = 0; i < n; ++i) blocks += ((long)t[i].O + 16 * nb - 1) / (16 * nb);
         const long cost = (blocks + cus - 1) / cus * (1 + nb);
@@ -112,7 +142,7 @@ SkinnyGroupPlan plan_skinny_group(int fmt, SkinnyGroupDesc *t, int n, int cus, b
         const long nchunks = round_up((npos + kChunk - 1) / kChunk, 2);
         if (nchunks * kChunk >= (1L << 30)) return p;
         d.nchunks = (int)nchunks;
-        d.chunks_per_wave = (int)round_up((nchunks + 7) / 8, 2);
+        d.chunks_per_wave = (int)round_up((nchunks + p.waves - 1) / p.waves, 2);
         end += ((long)d.O + 16 * p.nb - 1) / (16 * p.nb);
         d.block_end = (int)end;
     }
