@@ -227,8 +227,9 @@ int wq_grouped_create(wq_tensor *const *ts, int G, wq_group **group);
  * of 8 experts: 24 tensors with 3 KiB and 1 KiB rows), the work cut into
  * pieces of equal weight bytes when the group is created; more tensors take
  * one launch per 64 (none of this with group-wise scales). Otherwise, when
- * every S[g] <= 16, every x_dev[g] is 16-byte aligned, every I % 4 == 0 and
- * every group size is a multiple of 128 (int8, int4) or 256 (int2), the
+ * every S[g] <= 32 (16 with group-wise scales), every x_dev[g] is 16-byte
+ * aligned, every I % 4 == 0 and every group size is a multiple of 128
+ * (int8, int4) or 256 (int2), the
  * tensors run on the few-rows matrix-core kernel, one launch per 32 tensors
  * with S[g] > 0 (blocks of 16 to 64 output rows of one tensor each; the
  * tile is that of the largest S[g]; with any group-scaled tensor the
