@@ -78,9 +78,19 @@ typedef struct wq_group wq_group;   /* opaque set of tensors run in one launch *
  * WQ_GEMV_MAX_S, WQ_MEM_LIMIT_BYTES, WQ_FAULT=upload|launch,
  * WQ_SKINNY_RING=4|6 (chunks of loads in flight per wave of the few-rows
  * kernel, capped at its spill-free depth; default 2), WQ_WAVES_PER_CU,
- * WQ_TILED_MODE=bf16x3|fp32, WQ_TILED_SHAPE=BMxBNxBK (a compiled tile shape:
+ * WQ_TILED_MODE=bf16x3|bf16|fp32, WQ_TILED_SHAPE=BMxBNxBK (a compiled tile shape:
  * 128x96x64, 128x96x128 or 64x64x64 in bf16x3 mode, 128x96x32 or 64x64x32 in
  * fp32 mode),
+ * where WQ_TILED_MODE=bf16 is an opt-in reduced-precision tiled mode for
+ * quantized weights (the int4 x 16-bit-activation matrix-unit dispatch in
+ * colibri docs "CUDA backend (Linux)", section "The GPU-resident pipeline"):
+ * each activation is rounded
+ * to the nearest bf16 (ties to even) and multiplied once on the bf16 matrix
+ * units. Its results are within the usual bound of the exact product on the
+ * rounded activations, hence within 2^-8 * sum_i |scale * q * x| of the exact
+ * product on the fp32 ones; the default bf16x3 mode gives up no precision.
+ * It applies to calls that take the tiled path only (quantized S > 32 by
+ * default),
  * WQ_VERBOSE=1 prints one line per device on stderr).
  */
 int wq_init(const int *devices, int ndev);

@@ -396,6 +396,58 @@ def test_tiled_modes(mode, fmt, O, I, S):
         gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_MODE=None)
 
 
+def bf16_rne(x):
+    """fp32 -> the nearest bf16 (ties to even), as fp32: the rounding the
+    opt-in one-plane mode applies to activations (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32)
+
+
+@pytest.mark.parametrize("fmt,O,I,S,gs", [
+    (I8, 6144, 1024, 256, 0),   # 128 x 96 tiles
+    (I4, 300, 4100, 40, 0),     # 64 x 192 tiles, split K, one permuted block plus a natural tail
+    (I2, 200, 1030, 70, 0),     # ragged, natural-order rows
+    (I4, 500, 2048, 9, 0),      # forced tiled at S <= 16: 64 x 64 tiles (no 16-row tile in this mode)
+    (I8, 257, 1000, 100, 128),  # group-wise scales
+])
+def test_tiled_bf16_activation_mode(fmt, O, I, S, gs):
+    """WQ_TILED_MODE=bf16: every activation rounded to the nearest bf16, one
+    plane, one MFMA per product. Pinned to the oracle on the rounded
+    activations at the usual bound, and to the oracle on the fp32 activations
+    within 2^-8 of the bound magnitude (the mode's contract)."""
+    p = synth.ragged(fmt, O, I, S, seed=7600 + O + I + S)
+    g = synth.rng(7601 + S)
+    p.x = (p.x * np.exp2(g.integers(-20, 21, size=p.x.shape))).astype(np.float32)
+    sc = None
+    if gs:
+        sc = synth.rng(7602).uniform(0.002, 0.05, size=(O, oracle.n_groups(I, gs))).astype(np.float32)
+        t = wq.wq_tensor_upload_gs(None, gu.DEV, fmt, O, I, gs, p.w, sc)
+    else:
+        t = gu.upload(p)
+    try:
+        gu.reinit_with_env(WQ_FORCE_PATH="tiled", WQ_TILED_MODE="bf16")
+        plan = wq.wq_describe_plan_gs(fmt, O, I, S, gs)
+        assert plan.startswith("tiled") and "mode=bf16 " in plan, plan
+        gu.banner("tiled bf16 activations fmt=%d O=%d I=%d S=%d gs=%d plan=%s" % (fmt, O, I, S, gs, plan))
+        y = gu.run_dev(t, p.x)
+    finally:
+        wq.wq_tensor_free(t)
+        gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_MODE=None)
+    xr = bf16_rne(p.x)
+    if gs:
+        y_r, A_r = oracle.matmul_gs(fmt, p.w, sc, gs, xr, I=I)
+        y_ref, A = oracle.matmul_gs(fmt, p.w, sc, gs, p.x, I=I)
+    else:
+        y_r, A_r = oracle.matmul(fmt, p.w, p.scales, xr, I=I)
+        y_ref, A = oracle.matmul(fmt, p.w, p.scales, p.x, I=I)
+    gu.assert_within_bound(y, y_r, A_r, "bf16 mode vs rounded activations")
+    err = np.abs(y.astype(np.float64) - y_ref)
+    assert np.all(err <= 2.0 ** -8 * A + 1e-30), float(np.max(err / (A + 1e-300)))
+    # and the rounding is really there: the exact split's result differs
+    assert np.any(y.astype(np.float64) != y_ref.astype(np.float32).astype(np.float64))
+
+
 @pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
 @pytest.mark.parametrize("fmt", [I8, I4, I2])
 def test_tiled_one_hot_full_mantissa(mode, fmt):

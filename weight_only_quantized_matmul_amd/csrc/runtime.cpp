@@ -107,6 +107,7 @@ void read_env(Config &c) {
     if (const char *v = getenv("WQ_TILED_MODE")) {
         if (!strcmp(v, "fp32")) c.tiled_mode = wq::kTiledF32;
         else if (!strcmp(v, "bf16x3")) c.tiled_mode = wq::kTiledBF16X3;
+        else if (!strcmp(v, "bf16")) c.tiled_mode = wq::kTiledBF16;
     }
     if (const char *v = getenv("WQ_TILED_SHAPE")) {
         int bm = 0, bn = 0, bk = 0;
@@ -1176,7 +1177,7 @@ int wq_describe_plan_gs(int fmt, int O, int I, int S, int gs, char *buf, size_t 
         snprintf(buf, buflen,
                  "tiled fmt=%d mode=%s bm=%d bn=%d bk=%d tiles_s=%d tiles_o=%d ksplit=%d grid=%d block=%d "
                  "workspace=%zu",
-                 fmt, tp.mode == wq::kTiledBF16X3 ? "bf16x3" : "fp32", tp.bm, tp.bn, tp.bk, tp.tiles_s, tp.tiles_o,
+                 fmt, tp.mode == wq::kTiledBF16X3 ? "bf16x3" : tp.mode == wq::kTiledBF16 ? "bf16" : "fp32", tp.bm, tp.bn, tp.bk, tp.tiles_s, tp.tiles_o,
                  tp.ksplit, tp.grid, tp.block, tp.ws_bytes);
     }
     return WQ_OK;

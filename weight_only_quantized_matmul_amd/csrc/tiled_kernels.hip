@@ -297,7 +297,7 @@ __device__ __forceinline__ uint32_t bf16_pair(uint32_t lo_bits, uint32_t hi_bits
 // of block t / 64 (blocks ordered with kc fastest); rows past S, elements
 // past I and positions past the row's fields are written as zeros, so every
 // element of the planes is rewritten on every call.
-template <int FMT>
+template <int FMT, int NP = 3>
 __global__ __launch_bounds__(256) void split_x_kernel(const float *__restrict__ x, int S, int I, int nfull,
                                                       int vec_ok, int sp, int kp, long plane,
                                                       uint16_t *__restrict__ xp) {
@@ -327,6 +327,18 @@ __global__ __launch_bounds__(256) void split_x_kernel(const float *__restrict__ 
             }
         }
     }
+    const long off = t * 8;
+    if constexpr (NP == 1) {  // one plane: each activation rounded to the nearest bf16 (ties to even)
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t u = __float_as_uint(v[e]);
+            b[e] = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+        }
+        *reinterpret_cast<u32x4 *>(xp + off) =
+            u32x4{bf16_pair(b[0], b[1]), bf16_pair(b[2], b[3]), bf16_pair(b[4], b[5]), bf16_pair(b[6], b[7])};
+        return;
+    }
     uint32_t b1[8], b2[8], b3[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -337,7 +349,6 @@ __global__ __launch_bounds__(256) void split_x_kernel(const float *__restrict__ 
         b2[e] = mb;
         b3[e] = __float_as_uint(r - __uint_as_float(mb));  // exact, at most 8 significant bits
     }
-    const long off = t * 8;
     *reinterpret_cast<u32x4 *>(xp + off) =
         u32x4{bf16_pair(b1[0], b1[1]), bf16_pair(b1[2], b1[3]), bf16_pair(b1[4], b1[5]), bf16_pair(b1[6], b1[7])};
     *reinterpret_cast<u32x4 *>(xp + plane + off) =
@@ -433,7 +444,8 @@ constexpr int kX3WeightSets = 4;   // weight-code register sets (loaded kX3Weigh
 // each K step lies in one group; the steps of a group accumulate into
 // separate fragments, which are added to the accumulators times the group
 // scale of their output column when the group ends.
-template <int FMT, int WAVES, int WM, int WN, int BK_, int PD, int NW, bool GS>
+// NP: activation planes (3: the exact split; 1: x rounded to bf16).
+template <int FMT, int WAVES, int WM, int WN, int BK_, int PD, int NW, bool GS, int NP = 3>
 __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     using C = X3Cfg<WAVES, WM, WN, BK_>;
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LDB = C::LDB, CH = C::CH, KH = C::KH;
@@ -452,14 +464,14 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
     // A fragments of one step: [m][plane][32-position part], lane (li, g)
     // holds row 16m + li, positions 32 * part + 8g .. +8 of the step: one
     // 1 KiB block of the fragment-major planes each
-    typedef u32x4 AFrag[WM][3][KH];
+    typedef u32x4 AFrag[WM][NP][KH];
     const int kcs = a.kp / 32;
     const uint16_t *ap = a.xp + ((long)(s0 / 16 + WM * wave) * kcs) * 512 + lane * 8;
     auto load_a = [&](int kt, AFrag &af) {
 #pragma unroll
         for (int m = 0; m < WM; ++m)
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl)
+            for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
                 for (int h = 0; h < KH; ++h)
                     af[m][pl][h] = *reinterpret_cast<const u32x4 *>(ap + pl * a.plane +
@@ -535,7 +547,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
                 load_w(min(kt + NW, ke - 1), wload);
             }
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl)
+            for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
                 for (int m = 0; m < WM; ++m) {
                     const bf16x8 av = __builtin_bit_cast(bf16x8, cur[m][pl][h]);
@@ -822,22 +834,22 @@ hipError_t launch_f32(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int FMT, int WAVES, int WM, int WN, int BK, int PD, bool GS = false>
+template <int FMT, int WAVES, int WM, int WN, int BK, int PD, bool GS = false, int NP = 3>
 hipError_t launch_x3(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     using C = X3Cfg<WAVES, WM, WN, BK>;
     constexpr int NW = kX3WeightSets;
     static_assert(C::LDS_BYTES <= 160 * 1024, "tile does not fit in LDS");
     static const hipError_t lim =
-        raise_lds_limit(&tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW, GS>, C::LDS_BYTES);
+        raise_lds_limit(&tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW, GS, NP>, C::LDS_BYTES);
     if (lim != hipSuccess) return lim;
     const int vec_ok = ((a.I & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
     const long slots = (long)p.sp * p.kp / 8;  // one thread per 16-byte fragment slot
-    hipLaunchKernelGGL((split_x_kernel<FMT>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st, a.x, a.S,
+    hipLaunchKernelGGL((split_x_kernel<FMT, NP>), dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st, a.x, a.S,
                        a.I, a.nfull, vec_ok, p.sp, p.kp, (long)p.sp * p.kp, const_cast<uint16_t *>(a.xp));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW, GS>), dim3(p.grid), dim3(C::THREADS), C::LDS_BYTES,
-                       st, a);
+    hipLaunchKernelGGL((tiled_x3_kernel<FMT, WAVES, WM, WN, BK, PD, NW, GS, NP>), dim3(p.grid), dim3(C::THREADS),
+                       C::LDS_BYTES, st, a);
     e = hipGetLastError();
     if (e != hipSuccess || a.ksplit == 1) return e;
     const long n = (long)a.S * a.O;
@@ -878,6 +890,19 @@ constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
 template <int FMT>
 hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if constexpr (FMT != WQ_F32) {
+        if (p.mode == kTiledBF16) {  // one rounded plane; no 16-row tile
+            if (a.gs > 0) {
+                if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true, 1>(p, a, st);
+                if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, true, 1>(p, a, st);
+                return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true, 1>(p, a, st);
+            }
+            if (p.bm == 128) {
+                if (p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch, false, 1>(p, a, st);
+                return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, false, 1>(p, a, st);
+            }
+            if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, false, 1>(p, a, st);
+            return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, false, 1>(p, a, st);
+        }
         if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: 64-position K steps
             if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true>(p, a, st);
             if (p.bm == 16) return launch_x3o<FMT, 8, 1, true>(p, a, st);
@@ -911,7 +936,7 @@ TiledPlan plan_shape(TiledPlan p, const Shape &sh, int fmt, int O, int I, int S,
     p.tiles_s = (S + p.bm - 1) / p.bm;
     p.tiles_o = (O + p.bn - 1) / p.bn;
     p.grid = p.tiles_s * p.tiles_o;
-    p.block = (p.mode == kTiledBF16X3 && (p.bm == 128 || p.bm == 16)) ? 512 : 256;  // 64-row tiles: four waves
+    p.block = (p.mode != kTiledF32 && (p.bm == 128 || p.bm == 16)) ? 512 : 256;  // 64-row tiles: four waves
     if (p.mode == kTiledF32) {
         // fp32 mode: no planes; split K as below when the tiles leave the
         // chip short of waves (f32 12288 x 6144 at S = 9: 192 tiles)
@@ -929,14 +954,14 @@ TiledPlan plan_shape(TiledPlan p, const Shape &sh, int fmt, int O, int I, int S,
             }
         }
     }
-    if (p.mode == kTiledBF16X3) {
+    if (p.mode != kTiledF32) {
         const long stride = round_up(row_bytes(fmt, I), kRowAlign);
         const long npos = stride * elems_per_byte(fmt);
         p.kp = (int)round_up(npos, kTiledKAlign);
         // plane rows: the 16-row tile reads 16-row blocks only; the larger
         // tiles read up to 128-row multiples
         p.sp = (int)round_up(S, p.bm == 16 ? 16 : kTiledSAlign);
-        p.ws_bytes = (size_t)3 * p.sp * p.kp * sizeof(uint16_t);
+        p.ws_bytes = (size_t)(p.mode == kTiledBF16 ? 1 : 3) * p.sp * p.kp * sizeof(uint16_t);
         // Split K when the tiles alone leave the chip short of blocks (few
         // activation rows): each K chunk of at least kTiledMinChunk steps
         // becomes a block of its own. Group-scaled tensors keep whole rows.
@@ -973,12 +998,16 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
     TiledPlan p;
     // the bf16 split needs exact integer codes (quantized formats); f32 weights
     // stay fp32; group-scaled tensors always take the bf16x3 kernel
-    p.mode = (fmt != WQ_F32 && (mode == kTiledBF16X3 || gs > 0)) ? kTiledBF16X3 : kTiledF32;
+    p.mode = fmt == WQ_F32 ? kTiledF32
+             : mode == kTiledBF16 ? kTiledBF16
+             : (mode == kTiledBF16X3 || gs > 0) ? kTiledBF16X3 : kTiledF32;
     // plane sizes are kept in int: rows near the int limit take the fp32 mode
     if ((long)S > INT_MAX - kTiledSAlign || (long)I > INT_MAX / 2 - 4 * kTiledKAlign) p.mode = kTiledF32;
-    if (p.mode == kTiledBF16X3) {
+    if (p.mode != kTiledF32) {
+        const bool a16 = p.mode == kTiledBF16;  // no 16-row tile (its kernel reads three planes)
         for (const Shape &c : kX3Shapes)
-            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign))
+            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign) &&
+                !(a16 && c.bm == 16))
                 return plan_shape(p, c, fmt, O, I, S, gs);
         // S <= 16: 16 x 128 tiles of eight waves side by side along o,
         // sharing the activation fragments (tiled_x3o_kernel). 17..64: 64 x
@@ -995,7 +1024,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         // 342 big blocks vs 115.7 on 512 small ones; int4 14336 x 4096 at
         // S = 512 207.5 on 600 big blocks, fill 0.78, vs 255 on 1792 small
         // ones, fill 0.88).
-        if (S <= 16) return plan_shape(p, kX3Shapes[3], fmt, O, I, S, gs);
+        if (S <= 16) return plan_shape(p, a16 ? kX3Shapes[2] : kX3Shapes[3], fmt, O, I, S, gs);
         const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
         const TiledPlan large = plan_shape(p, S <= 64 ? kX3Shapes[4] : kX3Shapes[0], fmt, O, I, S, gs);
         return round_fill(large) + 0.2 >= round_fill(small) ? large : small;

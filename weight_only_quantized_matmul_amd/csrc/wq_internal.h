@@ -255,6 +255,7 @@ struct TiledArgs {
 
 constexpr int kTiledF32 = 0;     // fp32 operands, v_mfma_f32_16x16x4_f32
 constexpr int kTiledBF16X3 = 1;  // exact 3-way bf16 split of x, v_mfma_f32_16x16x32_bf16
+constexpr int kTiledBF16 = 2;    // opt-in: x rounded to the nearest bf16 (one plane), same MFMA
 constexpr int kTiledKAlign = 128; // plane rows padded (with zeros) to this many positions
 constexpr int kTiledSAlign = 128; // planes padded (with zero rows) to this many rows
 
@@ -265,7 +266,7 @@ struct TiledPlan {
     int sp = 0, kp = 0;   // bf16x3: plane rows and row length
     int ksplit = 1;       // bf16x3: K chunks per tile (grid = tiles * ksplit)
     size_t part_off = 0;  // split K: byte offset of the partials in the workspace
-    size_t ws_bytes = 0;  // device workspace the call needs (bf16x3: 3 planes [+ partials])
+    size_t ws_bytes = 0;  // device workspace the call needs (bf16x3: 3 planes, bf16: 1 [+ partials])
 };
 constexpr int kTiledSplitWaves = 2048;  // split K until the grid holds this many waves (8 per CU)
 constexpr int kTiledMinChunk = 4;       // K steps per chunk at least
