@@ -378,3 +378,22 @@ def test_stream_read_rejects_bad_arguments_before_any_device_call():
     assert f(buf, 1000, 4, 4, out, None) == wq.WQ_E_INVAL      # not a multiple of 16 bytes
     assert f(ctypes.c_void_p(0x20008), 1024, 4, 4, out, None) == wq.WQ_E_INVAL  # misaligned
     assert f(buf, 0, 4, 4, out, None) == wq.WQ_OK              # nothing to read: no launch
+
+
+@pytest.mark.parametrize("fmt,O,I,S,gs,shape", [
+    (wq.WQ_I8, 6144, 6144, 512, 0, ("128", "96", "128")),   # above 64 rows: 128-deep K steps
+    (wq.WQ_I2, 16384, 8192, 96, 0, ("128", "96", "128")),
+    (wq.WQ_I8, 6144, 6144, 512, 128, ("128", "96", "64")),  # group scales: one group per step
+    (wq.WQ_I4, 300, 4100, 40, 0, ("64", "192", "64")),      # 33..64 rows: the bf16x3 rule
+])
+def test_bf16_activation_mode_plans(fmt, O, I, S, gs, shape):
+    with forced(WQ_TILED_MODE="bf16"):
+        k, p = _plan_gs(fmt, O, I, S, gs)
+        assert k == "tiled" and p["mode"] == "bf16", p
+        assert (p["bm"], p["bn"], p["bk"]) == shape, p
+        assert int(p["workspace"]) >= int(p["tiles_s"]) * int(p["bm"]) * I * 2  # one plane
+        with forced(WQ_FORCE_PATH="tiled"):  # forced at S <= 16: 64 x 64 tiles (no 16-row tile)
+            k, p = _plan_gs(fmt, O, I, 9, gs)
+            assert (k, p["mode"], p["bm"], p["bn"]) == ("tiled", "bf16", "64", "64"), p
+    with forced(WQ_TILED_MODE="bf16x3"):
+        assert _plan_gs(fmt, O, I, S, gs)[1]["mode"] == "bf16x3"

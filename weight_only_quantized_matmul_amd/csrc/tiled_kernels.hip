@@ -1025,6 +1025,14 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         // S = 512 207.5 on 600 big blocks, fill 0.78, vs 255 on 1792 small
         // ones, fill 0.88).
         if (S <= 16) return plan_shape(p, a16 ? kX3Shapes[2] : kX3Shapes[3], fmt, O, I, S, gs);
+        // One rounded plane above 64 rows: 128 x 96 tiles with 128-deep K
+        // steps (half the barriers per product), whatever the fill (us,
+        // 128x96x128 / 128x96x64 / 64x64x64: int8 6144 x 6144 at S = 512
+        // 64.1 / 73.1 / 86.5, at S = 128 32.3 / 35.1 / 40.9; int4 12288 x 6144
+        // at S = 96 41.7 / 47.0 / 52.7; int4 14336 x 4096 at S = 512 100.2 /
+        // 115.4 / 127.9; int2 16384 x 8192 at S = 96 66.0 / 81.5 / 78.4).
+        // Group scales need 64-deep steps (one group per step).
+        if (a16 && S > 64 && gs == 0) return plan_shape(p, kX3Shapes[1], fmt, O, I, S, gs);
         const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
         const TiledPlan large = plan_shape(p, S <= 64 ? kX3Shapes[4] : kX3Shapes[0], fmt, O, I, S, gs);
         return round_fill(large) + 0.2 >= round_fill(small) ? large : small;
