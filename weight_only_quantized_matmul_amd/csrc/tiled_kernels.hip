@@ -1034,7 +1034,13 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         // Group scales need 64-deep steps (one group per step).
         if (a16 && S > 64 && gs == 0) return plan_shape(p, kX3Shapes[1], fmt, O, I, S, gs);
         const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
-        const TiledPlan large = plan_shape(p, S <= 64 ? kX3Shapes[4] : kX3Shapes[0], fmt, O, I, S, gs);
+        // The large tiles above 64 rows step 128 deep in K unless group scales
+        // need one group per step (us, 128x96x128 / 128x96x64 in this mode:
+        // int8 6144 x 6144 at S = 512 109.2 / 114.3, at S = 128 43.1 / 45.2;
+        // int4 12288 x 6144 at S = 96 62.6 / 66.6; int4 14336 x 4096 at
+        // S = 512 197.6 / 207.7).
+        const Shape &big = gs == 0 ? kX3Shapes[1] : kX3Shapes[0];
+        const TiledPlan large = plan_shape(p, S <= 64 ? kX3Shapes[4] : big, fmt, O, I, S, gs);
         return round_fill(large) + 0.2 >= round_fill(small) ? large : small;
     }
     // fp32: big tiles (128 x 96, 4 x 3 fragments per wave) when there are enough of them
