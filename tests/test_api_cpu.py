@@ -383,7 +383,8 @@ def test_stream_read_rejects_bad_arguments_before_any_device_call():
 @pytest.mark.parametrize("fmt,O,I,S,gs,shape", [
     (wq.WQ_I8, 6144, 6144, 512, 0, ("128", "96", "128")),   # above 64 rows: 128-deep K steps
     (wq.WQ_I2, 16384, 8192, 96, 0, ("128", "96", "128")),
-    (wq.WQ_I8, 6144, 6144, 512, 128, ("128", "96", "64")),  # group scales: one group per step
+    (wq.WQ_I8, 6144, 6144, 512, 128, ("128", "96", "128")),  # group scales: one group per step
+    (wq.WQ_I8, 6144, 6144, 512, 192, ("128", "96", "64")),   # 192 = 1.5 steps of 128: 64-deep steps
     (wq.WQ_I4, 300, 4100, 40, 0, ("64", "192", "64")),      # 33..64 rows: the bf16x3 rule
 ])
 def test_bf16_activation_mode_plans(fmt, O, I, S, gs, shape):
@@ -397,3 +398,12 @@ def test_bf16_activation_mode_plans(fmt, O, I, S, gs, shape):
             assert (k, p["mode"], p["bm"], p["bn"]) == ("tiled", "bf16", "64", "64"), p
     with forced(WQ_TILED_MODE="bf16x3"):
         assert _plan_gs(fmt, O, I, S, gs)[1]["mode"] == "bf16x3"
+
+
+@pytest.mark.parametrize("gs,bk", [(0, "128"), (128, "128"), (256, "128"), (64, "64"), (192, "64"), (320, "64")])
+def test_tiled_k_depth_follows_group_size(gs, bk):
+    """128 x 96 tiles step 128 deep unless a group would straddle a step."""
+    k, p = _plan_gs(wq.WQ_I8, 6144, 6144, 512, gs)
+    assert (k, p["mode"], p["bm"], p["bn"], p["bk"]) == ("tiled", "bf16x3", "128", "96", bk), p
+    with forced(WQ_TILED_SHAPE="128x96x128"):
+        assert _plan_gs(wq.WQ_I8, 6144, 6144, 512, gs)[1]["bk"] == bk

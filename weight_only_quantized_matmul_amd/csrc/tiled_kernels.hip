@@ -440,8 +440,9 @@ constexpr int kX3WeightSets = 4;   // weight-code register sets (loaded kX3Weigh
 
 // PD: activation fragments are loaded PD steps ahead (PD + 1 register sets);
 // NW: weight codes are loaded NW - 1 steps before they are staged (NW sets)
-// GS: group-wise scales (rows in natural order, gs a multiple of BK = 64):
-// each K step lies in one group; the steps of a group accumulate into
+// GS: group-wise scales (rows in natural order, gs a multiple of BK, 64 or
+// 128; the planner takes 128-deep steps only when gs % 128 == 0): each K step
+// lies in one group; the steps of a group accumulate into
 // separate fragments, which are added to the accumulators times the group
 // scale of their output column when the group ends.
 // NP: activation planes (3: the exact split; 1: x rounded to bf16).
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_x3_kernel(TiledArgs a) {
         float gsc[WN];
         bool group_ends = false;
         if constexpr (GS) {
-            static_assert(BK == kGroupAlign, "a group-scaled K step must lie in one group");
+            static_assert(BK % kGroupAlign == 0, "a group-scaled K step covers whole 64-position blocks");
             const long first = (long)kt * BK;
             const int grp = min((int)(first / a.gs), a.ng - 1);
             group_ends = (first + BK) % a.gs == 0 || kt + 1 == nk;  // wave-uniform
@@ -892,6 +893,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
     if constexpr (FMT != WQ_F32) {
         if (p.mode == kTiledBF16) {  // one rounded plane; no 16-row tile
             if (a.gs > 0) {
+                if (p.bm == 128 && p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch, true, 1>(p, a, st);
                 if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true, 1>(p, a, st);
                 if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, true, 1>(p, a, st);
                 return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true, 1>(p, a, st);
@@ -903,7 +905,8 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
             if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, false, 1>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, false, 1>(p, a, st);
         }
-        if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: 64-position K steps
+        if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: K steps within one group
+            if (p.bm == 128 && p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch, true>(p, a, st);
             if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true>(p, a, st);
             if (p.bm == 16) return launch_x3o<FMT, 8, 1, true>(p, a, st);
             if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, true>(p, a, st);
@@ -1006,7 +1009,7 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
     if (p.mode != kTiledF32) {
         const bool a16 = p.mode == kTiledBF16;  // no 16-row tile (its kernel reads three planes)
         for (const Shape &c : kX3Shapes)
-            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || c.bk == kGroupAlign) &&
+            if (shape == c.bm * 1000000 + c.bn * 1000 + c.bk && (gs == 0 || gs % c.bk == 0) &&
                 !(a16 && c.bm == 16))
                 return plan_shape(p, c, fmt, O, I, S, gs);
         // S <= 16: 16 x 128 tiles of eight waves side by side along o,
@@ -1031,15 +1034,15 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         // 64.1 / 73.1 / 86.5, at S = 128 32.3 / 35.1 / 40.9; int4 12288 x 6144
         // at S = 96 41.7 / 47.0 / 52.7; int4 14336 x 4096 at S = 512 100.2 /
         // 115.4 / 127.9; int2 16384 x 8192 at S = 96 66.0 / 81.5 / 78.4).
-        // Group scales need 64-deep steps (one group per step).
-        if (a16 && S > 64 && gs == 0) return plan_shape(p, kX3Shapes[1], fmt, O, I, S, gs);
+        // Group scales need steps within one group (gs % 128 == 0 here).
+        if (a16 && S > 64 && gs % 128 == 0) return plan_shape(p, kX3Shapes[1], fmt, O, I, S, gs);
         const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
-        // The large tiles above 64 rows step 128 deep in K unless group scales
-        // need one group per step (us, 128x96x128 / 128x96x64 in this mode:
+        // The large tiles above 64 rows step 128 deep in K unless a group
+        // holds fewer or an odd number of 64-position blocks (us, 128x96x128 / 128x96x64 in this mode:
         // int8 6144 x 6144 at S = 512 109.2 / 114.3, at S = 128 43.1 / 45.2;
         // int4 12288 x 6144 at S = 96 62.6 / 66.6; int4 14336 x 4096 at
         // S = 512 197.6 / 207.7).
-        const Shape &big = gs == 0 ? kX3Shapes[1] : kX3Shapes[0];
+        const Shape &big = gs % 128 == 0 ? kX3Shapes[1] : kX3Shapes[0];
         const TiledPlan large = plan_shape(p, S <= 64 ? kX3Shapes[4] : big, fmt, O, I, S, gs);
         return round_fill(large) + 0.2 >= round_fill(small) ? large : small;
     }
