@@ -385,7 +385,8 @@ def test_stream_read_rejects_bad_arguments_before_any_device_call():
     (wq.WQ_I2, 16384, 8192, 96, 0, ("128", "96", "128")),
     (wq.WQ_I8, 6144, 6144, 512, 128, ("128", "96", "128")),  # group scales: one group per step
     (wq.WQ_I8, 6144, 6144, 512, 192, ("128", "96", "64")),   # 192 = 1.5 steps of 128: 64-deep steps
-    (wq.WQ_I4, 300, 4100, 40, 0, ("64", "192", "64")),      # 33..64 rows: the bf16x3 rule
+    (wq.WQ_I4, 300, 4100, 40, 0, ("64", "64", "128")),      # 17..64 rows: 64 x 64 tiles, 128 deep
+    (wq.WQ_I4, 300, 4100, 40, 64, ("64", "192", "64")),     # gs = 64: the bf16x3 rule
 ])
 def test_bf16_activation_mode_plans(fmt, O, I, S, gs, shape):
     with forced(WQ_TILED_MODE="bf16"):

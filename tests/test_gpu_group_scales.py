@@ -77,7 +77,7 @@ def test_group_scales_misaligned_activations(fmt, O, I, gs):
     check(fmt, O, I, 1, gs, seed=8550 + O + I, what="gs-misaligned", x_offset=1)
 
 
-@pytest.mark.parametrize("shape", ["64x192x64", "64x64x64", "128x96x64", "128x96x128"])
+@pytest.mark.parametrize("shape", ["64x192x64", "64x64x64", "128x96x64", "128x96x128", "64x64x128"])
 @pytest.mark.parametrize("fmt,O,I,S,gs", [(I4, 500, 3000, 40, 128), (I8, 200, 1000, 20, 64), (I2, 300, 4100, 50, 256)])
 def test_group_scales_forced_tile_shapes(shape, fmt, O, I, S, gs):
     """Every group-scaled tiled kernel (the group sums added per K step; a 128-deep

@@ -409,7 +409,9 @@ def bf16_rne(x):
     (I4, 300, 4100, 40, 0),     # 64 x 192 tiles, split K, one permuted block plus a natural tail
     (I2, 200, 1030, 70, 0),     # ragged, natural-order rows
     (I4, 500, 2048, 9, 0),      # forced tiled at S <= 16: 64 x 64 tiles (no 16-row tile in this mode)
-    (I8, 257, 1000, 100, 128),  # group-wise scales
+    (I8, 257, 1000, 100, 128),  # group-wise scales, 128 x 96 tiles 128 deep
+    (I4, 300, 4100, 40, 128),   # group-wise scales, 64 x 64 tiles 128 deep
+    (I8, 130, 2000, 33, 0),     # 64 x 64 tiles 128 deep, split K
 ])
 def test_tiled_bf16_activation_mode(fmt, O, I, S, gs):
     """WQ_TILED_MODE=bf16: every activation rounded to the nearest bf16, one
@@ -582,3 +584,17 @@ def test_s1_wide_dynamic_range_activations(fmt, O, I):
     g = synth.rng(9301 + fmt)
     p.x = (p.x * np.power(10.0, g.uniform(-35, 35, size=p.x.shape))).astype(np.float32)
     check_problem(p, "wide-range")
+
+
+@pytest.mark.parametrize("shape", ["64x64x128", "128x96x128", "64x64x64", "128x96x64"])
+@pytest.mark.parametrize("fmt,O,I,S", [(I2, 300, 1030, 70), (I8, 129, 4100, 100), (I4, 1000, 2000, 40)])
+def test_tiled_forced_shapes(shape, fmt, O, I, S):
+    """Every compiled bf16x3 tile shape on ragged O, I and S (64- and 128-deep K steps)."""
+    p = synth.ragged(fmt, O, I, S, seed=7700 + O + S)
+    try:
+        gu.reinit_with_env(WQ_FORCE_PATH="tiled", WQ_TILED_SHAPE=shape)
+        plan = wq.wq_describe_plan(fmt, O, I, S)
+        assert ("bm=%s bn=%s bk=%s" % tuple(shape.split("x"))) in plan, plan
+        check_problem(p, "tiled-" + shape)
+    finally:
+        gu.reinit_with_env(WQ_FORCE_PATH=None, WQ_TILED_SHAPE=None)

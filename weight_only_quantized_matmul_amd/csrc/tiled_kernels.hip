@@ -885,7 +885,8 @@ hipError_t launch_x3o(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
 struct Shape {
     int bm, bn, bk;
 };
-constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 128}, {64, 64, 64}, {16, 128, 64}, {64, 192, 64}};
+constexpr Shape kX3Shapes[] = {{128, 96, 64}, {128, 96, 128}, {64, 64, 64}, {16, 128, 64}, {64, 192, 64},
+                               {64, 64, 128}};
 constexpr Shape kF32Shapes[] = {{128, 96, 32}, {64, 64, 32}};
 
 template <int FMT>
@@ -896,6 +897,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
                 if (p.bm == 128 && p.bk == 128) return launch_x3<FMT, 8, 1, 6, 128, kX3ActPrefetch, true, 1>(p, a, st);
                 if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true, 1>(p, a, st);
                 if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, true, 1>(p, a, st);
+                if (p.bk == 128) return launch_x3<FMT, 4, 1, 4, 128, kX3ActPrefetch, true, 1>(p, a, st);
                 return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true, 1>(p, a, st);
             }
             if (p.bm == 128) {
@@ -903,6 +905,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
                 return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, false, 1>(p, a, st);
             }
             if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, false, 1>(p, a, st);
+            if (p.bk == 128) return launch_x3<FMT, 4, 1, 4, 128, kX3ActPrefetch, false, 1>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, false, 1>(p, a, st);
         }
         if (p.mode == kTiledBF16X3 && a.gs > 0) {  // group-wise scales: K steps within one group
@@ -910,6 +913,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
             if (p.bm == 128) return launch_x3<FMT, 8, 1, 6, 64, kX3ActPrefetch, true>(p, a, st);
             if (p.bm == 16) return launch_x3o<FMT, 8, 1, true>(p, a, st);
             if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch, true>(p, a, st);
+            if (p.bk == 128) return launch_x3<FMT, 4, 1, 4, 128, kX3ActPrefetch, true>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch, true>(p, a, st);
         }
         if (p.mode == kTiledBF16X3) {
@@ -919,6 +923,7 @@ hipError_t launch_fmt(const TiledPlan &p, const TiledArgs &a, hipStream_t st) {
             }
             if (p.bm == 16) return launch_x3o<FMT, 8, 1>(p, a, st);
             if (p.bn == 192) return launch_x3<FMT, 4, 1, 12, 64, kX3ActPrefetch>(p, a, st);
+            if (p.bk == 128) return launch_x3<FMT, 4, 1, 4, 128, kX3ActPrefetch>(p, a, st);
             return launch_x3<FMT, 4, 1, 4, 64, kX3ActPrefetch>(p, a, st);
         }
     }
@@ -1036,7 +1041,17 @@ TiledPlan plan_tiled(int fmt, int O, int I, int S, int mode, int shape, int gs) 
         // 115.4 / 127.9; int2 16384 x 8192 at S = 96 66.0 / 81.5 / 78.4).
         // Group scales need steps within one group (gs % 128 == 0 here).
         if (a16 && S > 64 && gs % 128 == 0) return plan_shape(p, kX3Shapes[1], fmt, O, I, S, gs);
-        const TiledPlan small = plan_shape(p, kX3Shapes[2], fmt, O, I, S, gs);
+        // ... and 64 x 64 tiles, also 128 deep, for 17..64 rows (us, 64x64x128 /
+        // 64x192x64: int4 12288 x 6144 at S = 40 34.5 / 41.5, at S = 48 36.3 /
+        // 43.7; int8 6144 x 6144 at S = 64 28.6 / 34.3). 64 x 192 tiles 128
+        // deep run one wave per SIMD and lost everywhere (5-50 %).
+        if (a16 && gs % 128 == 0) return plan_shape(p, kX3Shapes[5], fmt, O, I, S, gs);
+        // bf16x3: where the 64 x 64 tiles win above 64 rows they step 128 deep
+        // (int2 16384 x 8192 at S = 96 106.2 against 114.9 us); at 17..64 rows
+        // 128-deep 64 x 64 tiles lost to 64 x 192 ones (int4 at S = 40 54.0 /
+        // 48.6, int8 at S = 64 39.7 / 38.3).
+        const TiledPlan small =
+            plan_shape(p, S > 64 && gs % 128 == 0 ? kX3Shapes[5] : kX3Shapes[2], fmt, O, I, S, gs);
         // The large tiles above 64 rows step 128 deep in K unless a group
         // holds fewer or an odd number of 64-position blocks (us, 128x96x128 / 128x96x64 in this mode:
         // int8 6144 x 6144 at S = 512 109.2 / 114.3, at S = 128 43.1 / 45.2;
