@@ -79,8 +79,10 @@ typedef struct wq_group wq_group;   /* opaque set of tensors run in one launch *
  * WQ_SKINNY_RING=4|6 (chunks of loads in flight per wave of the few-rows
  * kernel, capped at its spill-free depth; default 2), WQ_WAVES_PER_CU,
  * WQ_TILED_MODE=bf16x3|bf16|fp32, WQ_TILED_SHAPE=BMxBNxBK (a compiled tile shape:
- * 128x96x64, 128x96x128 or 64x64x64 in bf16x3 mode, 128x96x32 or 64x64x32 in
- * fp32 mode),
+ * 128x96x64, 128x96x128, 64x64x64, 64x64x128, 64x192x64 or 16x128x64 in the
+ * bf16x3 mode, the same but 16x128x64 in the bf16 mode, 128x96x32 or 64x64x32
+ * in fp32 mode; a 128-deep shape is taken with group scales only when the
+ * group size is a multiple of 128, else the automatic choice stands),
  * where WQ_TILED_MODE=bf16 is an opt-in reduced-precision tiled mode for
  * quantized weights (the int4 x 16-bit-activation matrix-unit dispatch in
  * colibri docs "CUDA backend (Linux)", section "The GPU-resident pipeline"):
